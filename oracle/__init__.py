@@ -1,0 +1,229 @@
+"""CPU oracle for the K-grouped MoE weight-gradient GEMM (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The product path (the
+HIP library and its Python binding) never imports this package, and this
+package never imports the product.
+
+The arithmetic lives in ``kgw_oracle.c`` (plain C, IEEE double, OpenMP over
+output rows).  This module builds it with gcc, loads it with ctypes, and
+adds the output semantics of the cuDNN "Grouped GEMM + WGrad (Unified)"
+page, section "Operation": overwrite writes Wgrad[e] (an empty expert gives
+zero); accumulate adds Wgrad[e] onto the caller-initialised output.
+
+Every function here is pinned by tests/test_oracle.py against brute force,
+closed forms, library decoders or invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kgw_oracle.c")
+_LIB = os.path.join(_HERE, "libkgw_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile kgw_oracle.c into libkgw_oracle.so next to it (gcc, OpenMP)."""
+    global _lib
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3fn_value.restype = ctypes.c_double
+    lib.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_expert_range.restype = None
+    lib.oracle_expert_range.argtypes = [p, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_wgrad_rows_bf16.restype = ctypes.c_int
+    lib.oracle_wgrad_rows_bf16.argtypes = [p, p, i64, i64, i64, i64, p, i64, p]
+    lib.oracle_wgrad_rows_fp8.restype = ctypes.c_int
+    lib.oracle_wgrad_rows_fp8.argtypes = [p, p, i64, p, p, i64, i64, i64, i64, p, i64, p]
+    lib.oracle_wgrad_bf16.restype = ctypes.c_int
+    lib.oracle_wgrad_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p]
+    lib.oracle_wgrad_fp8.restype = ctypes.c_int
+    lib.oracle_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _u16(a) -> np.ndarray:
+    a = _as_numpy(a)
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    assert a.dtype == np.uint16, a.dtype
+    return np.ascontiguousarray(a)
+
+
+def _u8(a) -> np.ndarray:
+    a = _as_numpy(a)
+    if a.dtype == np.int8:
+        a = a.view(np.uint8)
+    assert a.dtype == np.uint8, a.dtype
+    return np.ascontiguousarray(a)
+
+
+def _as_numpy(a) -> np.ndarray:
+    """Raw storage of a host array or CPU torch tensor (bf16 viewed as its bit pattern)."""
+    if isinstance(a, np.ndarray):
+        return a
+    import torch  # only for accepting CPU tensors; no torch arithmetic is used
+    t = a.detach()
+    assert t.device.type == "cpu", "the oracle works on host memory"
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.float8_e4m3fn,):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+# ----------------------------------------------------------------------------
+# decoders and offsets
+# ----------------------------------------------------------------------------
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(bits)
+
+
+def e4m3fn_value(bits: int) -> float:
+    return _load().oracle_e4m3fn_value(bits)
+
+
+def e8m0_value(bits: int) -> float:
+    return _load().oracle_e8m0_value(bits)
+
+
+def expert_range(offsets, e: int):
+    off = np.ascontiguousarray(_as_numpy(offsets).astype(np.int32))
+    b, t = ctypes.c_int64(), ctypes.c_int64()
+    _load().oracle_expert_range(_ptr(off), int(e), ctypes.byref(b), ctypes.byref(t))
+    return b.value, t.value
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+# ----------------------------------------------------------------------------
+# the grouped product
+# ----------------------------------------------------------------------------
+def wgrad_rows_bf16(A, B, offsets, e: int, rows: Sequence[int]) -> np.ndarray:
+    """Rows `rows` of Wgrad[e] in float64 (bf16 operands)."""
+    a, b = _u16(A), _u16(B)
+    hidden, T = a.shape
+    n = b.shape[1]
+    begin, end = expert_range(offsets, e)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert r.size == 0 or (r.min() >= 0 and r.max() < hidden)
+    out = np.empty((r.size, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_rows_bf16(_ptr(a), _ptr(b), T, n, begin, end, _ptr(r), r.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle: bad token range [{begin}, {end}) for tokens_sum {T}")
+    return out
+
+
+def wgrad_rows_fp8(A, sfa, B, sfb, offsets, e: int, rows: Sequence[int]) -> np.ndarray:
+    """Rows `rows` of Wgrad[e] in float64 (e4m3 operands, UE8M0 per 128 tokens)."""
+    a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
+    hidden, T = a.shape
+    n = b.shape[1]
+    begin, end = expert_range(offsets, e)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert r.size == 0 or (r.min() >= 0 and r.max() < hidden)
+    out = np.empty((r.size, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_rows_fp8(_ptr(a), _ptr(sa), hidden, _ptr(b), _ptr(sb), T, n, begin, end,
+                                       _ptr(r), r.size, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle: bad token range [{begin}, {end}) for tokens_sum {T}")
+    return out
+
+
+def wgrad_bf16(A, B, offsets) -> np.ndarray:
+    """Dense Wgrad (E, hidden, n) in float64 for bf16 operands."""
+    a, b = _u16(A), _u16(B)
+    off = np.ascontiguousarray(_as_numpy(offsets).astype(np.int32))
+    hidden, T = a.shape
+    n = b.shape[1]
+    out = np.empty((off.size, hidden, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_bf16(_ptr(a), _ptr(b), _ptr(off), off.size, hidden, n, T, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: malformed offsets")
+    return out
+
+
+def wgrad_fp8(A, sfa, B, sfb, offsets) -> np.ndarray:
+    """Dense Wgrad (E, hidden, n) in float64 for e4m3 operands with UE8M0 block scales."""
+    a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
+    off = np.ascontiguousarray(_as_numpy(offsets).astype(np.int32))
+    hidden, T = a.shape
+    n = b.shape[1]
+    out = np.empty((off.size, hidden, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_fp8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(off), off.size, hidden, n, T,
+                                  _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: malformed offsets")
+    return out
+
+
+def apply_output_mode(W: np.ndarray, accumulate: bool, C0: Optional[np.ndarray] = None) -> np.ndarray:
+    """Exact (float64) value the output should hold before rounding to its dtype.
+
+    overwrite: Wgrad itself (an empty expert's sum is over no tokens: zero);
+    accumulate: the caller's initial output plus Wgrad.
+    """
+    if not accumulate:
+        return W
+    assert C0 is not None and C0.shape == W.shape
+    return C0.astype(np.float64) + W
+
+
+# ----------------------------------------------------------------------------
+# output rounding (for exactness pins) and the bf16 unit in the last place
+# ----------------------------------------------------------------------------
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (round to nearest, ties to even), returned as float64.
+
+    Goes through float32 first, which is exact for every value the exactness
+    pins use (integers below 2^24); NaN stays NaN.
+    """
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    out = (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits): 2^(floor(log2|x|) - 7)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    tiny = 2.0 ** -126
+    ax = np.maximum(ax, tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 7.0)

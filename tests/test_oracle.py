@@ -1,0 +1,280 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+Each test checks the oracle against something other than itself: a worked
+example, a library decoder, a closed form, an invariant the operation must
+satisfy, or a brute-force product computed independently with numpy.  They
+are chosen so that a dropped term, a wrong sign, an off-by-one token range
+or a transposed operand in the oracle fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float values that are exact in bf16 -> uint16 bit patterns (test-side, independent of the oracle)."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def brute_force(A64, B64, counts):
+    """Independent per-expert product with numpy float64 matmul."""
+    out = []
+    start = 0
+    for c in counts:
+        out.append(A64[:, start:start + c] @ B64[start:start + c, :])
+        start += c
+    return np.stack(out)
+
+
+# ----------------------------------------------------------------------------
+# worked example and offsets decode
+# ----------------------------------------------------------------------------
+def test_hand_worked_example(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    A = bf16_bits(np.array(g["A"], dtype=np.float32))
+    B = bf16_bits(np.array(g["B"], dtype=np.float32))
+    off = np.array(g["offsets"], dtype=np.int32)
+    W = oracle.wgrad_bf16(A, B, off)
+    np.testing.assert_array_equal(W, np.array(g["wgrad"], dtype=np.float64))
+    acc = oracle.apply_output_mode(W, True, np.ones_like(W))
+    np.testing.assert_array_equal(acc, np.array(g["accumulate_onto_ones"], dtype=np.float64))
+
+
+def test_expert_range_inclusive_cumsum(oracle_lib):
+    off = np.array([256, 256, 768, 1024], dtype=np.int32)
+    assert [oracle.expert_range(off, e) for e in range(4)] == [(0, 256), (256, 256), (256, 768), (768, 1024)]
+
+
+# ----------------------------------------------------------------------------
+# format decoders against library decoders and printed spec values
+# ----------------------------------------------------------------------------
+def test_bf16_decoder_all_patterns(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_value(int(b)) for b in bits])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.array_equal(got[~both_nan], ref[~both_nan])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_e4m3fn_decoder_all_patterns(oracle_lib):
+    bits = np.arange(256, dtype=np.int32).astype(np.uint8)
+    ref = torch.from_numpy(bits).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3fn_value(int(b)) for b in bits])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # spec values: largest finite, smallest subnormal, smallest normal, NaN, signed zero
+    assert oracle.e4m3fn_value(0x7E) == 448.0
+    assert oracle.e4m3fn_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3fn_value(0x08) == 2.0 ** -6
+    assert np.isnan(oracle.e4m3fn_value(0x7F)) and np.isnan(oracle.e4m3fn_value(0xFF))
+    assert np.signbit(oracle.e4m3fn_value(0x80))
+
+
+def test_e8m0_decoder(oracle_lib):
+    bits = np.arange(256, dtype=np.int32).astype(np.uint8)
+    ref = torch.from_numpy(bits).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.e8m0_value(int(b)) for b in bits])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert oracle.e8m0_value(127) == 1.0 and oracle.e8m0_value(128) == 2.0 and oracle.e8m0_value(126) == 0.5
+
+
+# ----------------------------------------------------------------------------
+# the product: brute force, special cases, invariants
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_bf16_matches_numpy_brute_force(oracle_lib, seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 7))
+    counts = [int(x) for x in rng.integers(0, 5, size=E) * 8]
+    counts[int(rng.integers(0, E))] = 0
+    H, N = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+    T = sum(counts)
+    A = bf16_bits(rng.standard_normal((H, T)))
+    B = bf16_bits(rng.standard_normal((T, N)))
+    off = workloads.offsets_from_counts(counts)
+    W = oracle.wgrad_bf16(A, B, off)
+    ref = brute_force(bf16_to_f64(A), bf16_to_f64(B), counts)
+    assert W.shape == (E, H, N)
+    np.testing.assert_allclose(W, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_plain_gemm(oracle_lib):
+    rng = np.random.default_rng(7)
+    H, T, N = 17, 64, 23
+    A = bf16_bits(rng.standard_normal((H, T)))
+    B = bf16_bits(rng.standard_normal((T, N)))
+    W = oracle.wgrad_bf16(A, B, np.array([T], dtype=np.int32))
+    ref = torch.from_numpy(bf16_to_f64(A)) @ torch.from_numpy(bf16_to_f64(B))
+    np.testing.assert_allclose(W[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sum_over_experts_is_full_product(oracle_lib):
+    rng = np.random.default_rng(8)
+    counts = [32, 0, 96, 64, 0, 32]
+    H, N = 24, 40
+    T = sum(counts)
+    A = bf16_bits(rng.standard_normal((H, T)))
+    B = bf16_bits(rng.standard_normal((T, N)))
+    W = oracle.wgrad_bf16(A, B, workloads.offsets_from_counts(counts))
+    full = bf16_to_f64(A) @ bf16_to_f64(B)
+    np.testing.assert_allclose(W.sum(axis=0), full, rtol=1e-11, atol=1e-11)
+
+
+def test_integer_inputs_are_exact(oracle_lib):
+    rng = np.random.default_rng(9)
+    counts = [256, 0, 512, 256]
+    H, N = 20, 33
+    T = sum(counts)
+    Ai = rng.integers(-4, 5, size=(H, T))
+    Bi = rng.integers(-4, 5, size=(T, N))
+    W = oracle.wgrad_bf16(bf16_bits(Ai), bf16_bits(Bi), workloads.offsets_from_counts(counts))
+    start = 0
+    for e, c in enumerate(counts):
+        exact = Ai[:, start:start + c].astype(np.int64) @ Bi[start:start + c].astype(np.int64)
+        assert np.array_equal(W[e], exact.astype(np.float64))
+        start += c
+
+
+def test_empty_experts_are_zero(oracle_lib):
+    rng = np.random.default_rng(10)
+    H, N = 8, 8
+    A = bf16_bits(rng.standard_normal((H, 0)))
+    B = bf16_bits(rng.standard_normal((0, N)))
+    W = oracle.wgrad_bf16(A, B, np.array([0, 0, 0], dtype=np.int32))
+    assert W.shape == (3, H, N) and np.all(W == 0.0)
+    counts = [0, 16, 0]
+    A = bf16_bits(rng.standard_normal((H, 16)))
+    B = bf16_bits(rng.standard_normal((16, N)))
+    W = oracle.wgrad_bf16(A, B, workloads.offsets_from_counts(counts))
+    assert np.all(W[0] == 0.0) and np.all(W[2] == 0.0) and np.any(W[1] != 0.0)
+
+
+def test_power_of_two_scaling_is_exact(oracle_lib):
+    rng = np.random.default_rng(11)
+    counts = [48, 80]
+    H, N = 12, 20
+    A = rng.standard_normal((H, 128)).astype(np.float32)
+    B = bf16_bits(rng.standard_normal((128, N)))
+    off = workloads.offsets_from_counts(counts)
+    W1 = oracle.wgrad_bf16(bf16_bits(A), B, off)
+    W2 = oracle.wgrad_bf16(bf16_bits(bf16_to_f64(bf16_bits(A)) * 2.0), B, off)
+    assert np.array_equal(W2, 2.0 * W1)
+
+
+def test_token_permutation_within_expert(oracle_lib):
+    rng = np.random.default_rng(12)
+    counts = [64, 96]
+    H, N = 10, 14
+    A = bf16_bits(rng.standard_normal((H, 160)))
+    B = bf16_bits(rng.standard_normal((160, N)))
+    off = workloads.offsets_from_counts(counts)
+    W = oracle.wgrad_bf16(A, B, off)
+    perm = np.concatenate([rng.permutation(64), 64 + rng.permutation(96)])
+    Wp = oracle.wgrad_bf16(np.ascontiguousarray(A[:, perm]), np.ascontiguousarray(B[perm]), off)
+    np.testing.assert_allclose(Wp, W, rtol=1e-12, atol=1e-12)
+    # moving a token across the expert boundary must change both experts
+    swap = np.arange(160)
+    swap[63], swap[64] = 64, 63
+    Ws = oracle.wgrad_bf16(np.ascontiguousarray(A[:, swap]), np.ascontiguousarray(B[swap]), off)
+    assert not np.allclose(Ws[0], W[0]) and not np.allclose(Ws[1], W[1])
+
+
+def test_rows_agree_with_dense(oracle_lib):
+    wl = workloads.make_workload("tiny", seed=3)
+    W = oracle.wgrad_bf16(wl.A, wl.B, wl.offsets)
+    for e in range(wl.num_experts):
+        rows = [0, 17, 255]
+        np.testing.assert_array_equal(oracle.wgrad_rows_bf16(wl.A, wl.B, wl.offsets, e, rows), W[e][rows])
+
+
+def test_tiny_config_against_brute_force(oracle_lib):
+    wl = workloads.make_workload("tiny", seed=1)
+    W = oracle.wgrad_bf16(wl.A, wl.B, wl.offsets)
+    ref = brute_force(wl.A.double().numpy(), wl.B.double().numpy(), wl.counts)
+    np.testing.assert_allclose(W, ref, rtol=1e-12, atol=1e-10)
+    assert np.all(W[1] == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# fp8 block-scaled product
+# ----------------------------------------------------------------------------
+def dequant(q: torch.Tensor, s: torch.Tensor, token_axis: int) -> np.ndarray:
+    """Library-side dequantisation: torch float8 decode times 2^(s-127) per 128-token block."""
+    v = q.view(torch.float8_e4m3fn).double()
+    sc = torch.exp2(s.double() - 127.0).repeat_interleave(128, dim=0)    # (T, other)
+    if token_axis == 1:
+        sc = sc.t()
+    return (v * sc).numpy()
+
+
+def test_fp8_matches_dequantised_brute_force(oracle_lib):
+    counts = [128, 0, 256, 384]
+    wl = workloads.make_operands(counts, 24, 40, "fp8", torch.bfloat16, False, seed=5)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets)
+    ref = brute_force(dequant(wl.A, wl.sfa, 1), dequant(wl.B, wl.sfb, 0), counts)
+    np.testing.assert_allclose(W, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_block_scale_byte_doubles_its_block(oracle_lib):
+    counts = [256, 128]
+    wl = workloads.make_operands(counts, 8, 16, "fp8", torch.bfloat16, False, seed=6)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets)
+    # contribution of token block 1 (tokens 128..255, inside expert 0) to row 3
+    A1 = wl.A.clone()
+    A1[:, :128] = 0  # zero e4m3 byte is +0
+    A1[:, 256:] = 0
+    part = oracle.wgrad_fp8(A1, wl.sfa, wl.B, wl.sfb, wl.offsets)
+    sfa2 = wl.sfa.clone()
+    sfa2[1, 3] += 1
+    W2 = oracle.wgrad_fp8(wl.A, sfa2, wl.B, wl.sfb, wl.offsets)
+    np.testing.assert_allclose(W2[0, 3] - W[0, 3], part[0, 3], rtol=1e-12, atol=1e-12)
+    mask = np.ones_like(W, dtype=bool)
+    mask[0, 3] = False
+    assert np.array_equal(W2[mask], W[mask])
+
+
+def test_fp8_integer_inputs_are_exact(oracle_lib):
+    counts = [128, 256]
+    wl = workloads.make_operands(counts, 6, 10, "fp8", torch.bfloat16, False, seed=7, integer_range=8)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets)
+    Ai = wl.A.view(torch.float8_e4m3fn).double().numpy().astype(np.int64)
+    Bi = wl.B.view(torch.float8_e4m3fn).double().numpy().astype(np.int64)
+    assert np.array_equal(W[0], (Ai[:, :128] @ Bi[:128]).astype(np.float64))
+    assert np.array_equal(W[1], (Ai[:, 128:] @ Bi[128:]).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# rounding helpers used by the exactness comparisons
+# ----------------------------------------------------------------------------
+def test_round_to_bf16_matches_library(oracle_lib):
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 8, 20000),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875])])  # two exact ties
+    got = oracle.round_to_bf16(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_ulp_is_spacing(oracle_lib):
+    rng = np.random.default_rng(14)
+    x = oracle.round_to_bf16(rng.standard_normal(5000) * 100.0)
+    x = x[x > 0]
+    bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    nxt = (bits + 1).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(nxt - x, oracle.bf16_ulp(x))

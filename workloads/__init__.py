@@ -1,0 +1,273 @@
+"""Seeded synthetic inputs for the K-grouped weight-gradient GEMM.
+
+This module only *produces inputs*: per-expert token counts, the int32
+inclusive-cumulative offsets built from them, random operand matrices, and
+the fp8 test-data quantiser that turns bf16 operands into (e4m3 bytes,
+UE8M0 scale bytes) pairs.  It holds none of the grouped GEMM's arithmetic;
+both the CPU oracle (via the tests) and the HIP path consume what it makes.
+
+Shapes follow the cuDNN "Grouped GEMM + WGrad (Unified)" page, section
+"BF16 contract": A is (hidden, tokens_sum) with the token axis contiguous,
+B is (tokens_sum, intermediate) row-major, offsets is int32 (num_experts,),
+the dense output is (num_experts, hidden, intermediate).
+
+Count distributions:
+  * balanced / fp8: expected tokens per expert times U(0.7, 1.3), the
+    generator quoted on the llm-infra-atlas page, section 2.1 (contiguous
+    layout), rounded up to the alignment unit;
+  * skewed: 256 * round(lognormal(ln 16, 1)), four experts forced empty,
+    total capped at 262144 tokens;
+  * many-small: 65536 tokens over 256 experts, ~40% empty, the rest spread
+    by a Zipf(1.2) law over ranks (see ``counts_many_small``).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0          # largest finite OCP E4M3 ("fn") magnitude
+E8M0_BIAS = 127
+SCALE_BLOCK = 128         # tokens per fp8 scale block (1 x 128 along the token axis)
+
+
+# ----------------------------------------------------------------------------
+# per-expert token counts
+# ----------------------------------------------------------------------------
+def _roundup(x: np.ndarray, unit: int) -> np.ndarray:
+    return ((x + unit - 1) // unit) * unit
+
+
+def counts_tiny() -> List[int]:
+    return [256, 0, 512, 256]
+
+
+def counts_uniform(num_experts: int, expected: int, unit: int, seed: int) -> List[int]:
+    """expected * U(0.7, 1.3) tokens per expert, rounded up to `unit`."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(0.7, 1.3, size=num_experts)
+    n = np.ceil(expected * u).astype(np.int64)
+    return _roundup(n, unit).astype(int).tolist()
+
+
+def counts_skewed(seed: int, num_experts: int = 32, unit: int = 256,
+                  forced_zeros: int = 4, cap_tokens: int = 262144) -> List[int]:
+    """unit * round(lognormal(ln 16, 1)); `forced_zeros` experts emptied; total capped.
+
+    The cap rescales unit counts by floor(units * cap_units / sum(units)) when
+    the sum exceeds the cap; the forced-empty experts are drawn after sampling.
+    """
+    rng = np.random.default_rng(seed)
+    units = np.rint(rng.lognormal(mean=math.log(16.0), sigma=1.0, size=num_experts)).astype(np.int64)
+    zeros = rng.choice(num_experts, size=forced_zeros, replace=False)
+    units[zeros] = 0
+    cap_units = cap_tokens // unit
+    total = int(units.sum())
+    if total > cap_units:
+        units = (units * cap_units) // total
+    return (units * unit).astype(int).tolist()
+
+
+def counts_many_small(seed: int, num_experts: int = 256, tokens_sum: int = 65536,
+                      unit: int = 256, empty_frac: float = 0.4, zipf_s: float = 1.2) -> List[int]:
+    """Many small experts with a Zipf(1.2) tail and about 40% empty experts.
+
+    A seeded permutation picks round(empty_frac * E) empty experts; each of the
+    others gets one `unit` of tokens, and the remaining units are spread with
+    multinomial(remaining, p_r ~ r^-s) over the non-empty experts in permuted
+    rank order.  The total is exactly `tokens_sum`.
+    """
+    rng = np.random.default_rng(seed)
+    total_units = tokens_sum // unit
+    n_empty = int(round(empty_frac * num_experts))
+    perm = rng.permutation(num_experts)
+    nonempty = perm[n_empty:]
+    k = len(nonempty)
+    ranks = np.arange(1, k + 1, dtype=np.float64)
+    p = ranks ** (-zipf_s)
+    p /= p.sum()
+    units = np.ones(k, dtype=np.int64) + rng.multinomial(total_units - k, p)
+    counts = np.zeros(num_experts, dtype=np.int64)
+    counts[nonempty] = units * unit
+    return counts.astype(int).tolist()
+
+
+def offsets_from_counts(counts: List[int]) -> np.ndarray:
+    """int32 inclusive cumulative sum of per-expert token counts."""
+    return np.cumsum(np.asarray(counts, dtype=np.int64)).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# operands
+# ----------------------------------------------------------------------------
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn_bf16(shape, std: float, gen: torch.Generator, device) -> torch.Tensor:
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def randint_values(shape, lo: int, hi: int, gen: torch.Generator, device, dtype) -> torch.Tensor:
+    """Integer values in [lo, hi] stored in a float dtype (exact in bf16 / e4m3 for small ranges)."""
+    return torch.randint(lo, hi + 1, shape, generator=gen, device=device, dtype=torch.int32).to(dtype)
+
+
+def e8m0_exponent_for_block(amax: torch.Tensor) -> torch.Tensor:
+    """Biased UE8M0 exponent e with amax / 2^(e-127) <= 448 (127 where the block is all zero)."""
+    a = amax.to(torch.float64)
+    safe = torch.where(a > 0, a, torch.ones_like(a))
+    e = torch.ceil(torch.log2(safe / E4M3_MAX))
+    # guard against log2 rounding: bump where the scaled max would still exceed the range
+    e = torch.where(safe / torch.exp2(e) > E4M3_MAX, e + 1, e)
+    e = torch.where(a > 0, e, torch.zeros_like(e)) + E8M0_BIAS
+    return e.clamp_(1, 254).to(torch.uint8)
+
+
+def quantize_token_blocks(x: torch.Tensor, token_axis: int):
+    """Quantise a bf16/fp32 matrix to OCP e4m3fn with one UE8M0 scale per 128 tokens.
+
+    token_axis = 1 for A (hidden, tokens) and 0 for B (tokens, N).  Returns
+    (q, s): q holds e4m3fn bytes (uint8) in x's layout; s holds the biased
+    exponents (uint8) laid out (tokens/128, other_dim), i.e. mn-major.
+    Rounding: round-to-nearest-even in the float8 conversion.
+    """
+    xf = x.to(torch.float32)
+    if token_axis == 1:
+        xf = xf.t()                      # (tokens, other)
+    t, o = xf.shape
+    assert t % SCALE_BLOCK == 0, "token count must be a multiple of the scale block"
+    blocks = xf.reshape(t // SCALE_BLOCK, SCALE_BLOCK, o)
+    amax = blocks.abs().amax(dim=1)      # (t/128, o)
+    s = e8m0_exponent_for_block(amax)    # (t/128, o) uint8
+    scale = torch.exp2(s.to(torch.float32) - E8M0_BIAS)
+    q = (blocks / scale[:, None, :]).reshape(t, o).to(torch.float8_e4m3fn).view(torch.uint8)
+    if token_axis == 1:
+        q = q.t()
+    return q.contiguous(), s.contiguous()
+
+
+# ----------------------------------------------------------------------------
+# named workloads
+# ----------------------------------------------------------------------------
+@dataclass
+class Workload:
+    name: str
+    counts: List[int]
+    hidden: int
+    n: int
+    kind: str                     # "bf16" or "fp8"
+    out_dtype: torch.dtype
+    accumulate: bool
+    A: torch.Tensor = None        # bf16 (hidden, T) or uint8 e4m3 bytes
+    B: torch.Tensor = None        # bf16 (T, n) or uint8 e4m3 bytes
+    sfa: Optional[torch.Tensor] = None   # uint8 (T/128, hidden)
+    sfb: Optional[torch.Tensor] = None   # uint8 (T/128, n)
+    C0: Optional[torch.Tensor] = None    # initial output for accumulate mode
+    offsets: torch.Tensor = None         # int32 (E,)
+    meta: Dict = field(default_factory=dict)
+
+    @property
+    def num_experts(self) -> int:
+        return len(self.counts)
+
+    @property
+    def tokens_sum(self) -> int:
+        return int(sum(self.counts))
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.hidden * self.n * self.tokens_sum
+
+
+DESCRIPTIONS = {
+    "tiny": "tiny bf16 E=4 H=256 N=512 counts [256,0,512,256], fp32 out, overwrite",
+    "balanced": "balanced bf16 fc2-wgrad E=8 H=4096 N=2048 n_e=roundup256(4096*U(0.7,1.3)), bf16 out, overwrite",
+    "skewed": "skewed bf16 fc1-wgrad E=32 H=7168 N=4096 lognormal counts, 4 empty, fp32 out, accumulate",
+    "fp8": "fp8 e4m3 1x128 UE8M0 block-scaled E=32 H=7168 N=4096 n_e=roundup128(8192*U(0.7,1.3)), bf16 out, overwrite",
+    "many_small": "many-small bf16 E=256 H=7168 N=2048 tokens_sum=65536 Zipf(1.2) ~40% empty, fp32 out, overwrite",
+}
+
+
+def config_spec(name: str, seed: int = 1) -> Dict:
+    """Shape-only description of a named workload (no tensors)."""
+    if name == "tiny":
+        return dict(counts=counts_tiny(), hidden=256, n=512, kind="bf16", out_dtype=torch.float32,
+                    accumulate=False, std=1.0)
+    if name == "balanced":
+        return dict(counts=counts_uniform(8, 4096, 256, seed), hidden=4096, n=2048, kind="bf16",
+                    out_dtype=torch.bfloat16, accumulate=False, std=0.02)
+    if name == "skewed":
+        return dict(counts=counts_skewed(seed), hidden=7168, n=4096, kind="bf16", out_dtype=torch.float32,
+                    accumulate=True, std=1.0)
+    if name == "fp8":
+        return dict(counts=counts_uniform(32, 8192, 128, seed), hidden=7168, n=4096, kind="fp8",
+                    out_dtype=torch.bfloat16, accumulate=False, std=1.0)
+    if name == "many_small":
+        return dict(counts=counts_many_small(seed), hidden=7168, n=2048, kind="bf16", out_dtype=torch.float32,
+                    accumulate=False, std=1.0)
+    raise KeyError(name)
+
+
+def make_operands(counts: List[int], hidden: int, n: int, kind: str, out_dtype: torch.dtype,
+                  accumulate: bool, seed: int, device="cpu", std: float = 1.0,
+                  integer_range: Optional[int] = None, name: str = "custom") -> Workload:
+    """Build a Workload with tensors on `device`.
+
+    Draw order from one generator seeded with `seed`: A, then B, then the
+    initial output C0 (accumulate mode only).  With `integer_range=r` the
+    operands hold integers in [-r, r] instead of normals (for fp8 the integers
+    are stored exactly as e4m3 values with unit scales).
+    """
+    T = int(sum(counts))
+    g = _gen(seed, device)
+    wl = Workload(name=name, counts=list(map(int, counts)), hidden=hidden, n=n, kind=kind,
+                  out_dtype=out_dtype, accumulate=accumulate)
+    if integer_range is None:
+        A = randn_bf16((hidden, T), std, g, device)
+        B = randn_bf16((T, n), std, g, device)
+    else:
+        A = randint_values((hidden, T), -integer_range, integer_range, g, device, torch.bfloat16)
+        B = randint_values((T, n), -integer_range, integer_range, g, device, torch.bfloat16)
+    if kind == "bf16":
+        wl.A, wl.B = A, B
+    elif kind == "fp8":
+        if integer_range is None:
+            wl.A, wl.sfa = quantize_token_blocks(A, token_axis=1)
+            wl.B, wl.sfb = quantize_token_blocks(B, token_axis=0)
+        else:
+            wl.A = A.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+            wl.B = B.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+            wl.sfa = torch.full((T // SCALE_BLOCK, hidden), E8M0_BIAS, dtype=torch.uint8, device=device)
+            wl.sfb = torch.full((T // SCALE_BLOCK, n), E8M0_BIAS, dtype=torch.uint8, device=device)
+        del A, B
+    else:
+        raise ValueError(kind)
+    if accumulate:
+        E = len(counts)
+        if integer_range is None:
+            wl.C0 = torch.randn((E, hidden, n), generator=g, device=device, dtype=torch.float32).to(out_dtype)
+        else:
+            wl.C0 = randint_values((E, hidden, n), -integer_range, integer_range, g, device, out_dtype)
+    wl.offsets = torch.from_numpy(offsets_from_counts(counts)).to(device)
+    return wl
+
+
+def make_workload(name: str, seed: int = 1, device="cpu") -> Workload:
+    spec = config_spec(name, seed)
+    std = spec.pop("std")
+    wl = make_operands(seed=seed, device=device, std=std, name=name, **spec)
+    wl.meta["description"] = DESCRIPTIONS[name]
+    wl.meta["seed"] = seed
+    return wl
+
+
+CONFIG_NAMES = ["tiny", "balanced", "skewed", "fp8", "many_small"]
