@@ -1,0 +1,263 @@
+"""Python binding of libkgw: the K-grouped MoE weight-gradient GEMM for MI355X.
+
+For expert e with token range [begin, end) from int32 inclusive cumulative
+offsets (begin = 0 for the first expert, offsets[e-1] otherwise; end =
+offsets[e]) the library computes
+
+    Wgrad[e] = A[:, begin:end] @ B[begin:end, :]
+
+into a dense (num_experts, hidden, n) output, overwriting it or accumulating
+into it (cuDNN "Grouped GEMM + WGrad (Unified)", section "Operation").
+
+Every function here only marshals arguments (tensor shapes, dtypes, device
+pointers, the current HIP stream) and calls the C-ABI entry point of the
+same name in libkgw.so; all arithmetic runs in the library's HIP kernels.
+Status codes 1-4 raise ValueError, 5 raises RuntimeError (the cuDNN page,
+section "Scheduling, cache, and errors", splits errors the same way).
+There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_workspace_bytes", "kgw_validate_offsets",
+    "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
+    "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
+    "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16",
+    "BF16_TOKEN_ALIGN", "FP8_TOKEN_ALIGN", "library_path", "load_library",
+]
+
+KGW_SUCCESS = 0
+KGW_ERROR_INVALID_VALUE = 1
+KGW_ERROR_MISALIGNED = 2
+KGW_ERROR_BAD_OFFSETS = 3
+KGW_ERROR_UNSUPPORTED = 4
+KGW_ERROR_DEVICE = 5
+KGW_OUT_FP32 = 0
+KGW_OUT_BF16 = 1
+BF16_TOKEN_ALIGN = 256
+FP8_TOKEN_ALIGN = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkgw.so")
+_lib = None
+
+# Every symbol include/kgw.h declares.
+EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_workspace_bytes", "kgw_validate_offsets_host",
+                    "kgw_validate_offsets", "kgw_status_string", "kgw_device_info")
+
+
+def load_library():
+    """Load libkgw.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is missing: build it with "
+                           "`python -m grouped_gemm_expert_offsets_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kgw_wgrad_bf16.restype = ctypes.c_int
+    lib.kgw_wgrad_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_fp8.restype = ctypes.c_int
+    lib.kgw_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_fp8_native.restype = ctypes.c_int
+    lib.kgw_wgrad_fp8_native.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_workspace_bytes.restype = sz
+    lib.kgw_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+    lib.kgw_validate_offsets_host.restype = ctypes.c_int
+    lib.kgw_validate_offsets_host.argtypes = [p, i32, i64, i32, ctypes.POINTER(i32)]
+    lib.kgw_validate_offsets.restype = ctypes.c_int
+    lib.kgw_validate_offsets.argtypes = [p, i32, i64, i32, ctypes.POINTER(i32), p]
+    lib.kgw_status_string.restype = ctypes.c_char_p
+    lib.kgw_status_string.argtypes = [ctypes.c_int]
+    lib.kgw_device_info.restype = ctypes.c_int
+    lib.kgw_device_info.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    _lib = lib
+    return lib
+
+
+def kgw_status_string(status: int) -> str:
+    return load_library().kgw_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status == KGW_SUCCESS:
+        return
+    msg = f"{what}: {kgw_status_string(status)} (status {status})"
+    if status == KGW_ERROR_DEVICE:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _out_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return KGW_OUT_FP32
+    if dtype == torch.bfloat16:
+        return KGW_OUT_BF16
+    raise ValueError(f"output dtype must be float32 or bfloat16, got {dtype}")
+
+
+def _prepare_out(out, E, hidden, n, out_dtype, accumulate, device):
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an initialised `out`")
+        return torch.empty((E, hidden, n), dtype=out_dtype, device=device)
+    if tuple(out.shape) != (E, hidden, n):
+        raise ValueError(f"out must have shape {(E, hidden, n)}, got {tuple(out.shape)}")
+    if not out.is_contiguous() or out.device != device:
+        raise ValueError("out must be a contiguous tensor on the operands' device")
+    return out
+
+
+def _check_offsets(offsets: torch.Tensor, device):
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    if offsets.device != device:
+        raise ValueError("offsets must live on the operands' device")
+    if offsets.numel() < 1:
+        raise ValueError("need at least one expert")
+
+
+def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   *, out_dtype: torch.dtype = torch.float32, accumulate: bool = False, validate: bool = False,
+                   stream=None) -> torch.Tensor:
+    """bf16 A (hidden, tokens_sum) token-contiguous, B (tokens_sum, n) row-major -> out (E, hidden, n).
+
+    validate=True first checks the offsets on the host (one synchronising copy).
+    """
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("kgw_wgrad_bf16 takes bfloat16 A and B")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (A token-contiguous, B row-major)")
+    device = A.device
+    if B.device != device:
+        raise ValueError("A and B must be on the same device")
+    _check_offsets(offsets, device)
+    hidden, T = A.shape
+    n = B.shape[1]
+    E = offsets.numel()
+    if out is not None:
+        out_dtype = out.dtype
+    code = _out_code(out_dtype)
+    out = _prepare_out(out, E, hidden, n, out_dtype, accumulate, device)
+    if validate:
+        kgw_validate_offsets(offsets, T, BF16_TOKEN_ALIGN, stream=stream)
+    st = load_library().kgw_wgrad_bf16(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
+                                       int(bool(accumulate)), None, 0, _stream_ptr(stream))
+    _check(st, "kgw_wgrad_bf16")
+    return out
+
+
+def kgw_wgrad_fp8(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.bfloat16,
+                  accumulate: bool = False, validate: bool = False, stream=None) -> torch.Tensor:
+    """e4m3 A (hidden, T) with UE8M0 sfa (T/128, hidden); e4m3 B (T, n) with sfb (T/128, n)."""
+    return _fp8_call("kgw_wgrad_fp8", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream)
+
+
+def kgw_wgrad_fp8_native(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor,
+                         offsets: torch.Tensor, out: Optional[torch.Tensor] = None, *,
+                         out_dtype: torch.dtype = torch.bfloat16, accumulate: bool = False, validate: bool = False,
+                         stream=None) -> torch.Tensor:
+    """kgw_wgrad_fp8 on the native scaled fp8 MFMA (faster, ~13-bit in-group alignment; see include/kgw.h)."""
+    return _fp8_call("kgw_wgrad_fp8_native", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate,
+                     stream)
+
+
+def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream):
+    fp8_types = (torch.uint8, torch.float8_e4m3fn)
+    if A.dtype not in fp8_types or B.dtype not in fp8_types:
+        raise ValueError(f"{name} takes e4m3fn (or raw uint8) A and B")
+    if sfa is None or sfb is None:
+        raise ValueError(f"{name} needs both scale tensors sfa and sfb")
+    if sfa.dtype != torch.uint8 or sfb.dtype != torch.uint8:
+        raise ValueError("sfa and sfb hold UE8M0 exponent bytes (uint8)")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    hidden, T = A.shape
+    n = B.shape[1]
+    if tuple(sfa.shape) != (T // FP8_TOKEN_ALIGN, hidden) or tuple(sfb.shape) != (T // FP8_TOKEN_ALIGN, n):
+        raise ValueError(f"scale shapes must be {(T // FP8_TOKEN_ALIGN, hidden)} and {(T // FP8_TOKEN_ALIGN, n)}")
+    for t in (A, B, sfa, sfb):
+        if not t.is_contiguous():
+            raise ValueError("fp8 operands and scales must be contiguous")
+    device = A.device
+    if any(t.device != device for t in (B, sfa, sfb)):
+        raise ValueError("operands and scales must be on the same device")
+    _check_offsets(offsets, device)
+    E = offsets.numel()
+    if out is not None:
+        out_dtype = out.dtype
+    code = _out_code(out_dtype)
+    out = _prepare_out(out, E, hidden, n, out_dtype, accumulate, device)
+    if validate:
+        kgw_validate_offsets(offsets, T, FP8_TOKEN_ALIGN, stream=stream)
+    fn = getattr(load_library(), name)
+    st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
+            int(bool(accumulate)), None, 0, _stream_ptr(stream))
+    _check(st, name)
+    return out
+
+
+def kgw_workspace_bytes(num_experts: int, hidden: int, n: int, tokens_sum: int, fp8: bool = False) -> int:
+    return int(load_library().kgw_workspace_bytes(num_experts, hidden, n, tokens_sum, int(bool(fp8))))
+
+
+def kgw_validate_offsets_host(offsets, tokens_sum: int, alignment: int) -> Tuple[int, int]:
+    """Check host offsets (sequence or CPU tensor); returns (status, first bad expert or -1)."""
+    t = torch.as_tensor(offsets, dtype=torch.int32).contiguous()
+    if t.device.type != "cpu":
+        raise ValueError("kgw_validate_offsets_host takes host offsets")
+    bad = ctypes.c_int32(-1)
+    st = load_library().kgw_validate_offsets_host(t.data_ptr(), t.numel(), int(tokens_sum), int(alignment),
+                                                  ctypes.byref(bad))
+    return int(st), int(bad.value)
+
+
+def kgw_validate_offsets(offsets: torch.Tensor, tokens_sum: int, alignment: int, stream=None) -> None:
+    """Check device offsets (synchronising); raises ValueError naming the first bad expert."""
+    bad = ctypes.c_int32(-1)
+    st = load_library().kgw_validate_offsets(_ptr(offsets), offsets.numel(), int(tokens_sum), int(alignment),
+                                             ctypes.byref(bad), _stream_ptr(stream))
+    if st != KGW_SUCCESS:
+        _check(st, f"kgw_validate_offsets (first bad expert {bad.value})")
+
+
+def kgw_device_info() -> dict:
+    cus, g950, xcds = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().kgw_device_info(ctypes.byref(cus), ctypes.byref(g950), ctypes.byref(xcds)),
+           "kgw_device_info")
+    return {"num_cus": cus.value, "is_gfx950": bool(g950.value), "num_xcds": xcds.value}
+
+
+def wgrad(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, *, sfa: Optional[torch.Tensor] = None,
+          sfb: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+          out_dtype: Optional[torch.dtype] = None, accumulate: bool = False, validate: bool = False) -> torch.Tensor:
+    """Dispatch on operand dtype like the cuDNN wrapper: bf16 operands take no scales
+    (any scale is a ValueError, section "BF16 contract"); fp8 operands need both."""
+    if a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16:
+        if sfa is not None or sfb is not None:
+            raise ValueError("bf16 operands take no scale tensors")
+        return kgw_wgrad_bf16(a, b, offsets, out, out_dtype=out_dtype or torch.float32, accumulate=accumulate,
+                              validate=validate)
+    if a.dtype in (torch.float8_e4m3fn, torch.uint8) and b.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return kgw_wgrad_fp8(a, sfa, b, sfb, offsets, out, out_dtype=out_dtype or torch.bfloat16,
+                             accumulate=accumulate, validate=validate)
+    raise ValueError(f"unsupported operand dtypes {a.dtype}, {b.dtype}")

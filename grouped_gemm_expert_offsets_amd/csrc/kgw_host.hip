@@ -1,0 +1,217 @@
+// C-ABI layer: argument checks, per-device properties, dispatch to the kernels.
+// Declarations and the contract of every entry point are in include/kgw.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+#include <vector>
+
+#include "../../include/kgw.h"
+#include "kgw_internal.h"
+
+namespace {
+
+struct DeviceProps {
+    int num_cus = 0;
+    int is_gfx950 = 0;
+    int num_xcds = 1;
+    bool ok = false;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DeviceProps g_props[kMaxDevices];
+
+kgw_status_t current_props(DeviceProps* out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KGW_ERROR_DEVICE;
+    std::call_once(g_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+        DeviceProps& d = g_props[dev];
+        d.num_cus = prop.multiProcessorCount;
+        d.is_gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        // MI355X: 8 XCDs of 32 CUs; workgroups are dispatched round-robin over XCDs.
+        d.num_xcds = (d.is_gfx950 && d.num_cus % 8 == 0) ? 8 : 1;
+        d.ok = d.num_cus > 0;
+    });
+    if (!g_props[dev].ok) return KGW_ERROR_DEVICE;
+    *out = g_props[dev];
+    return KGW_SUCCESS;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by both entry points; everything here is pure host logic.
+kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
+                          int64_t hidden, int64_t n, int64_t tokens_sum, const void* out,
+                          int32_t out_dtype, int32_t accumulate, int64_t token_align, int64_t n_align,
+                          int64_t bm, int64_t bn) {
+    if (num_experts < 1 || hidden < 0 || n < 0 || tokens_sum < 0) return KGW_ERROR_INVALID_VALUE;
+    if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16) return KGW_ERROR_INVALID_VALUE;
+    if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
+    if (!offsets) return KGW_ERROR_INVALID_VALUE;
+    const bool has_output = hidden > 0 && n > 0;
+    if (has_output && !out) return KGW_ERROR_INVALID_VALUE;
+    if (tokens_sum > 0 && has_output && (!A || !B)) return KGW_ERROR_INVALID_VALUE;
+    if (num_experts > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
+    if (tokens_sum > INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    if (tokens_sum % token_align != 0) return KGW_ERROR_BAD_OFFSETS;
+    if (n % n_align != 0) return KGW_ERROR_MISALIGNED;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || ((uintptr_t)offsets & 3u))
+        return KGW_ERROR_MISALIGNED;
+    // The kernels address one tile's rows with 32-bit byte offsets.
+    if (bm * tokens_sum * 2 >= (int64_t)1 << 32 || 64 * n * 2 >= (int64_t)1 << 31) return KGW_ERROR_UNSUPPORTED;
+    const int64_t tiles = ((hidden + bm - 1) / bm) * ((n + bn - 1) / bn);
+    if (tiles * (int64_t)num_experts >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    return KGW_SUCCESS;
+}
+
+enum class Kernel { kBf16, kFp8, kFp8Native };
+
+kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
+                 const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                 int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate, void* stream) {
+    const bool fp8 = kernel != Kernel::kBf16;
+    const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
+    const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
+    const int64_t talign = fp8 ? KGW_FP8_TOKEN_ALIGN : KGW_BF16_TOKEN_ALIGN;
+    const int64_t nalign = fp8 ? 16 : 8;
+    kgw_status_t st = check_common(A, B, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
+                                   accumulate, talign, nalign, bm, bn);
+    if (st != KGW_SUCCESS) return st;
+    if (fp8 && tokens_sum > 0 && hidden > 0 && n > 0 && (!sfa || !sfb)) return KGW_ERROR_INVALID_VALUE;
+    if (hidden == 0 || n == 0) return KGW_SUCCESS;                 // no output elements
+    if (accumulate && tokens_sum == 0) return KGW_SUCCESS;         // adds nothing
+
+    DeviceProps d;
+    st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+
+    kgw::GroupedParams p;
+    p.A = A;
+    p.B = B;
+    p.sfa = sfa;
+    p.sfb = sfb;
+    p.offsets = offsets;
+    p.out = out;
+    p.hidden = hidden;
+    p.n = n;
+    p.tokens_sum = tokens_sum;
+    p.num_experts = num_experts;
+    p.tiles_m = (int32_t)((hidden + bm - 1) / bm);
+    p.tiles_n = (int32_t)((n + bn - 1) / bn);
+    p.num_items = p.tiles_m * p.tiles_n * num_experts;
+    p.accumulate = accumulate;
+    p.num_xcds = d.num_xcds;
+    const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
+    const bool out_bf16 = out_dtype == KGW_OUT_BF16;
+    hipError_t err;
+    switch (kernel) {
+        case Kernel::kBf16: err = kgw::launch_wgrad_bf16(p, out_bf16, grid, (hipStream_t)stream); break;
+        case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_bf16, grid, (hipStream_t)stream); break;
+        default: err = kgw::launch_wgrad_fp8_native(p, out_bf16, grid, (hipStream_t)stream); break;
+    }
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
+                            int64_t hidden, int64_t n, int64_t tokens_sum, void* out, int32_t out_dtype,
+                            int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return run(Kernel::kBf16, A, nullptr, B, nullptr, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
+               accumulate, stream);
+}
+
+kgw_status_t kgw_wgrad_fp8(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
+                           const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                           int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return run(Kernel::kFp8, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
+               accumulate, stream);
+}
+
+kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
+                                  const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                                  int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return run(Kernel::kFp8Native, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
+               accumulate, stream);
+}
+
+size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int32_t fp8) {
+    (void)num_experts;
+    (void)hidden;
+    (void)n;
+    (void)tokens_sum;
+    (void)fp8;
+    return 0;
+}
+
+kgw_status_t kgw_validate_offsets_host(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                                       int32_t alignment, int32_t* bad_expert) {
+    if (bad_expert) *bad_expert = -1;
+    if (!offsets || num_experts < 1 || alignment < 1) return KGW_ERROR_INVALID_VALUE;
+    int64_t prev = 0;
+    for (int32_t e = 0; e < num_experts; ++e) {
+        const int64_t cur = offsets[e];
+        const int64_t count = cur - prev;
+        if (count < 0 || count % alignment != 0) {
+            if (bad_expert) *bad_expert = e;
+            return KGW_ERROR_BAD_OFFSETS;
+        }
+        prev = cur;
+    }
+    if (prev != tokens_sum) {
+        if (bad_expert) *bad_expert = num_experts - 1;
+        return KGW_ERROR_BAD_OFFSETS;
+    }
+    return KGW_SUCCESS;
+}
+
+kgw_status_t kgw_validate_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                                  int32_t alignment, int32_t* bad_expert, void* stream) {
+    if (bad_expert) *bad_expert = -1;
+    if (!offsets || num_experts < 1 || alignment < 1) return KGW_ERROR_INVALID_VALUE;
+    std::vector<int32_t> host((size_t)num_experts);
+    if (hipMemcpyAsync(host.data(), offsets, sizeof(int32_t) * (size_t)num_experts, hipMemcpyDeviceToHost,
+                       (hipStream_t)stream) != hipSuccess)
+        return KGW_ERROR_DEVICE;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KGW_ERROR_DEVICE;
+    return kgw_validate_offsets_host(host.data(), num_experts, tokens_sum, alignment, bad_expert);
+}
+
+const char* kgw_status_string(kgw_status_t status) {
+    switch (status) {
+        case KGW_SUCCESS: return "success";
+        case KGW_ERROR_INVALID_VALUE: return "invalid value (null pointer, bad size, dtype or flag)";
+        case KGW_ERROR_MISALIGNED: return "misaligned pointer or n not a multiple of the vector width";
+        case KGW_ERROR_BAD_OFFSETS: return "malformed or unaligned offsets / tokens_sum";
+        case KGW_ERROR_UNSUPPORTED: return "size outside what the kernels support";
+        case KGW_ERROR_DEVICE: return "no usable gfx950 device or a HIP error";
+    }
+    return "unknown status";
+}
+
+kgw_status_t kgw_device_info(int32_t* num_cus, int32_t* is_gfx950, int32_t* num_xcds) {
+    DeviceProps d;
+    kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (num_cus) *num_cus = d.num_cus;
+    if (is_gfx950) *is_gfx950 = d.is_gfx950;
+    if (num_xcds) *num_xcds = d.num_xcds;
+    return KGW_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Host/device launch contract between the C-ABI layer (kgw_host.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kgw {
+
+// Largest expert count whose clamped offsets fit the kernels' LDS table.
+constexpr int kMaxExperts = 4096;
+
+struct GroupedParams {
+    const void* A;          // (hidden, tokens_sum), token axis contiguous
+    const void* B;          // (tokens_sum, n), row-major
+    const uint8_t* sfa;     // fp8 only: (tokens_sum/128, hidden) UE8M0 bytes
+    const uint8_t* sfb;     // fp8 only: (tokens_sum/128, n) UE8M0 bytes
+    const int32_t* offsets; // (num_experts,) inclusive cumulative token counts
+    void* out;              // (num_experts, hidden, n) fp32 or bf16
+    int64_t hidden;
+    int64_t n;
+    int64_t tokens_sum;
+    int32_t num_experts;
+    int32_t tiles_m;        // ceil(hidden / BM)
+    int32_t tiles_n;        // ceil(n / BN)
+    int32_t num_items;      // num_experts * tiles_m * tiles_n
+    int32_t accumulate;     // 1: out += W, 0: out = W
+    int32_t num_xcds;       // XCD count used to remap workgroup ids
+};
+
+// Tile shape of the bf16 and fp8 kernels (output tile BM x BN, K step BK).
+constexpr int kBf16BM = 256, kBf16BN = 256, kBf16BK = 64;
+constexpr int kFp8BM = 256, kFp8BN = 256, kFp8BK = 128;
+
+hipError_t launch_wgrad_bf16(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_wgrad_fp8(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_wgrad_fp8_native(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+
+}  // namespace kgw

@@ -1,0 +1,79 @@
+// Output side shared by the kernels: zero-filling a tile of an empty expert and
+// writing a wave's accumulators (overwrite or accumulate, fp32 or bf16).
+#pragma once
+
+#include "kgw_device.h"
+#include "kgw_internal.h"
+
+namespace kgw {
+
+// Overwrite-mode output of an expert without tokens: +0.0 over the tile
+// [m0, m0+BM) x [n0, n0+BN) of out[e], clipped to (hidden, n).
+template <bool OUT_BF16, int BM, int BN, int NT>
+__device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t m0, int64_t n0, int tid) {
+    constexpr int ESIZE = OUT_BF16 ? 2 : 4;
+    constexpr int PER_CHUNK = 16 / ESIZE;
+    const int rows = (int)min<int64_t>(BM, p.hidden - m0);
+    const int cols = (int)min<int64_t>(BN, p.n - n0);
+    const int cpr = cols / PER_CHUNK;  // n is a multiple of 8: whole 16-byte chunks
+    const int total = rows * cpr;
+    char* base = (char*)p.out + (((int64_t)e * p.hidden + m0) * p.n + n0) * ESIZE;
+    const i32x4 z = {0, 0, 0, 0};
+    for (int c = tid; c < total; c += NT) {
+        const int r = c / cpr;
+        const int q = c - r * cpr;
+        *(i32x4*)(base + ((int64_t)r * p.n + q * PER_CHUNK) * ESIZE) = z;
+    }
+}
+
+// A wave's 128x128 quarter of the tile, held as 4 (N blocks j) x 4 (M blocks i)
+// MFMA 32x32 accumulators of the transposed product: acc[j][i][4g + t] is
+// out[m][n] with m = mb + 32i + (lane & 31) and n = nb + 32j + 8g + 4*(lane >> 5) + t.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_wave_tile(const GroupedParams& p, int e, int64_t mb, int64_t nb,
+                                                int lane, const f32x16 (&acc)[4][4]) {
+    constexpr int ESIZE = OUT_BF16 ? 2 : 4;
+    const int64_t H = p.hidden, N = p.n;
+    const int l32 = lane & 31, lhi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = mb + 32 * i + l32;
+        if (m >= H) continue;
+        char* rowp = (char*)p.out + (((int64_t)e * H + m) * N) * ESIZE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t nn = nb + 32 * j + 8 * g + 4 * lhi;
+                if (nn >= N) continue;
+                float v0 = acc[j][i][4 * g + 0], v1 = acc[j][i][4 * g + 1];
+                float v2 = acc[j][i][4 * g + 2], v3 = acc[j][i][4 * g + 3];
+                if constexpr (OUT_BF16) {
+                    i32x2* dst = (i32x2*)(rowp + nn * 2);
+                    if (p.accumulate) {
+                        const i32x2 old = *dst;
+                        v0 += bf16_lo((uint32_t)old[0]);
+                        v1 += bf16_hi((uint32_t)old[0]);
+                        v2 += bf16_lo((uint32_t)old[1]);
+                        v3 += bf16_hi((uint32_t)old[1]);
+                    }
+                    const i32x2 w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
+                    *dst = w;
+                } else {
+                    f32x4* dst = (f32x4*)(rowp + nn * 4);
+                    if (p.accumulate) {
+                        const f32x4 old = *dst;
+                        v0 += old[0];
+                        v1 += old[1];
+                        v2 += old[2];
+                        v3 += old[3];
+                    }
+                    const f32x4 w = {v0, v1, v2, v3};
+                    *dst = w;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace kgw

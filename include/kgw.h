@@ -1,0 +1,193 @@
+/*
+ * kgw.h -- K-grouped MoE weight-gradient GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (cuDNN "Grouped GEMM + WGrad (Unified)", section "Operation";
+ * llm-infra-atlas "05 Grouped GEMM", section 5.2 "wgrad: k-grouped GEMM"):
+ * for expert e, with begin = 0 for e == 0 and offsets[e-1] otherwise and
+ * end = offsets[e],
+ *
+ *     Wgrad[e] = A[:, begin:end] @ B[begin:end, :]
+ *
+ * The contracted axis is the token axis; each expert's token count is only
+ * known on the device.  One call computes every expert in one persistent
+ * kernel launch on `stream`.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named A, B, sfa, sfb, offsets, out and workspace are DEVICE
+ *    pointers on the current HIP device.  The caller owns every buffer and
+ *    keeps it alive until the work queued on `stream` has finished (same
+ *    page, section "Output modes": caller-owned allocations).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *  - Calls are asynchronous and stream-ordered: no device-to-host transfer,
+ *    no synchronisation, no allocation (except kgw_validate_offsets, which is
+ *    documented as synchronous).  The library keeps no mutable global state
+ *    other than a per-device property cache; it is thread-safe.
+ *  - Errors are returned as kgw_status_t; nothing is thrown across the ABI.
+ *    Every argument check happens on the host before anything is enqueued, so
+ *    a failed call leaves the output untouched.
+ *  - Offsets are NOT read on the host by kgw_wgrad_*.  Malformed offsets
+ *    (decreasing, unaligned counts, last value != tokens_sum) are the caller's
+ *    to rule out, e.g. with kgw_validate_offsets.  The kernels clamp every
+ *    token range into [0, tokens_sum) and round it down to the kernel's K
+ *    step, so malformed offsets can give wrong values for the experts they
+ *    touch but never an out-of-bounds access.
+ */
+#ifndef KGW_H
+#define KGW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The cuDNN page (section "Scheduling, cache, and errors")
+ * splits its errors into ValueError (contract violations) and RuntimeError
+ * (device trouble); the Python binding maps codes 1-4 to ValueError and 5 to
+ * RuntimeError. */
+typedef enum {
+    KGW_SUCCESS = 0,
+    KGW_ERROR_INVALID_VALUE = 1, /* NULL pointer where data is needed, num_experts < 1,
+                                    negative size, unknown out_dtype, accumulate not 0/1   */
+    KGW_ERROR_MISALIGNED = 2,    /* a pointer not 16-byte aligned, or n not a multiple of
+                                    8 (bf16) / 16 (fp8) elements                           */
+    KGW_ERROR_BAD_OFFSETS = 3,   /* decreasing offsets, a count not a multiple of the
+                                    alignment or offsets[E-1] != tokens_sum (from the
+                                    kgw_validate_offsets* calls); tokens_sum not a multiple
+                                    of the alignment (from every call)                     */
+    KGW_ERROR_UNSUPPORTED = 4,   /* a size beyond what the kernels index (see below)       */
+    KGW_ERROR_DEVICE = 5         /* no HIP device, device is not gfx950, or a HIP call or
+                                    kernel launch failed                                   */
+} kgw_status_t;
+
+/* Output element type of the dense (num_experts, hidden, n) result. */
+typedef enum {
+    KGW_OUT_FP32 = 0,
+    KGW_OUT_BF16 = 1
+} kgw_out_dtype_t;
+
+/* Token-count alignment each entry point requires (cuDNN page, section "BF16
+ * contract": every count a multiple of 256 for BF16; for fp8 one UE8M0 scale
+ * block, llm-infra-atlas section 3, is 128 tokens). */
+#define KGW_BF16_TOKEN_ALIGN 256
+#define KGW_FP8_TOKEN_ALIGN 128
+
+/*
+ * kgw_wgrad_bf16 -- bf16 operands, fp32 accumulation (cuDNN page, "BF16 contract":
+ * FP32 accumulation for BF16 inputs).
+ *
+ *   A        bf16 (hidden, tokens_sum), row-major: the token axis is contiguous
+ *            (the page's K-major A, stride (tokens_sum, 1)).
+ *   B        bf16 (tokens_sum, n), row-major (the page's N-major B, stride (n, 1)).
+ *   offsets  int32 (num_experts,), inclusive cumulative token counts.
+ *            Contract: non-decreasing, every count a multiple of 256,
+ *            offsets[num_experts-1] == tokens_sum.
+ *   out      dense (num_experts, hidden, n), row-major, element type out_dtype.
+ *   accumulate  1: out[e] += Wgrad[e] (out must be initialised; an empty expert is
+ *                  left untouched, bit for bit);
+ *               0: out[e]  = Wgrad[e] (an empty expert is written with +0.0).
+ *            Section "Operation" of the cuDNN page defines both modes.
+ *   workspace, workspace_bytes  reserved; pass NULL and 0 (kgw_workspace_bytes
+ *            returns 0 for every shape this version supports).
+ *
+ * Sizes: 1 <= num_experts <= 65536; hidden, n >= 0; tokens_sum >= 0 and a
+ * multiple of 256; n a multiple of 8; tokens_sum < 2^31 (int32 offsets).
+ * tokens_sum == 0 (or hidden == 0, or n == 0) is valid: overwrite writes zeros,
+ * accumulate does nothing; A and B may then be NULL.  A, B and out must be
+ * 16-byte aligned.
+ */
+kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets,
+                            int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
+                            void* out, int32_t out_dtype, int32_t accumulate,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kgw_wgrad_fp8 -- OCP e4m3 ("fn") operands with one power-of-two (UE8M0) scale per
+ * 128 tokens, applied inside the K loop, fp32 accumulation (llm-infra-atlas
+ * "05 Grouped GEMM", section 3: per-block 1x128 scaling, UE8M0 scales, fp8
+ * consumed directly without a separate dequantisation pass; for the weight
+ * gradient the blocks run along the contracted token axis, section 5.2).
+ * Operands stay fp8 in memory; inside the K loop each fragment is converted
+ * exactly to bf16 with its scale folded in and multiplied on the bf16 MFMA, so
+ * the only rounding is the fp32 accumulation (see kgw_wgrad_fp8_native for the
+ * native fp8 MFMA variant).
+ *
+ *   A    e4m3 bytes (hidden, tokens_sum), token axis contiguous.
+ *   sfa  uint8 (tokens_sum/128, hidden): sfa[b][m] is the biased exponent of the
+ *        scale of A[m, 128b : 128b+128]; value 2^(byte-127).
+ *   B    e4m3 bytes (tokens_sum, n), row-major.
+ *   sfb  uint8 (tokens_sum/128, n): scale exponent of B[128b : 128b+128, j].
+ *   The real operand value is e4m3(q) * 2^(s - 127); a scale byte of 0xFF encodes
+ *   NaN and, like a NaN operand, makes the affected outputs NaN.
+ *   Counts must be multiples of 128; n a multiple of 16.  Everything else as for
+ *   kgw_wgrad_bf16 (out_dtype, accumulate, workspace, sizes, alignment).
+ */
+kgw_status_t kgw_wgrad_fp8(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
+                           const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                           int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kgw_wgrad_fp8_native -- same arguments, contract and results' definition as
+ * kgw_wgrad_fp8, computed with the native scaled fp8 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4: the UE8M0 bytes go straight into the
+ * instruction, as the scaled-MFMA reading of llm-infra-atlas section 3 suggests).
+ * Faster, but less accurate: inside one instruction the hardware aligns the
+ * products of a K group to the group's largest one and keeps only about 13 bits
+ * below it, so a result can differ from the exactly rounded sum by up to about
+ * 2^-13 of the largest product in each 32-token group (relative Frobenius error
+ * about 1.5e-5 on block-quantised Gaussian data, versus about 1e-7 for
+ * kgw_wgrad_fp8).  Integer-valued operands whose products share a binade range
+ * of less than 2^13 are exact.
+ */
+kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
+                                  const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                                  int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call needs for this shape
+ * (fp8 != 0 selects the fp8 entry point).  0 means none; this version always
+ * returns 0.
+ */
+size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
+                           int32_t fp8);
+
+/*
+ * kgw_validate_offsets_host -- check HOST offsets against the contract of the
+ * cuDNN page, section "BF16 contract": non-decreasing, every count
+ * (offsets[e] - offsets[e-1], offsets[0] for e == 0) a non-negative multiple of
+ * `alignment`, and offsets[num_experts-1] == tokens_sum.
+ * Returns KGW_SUCCESS or KGW_ERROR_BAD_OFFSETS (KGW_ERROR_INVALID_VALUE for
+ * NULL / num_experts < 1 / alignment < 1).  If bad_expert is not NULL it receives
+ * the first offending expert index (-1 on success).  Pure host code.
+ */
+kgw_status_t kgw_validate_offsets_host(const int32_t* offsets, int32_t num_experts,
+                                       int64_t tokens_sum, int32_t alignment,
+                                       int32_t* bad_expert);
+
+/*
+ * kgw_validate_offsets -- the same check on DEVICE offsets.  SYNCHRONOUS: copies the
+ * num_experts int32 values to the host after the work already queued on `stream`.
+ */
+kgw_status_t kgw_validate_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                                  int32_t alignment, int32_t* bad_expert, void* stream);
+
+/*
+ * kgw_status_string -- static description of a status code; never NULL.
+ */
+const char* kgw_status_string(kgw_status_t status);
+
+/*
+ * kgw_device_info -- properties of the current device as the library sees them:
+ * compute units, whether it is gfx950 (1/0), and the number of XCDs the
+ * workgroup remapping assumes.  Any output pointer may be NULL.
+ */
+kgw_status_t kgw_device_info(int32_t* num_cus, int32_t* is_gfx950, int32_t* num_xcds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KGW_H */

@@ -1,0 +1,140 @@
+"""C-ABI library checks that need no GPU: symbols, host validation, argument errors.
+
+Every call made here is rejected by the host-side argument checks (or is a
+pure host function), so nothing is ever enqueued on a device.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import grouped_gemm_expert_offsets_amd as kgw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kgw.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kgw_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kgw.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 7
+    for name in names:
+        assert hasattr(lib, name), f"libkgw.so does not export {name}"
+    assert sorted(kgw.EXPORTED_SYMBOLS) == names
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = kgw.kgw_status_string(code)
+        assert isinstance(s, str) and s
+    assert kgw.kgw_status_string(99) == "unknown status"
+
+
+def test_workspace_is_zero(lib):
+    assert kgw.kgw_workspace_bytes(8, 4096, 2048, 35584) == 0
+    assert kgw.kgw_workspace_bytes(32, 7168, 4096, 264320, fp8=True) == 0
+
+
+def validate(offsets, tokens_sum, align=256):
+    return kgw.kgw_validate_offsets_host(offsets, tokens_sum, align)
+
+
+def test_validate_offsets_host_accepts_contract():
+    assert validate([256, 256, 768, 1024], 1024) == (kgw.KGW_SUCCESS, -1)
+    assert validate([0, 0, 0], 0) == (kgw.KGW_SUCCESS, -1)
+    assert validate([128, 384], 384, 128) == (kgw.KGW_SUCCESS, -1)
+
+
+def test_validate_offsets_host_rejections():
+    assert validate([512, 256, 1024], 1024) == (kgw.KGW_ERROR_BAD_OFFSETS, 1)      # decreasing
+    assert validate([256, 300, 512], 512) == (kgw.KGW_ERROR_BAD_OFFSETS, 1)        # unaligned count
+    assert validate([256, 512], 768) == (kgw.KGW_ERROR_BAD_OFFSETS, 1)             # last != tokens_sum
+    assert validate([-256, 0], 0) == (kgw.KGW_ERROR_BAD_OFFSETS, 0)                # negative count
+    assert validate([128, 256], 256, 256)[0] == kgw.KGW_ERROR_BAD_OFFSETS          # fp8-aligned, bf16 rule
+    st, _ = kgw.kgw_validate_offsets_host([256], 256, 0)
+    assert st == kgw.KGW_ERROR_INVALID_VALUE
+
+
+def test_page_example_counts_are_rejected():
+    g = json.load(open(os.path.join(GOLDEN, "p1_example_counts.json")))
+    counts = g["tokens_per_expert"]
+    offs, acc = [], 0
+    for c in counts:
+        acc += c
+        offs.append(acc)
+    st, bad = validate(offs, acc, 256)
+    assert st == kgw.KGW_ERROR_BAD_OFFSETS and bad == g["first_bad_expert"]
+
+
+# ----------------------------------------------------------------------------
+# argument errors of the compute entry points (rejected before any HIP call)
+# ----------------------------------------------------------------------------
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def call_bf16(lib, A=FAKE, B=FAKE, off=FAKE, E=4, H=256, N=512, T=1024, out=FAKE, dt=0, acc=0):
+    return lib.kgw_wgrad_bf16(A, B, off, E, H, N, T, out, dt, acc, None, 0, None)
+
+
+def call_fp8(lib, A=FAKE, sa=FAKE, B=FAKE, sb=FAKE, off=FAKE, E=4, H=256, N=512, T=1024, out=FAKE, dt=1, acc=0):
+    return lib.kgw_wgrad_fp8(A, sa, B, sb, off, E, H, N, T, out, dt, acc, None, 0, None)
+
+
+def test_bf16_argument_errors(lib):
+    assert call_bf16(lib, E=0) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, H=-1) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, dt=7) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, acc=2) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, off=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, A=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, out=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16(lib, A=FAKE + 8) == kgw.KGW_ERROR_MISALIGNED
+    assert call_bf16(lib, out=FAKE + 4) == kgw.KGW_ERROR_MISALIGNED
+    assert call_bf16(lib, N=500) == kgw.KGW_ERROR_MISALIGNED
+    assert call_bf16(lib, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
+    assert call_bf16(lib, E=5000) == kgw.KGW_ERROR_UNSUPPORTED
+
+
+def test_fp8_argument_errors(lib):
+    assert call_fp8(lib, sa=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8(lib, sb=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8(lib, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
+    assert call_fp8(lib, N=520) == kgw.KGW_ERROR_MISALIGNED    # multiple of 8 but not 16
+    assert call_fp8(lib, B=FAKE + 1) == kgw.KGW_ERROR_MISALIGNED
+
+
+def test_empty_shapes_return_before_device(lib):
+    # no output elements: nothing to do, no device needed
+    assert call_bf16(lib, H=0, A=None, out=None) == kgw.KGW_SUCCESS
+    assert call_bf16(lib, N=0, B=None, out=None) == kgw.KGW_SUCCESS
+    # accumulate with no tokens adds nothing
+    assert call_bf16(lib, T=0, A=None, B=None, acc=1) == kgw.KGW_SUCCESS
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    A = torch.zeros(4, 256, dtype=torch.bfloat16)
+    B = torch.zeros(256, 8, dtype=torch.bfloat16)
+    off = torch.tensor([256], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        kgw.wgrad(A, B, off, sfa=torch.zeros(2, 4, dtype=torch.uint8))       # bf16 rejects scales
+    with pytest.raises(ValueError):
+        kgw.kgw_wgrad_bf16(A.float(), B, off)                                  # wrong dtype
+    with pytest.raises(ValueError):
+        kgw.kgw_wgrad_bf16(A, B[:128], off)                                    # shape mismatch
+    with pytest.raises(ValueError):
+        kgw.kgw_wgrad_fp8(A.view(torch.uint8)[:, :256], None, B.view(torch.uint8), None, off)  # no scales
+    with pytest.raises(ValueError):
+        kgw.kgw_wgrad_bf16(A, B, off, accumulate=True)                         # accumulate needs out

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Inputs are seeded and synthetic (workloads/); the oracle runs on host copies
+of exactly the tensors the GPU consumed.  Small and mid sizes are compared
+element by element; the full-size workloads compare sampled rows, which the
+oracle computes one by one, plus whole-tensor properties (zero-filled and
+untouched experts) checked on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import grouped_gemm_expert_offsets_amd as kgw
+import oracle
+import workloads
+from helpers import assert_bf16_close, assert_fp32_close, rel_frob, sample_rows, to_f64, FP32_REL_FROB
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+DEV = "cuda"
+
+
+def run_bf16(wl, out=None, out_dtype=None, accumulate=None):
+    acc = wl.accumulate if accumulate is None else accumulate
+    od = out_dtype or wl.out_dtype
+    if out is None and acc:
+        out = wl.C0.clone()
+    res = kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, out_dtype=od, accumulate=acc)
+    torch.cuda.synchronize()
+    return res
+
+
+# Accuracy bound of the native scaled fp8 MFMA entry point: the hardware keeps about 13 bits
+# below the largest product of each K group, measured 1.5e-5 relative Frobenius on
+# block-quantised Gaussian operands; the bound leaves a factor of ~6.
+NATIVE_FP8_REL_FROB = 1e-4
+
+
+def run_fp8(wl, out=None, out_dtype=None, accumulate=None, native=False):
+    acc = wl.accumulate if accumulate is None else accumulate
+    od = out_dtype or wl.out_dtype
+    if out is None and acc:
+        out = wl.C0.clone()
+    fn = kgw.kgw_wgrad_fp8_native if native else kgw.kgw_wgrad_fp8
+    res = fn(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, out_dtype=od, accumulate=acc)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_dense(wl):
+    off = wl.offsets.cpu()
+    if wl.kind == "bf16":
+        return oracle.wgrad_bf16(wl.A.cpu(), wl.B.cpu(), off)
+    return oracle.wgrad_fp8(wl.A.cpu(), wl.sfa.cpu(), wl.B.cpu(), wl.sfb.cpu(), off)
+
+
+def nan_filled(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+# ----------------------------------------------------------------------------
+# small and mid sizes: every element
+# ----------------------------------------------------------------------------
+def test_tiny_config_every_element():
+    wl = workloads.make_workload("tiny", seed=1, device=DEV)
+    out = nan_filled((4, 256, 512), torch.float32)
+    run_bf16(wl, out=out)
+    ref = oracle_dense(wl)
+    assert_fp32_close(to_f64(out), ref, "tiny")
+    assert not torch.signbit(out[1]).any()  # empty expert written with +0.0
+
+
+EXACT_CASES = [
+    # (counts, hidden, n)
+    ([256, 0, 512, 256], 256, 512),
+    ([256, 0, 768, 512, 0, 256], 320, 392),      # ragged M and N tails, empties in the middle
+    ([512, 256], 40, 24),                          # one partial tile
+    ([0, 0, 256], 512, 520),
+    ([1280], 264, 776),                            # single expert = plain GEMM, 20 K steps
+]
+
+
+@pytest.mark.parametrize("counts,hidden,n", EXACT_CASES)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_bf16_integer_inputs_bit_exact(counts, hidden, n, out_dtype, accumulate):
+    wl = workloads.make_operands(counts, hidden, n, "bf16", out_dtype, accumulate, seed=11, device=DEV,
+                                 integer_range=4)
+    out = wl.C0.clone() if accumulate else nan_filled((len(counts), hidden, n), out_dtype)
+    run_bf16(wl, out=out, accumulate=accumulate)
+    W = oracle_dense(wl)
+    ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
+    if out_dtype == torch.bfloat16:
+        ref = oracle.round_to_bf16(ref)
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_bf16_random_mid_size(out_dtype, accumulate):
+    counts = [256, 0, 1280, 512, 768, 0, 256]
+    wl = workloads.make_operands(counts, 576, 792, "bf16", out_dtype, accumulate, seed=21, device=DEV)
+    out = wl.C0.clone() if accumulate else nan_filled((7, 576, 792), out_dtype)
+    run_bf16(wl, out=out, accumulate=accumulate)
+    W = oracle_dense(wl)
+    C0 = to_f64(wl.C0) if accumulate else None
+    ref = oracle.apply_output_mode(W, accumulate, C0)
+    got = to_f64(out)
+    if accumulate:
+        for e in (1, 5):  # empty experts: untouched, bit for bit
+            assert torch.equal(out[e].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                               wl.C0[e].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+    if out_dtype == torch.float32:
+        assert_fp32_close(got, ref, "mid fp32")
+    else:
+        rms = np.sqrt(np.mean(W * W, axis=(1, 2)))
+        assert_bf16_close(got, ref, "mid bf16", rms=np.where(rms > 0, rms, np.sqrt(np.mean(ref * ref, axis=(1, 2)))))
+
+
+def test_no_tokens_at_all():
+    wl = workloads.make_operands([0, 0, 0], 64, 64, "bf16", torch.float32, True, seed=3, device=DEV)
+    out = nan_filled((3, 64, 64), torch.float32)
+    kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out)) and not torch.signbit(out).any()
+    c0 = wl.C0.clone()
+    kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, c0, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int32), wl.C0.view(torch.int32))
+
+
+def test_deterministic_and_stream_ordered():
+    wl = workloads.make_operands([512, 256, 0, 1024], 512, 512, "bf16", torch.float32, False, seed=5, device=DEV)
+    a = run_bf16(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out_dtype=torch.float32)
+    s.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_validate_offsets_on_device():
+    good = torch.tensor([256, 256, 768], dtype=torch.int32, device=DEV)
+    kgw.kgw_validate_offsets(good, 768, 256)
+    with pytest.raises(ValueError, match="first bad expert 1"):
+        kgw.kgw_validate_offsets(torch.tensor([256, 128, 768], dtype=torch.int32, device=DEV), 768, 256)
+    with pytest.raises(ValueError):
+        kgw.kgw_validate_offsets(good, 1024, 256)
+
+
+def test_malformed_offsets_stay_in_bounds():
+    # decreasing / beyond tokens_sum offsets: wrong values allowed, but the call completes and
+    # the experts whose ranges are well formed are still exact.
+    wl = workloads.make_operands([256, 256, 256], 64, 64, "bf16", torch.float32, False, seed=4, device=DEV,
+                                 integer_range=3)
+    bad = torch.tensor([256, 4096, 100], dtype=torch.int32, device=DEV)
+    out = kgw.kgw_wgrad_bf16(wl.A, wl.B, bad, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    W = oracle.wgrad_bf16(wl.A.cpu(), wl.B.cpu(), np.array([256, 512, 768], dtype=np.int32))
+    assert np.array_equal(to_f64(out[0]), W[0])
+
+
+# ----------------------------------------------------------------------------
+# fp8 block-scaled path
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fp8_random_small(out_dtype):
+    counts = [128, 0, 384, 256, 640]
+    wl = workloads.make_operands(counts, 264, 400, "fp8", out_dtype, False, seed=31, device=DEV)
+    out = nan_filled((5, 264, 400), out_dtype)
+    run_fp8(wl, out=out)
+    ref = oracle_dense(wl)
+    if out_dtype == torch.float32:
+        assert_fp32_close(to_f64(out), ref, "fp8 fp32")
+    else:
+        assert_bf16_close(to_f64(out), ref, "fp8 bf16")
+
+
+@pytest.mark.parametrize("native", [False, True])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_fp8_integer_inputs_with_scales_bit_exact(accumulate, native):
+    counts = [256, 128, 0, 512]
+    hidden, n = 200, 272
+    wl = workloads.make_operands(counts, hidden, n, "fp8", torch.float32, accumulate, seed=41, device=DEV,
+                                 integer_range=8)
+    g = torch.Generator(device=DEV).manual_seed(42)
+    # scales 2^j, |j| <= 2: every product and partial sum stays exact in fp32
+    wl.sfa = torch.randint(125, 130, wl.sfa.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    wl.sfb = torch.randint(125, 130, wl.sfb.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    out = wl.C0.clone() if accumulate else nan_filled((4, hidden, n), torch.float32)
+    run_fp8(wl, out=out, accumulate=accumulate, native=native)
+    W = oracle_dense(wl)
+    ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
+
+
+def test_fp8_native_random_small_within_its_bound():
+    counts = [128, 0, 384, 256, 640]
+    wl = workloads.make_operands(counts, 264, 400, "fp8", torch.float32, False, seed=31, device=DEV)
+    out = nan_filled((5, 264, 400), torch.float32)
+    run_fp8(wl, out=out, native=True)
+    ref = oracle_dense(wl)
+    got = to_f64(out)
+    assert np.all(got[1] == 0.0)
+    for e in (0, 2, 3, 4):
+        err = rel_frob(got[e], ref[e])
+        assert err <= NATIVE_FP8_REL_FROB, f"expert {e}: {err:.3e}"
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration: sampled rows
+# ----------------------------------------------------------------------------
+def check_sampled(wl, out, experts, rows_per_expert=6, seed=0):
+    Ah, Bh, off = wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu()
+    if wl.kind == "fp8":
+        sah, sbh = wl.sfa.cpu(), wl.sfb.cpu()
+    for e in experts:
+        rows = sample_rows(wl.hidden, rows_per_expert, seed + int(e))
+        if wl.kind == "bf16":
+            W = oracle.wgrad_rows_bf16(Ah, Bh, off, int(e), rows)
+        else:
+            W = oracle.wgrad_rows_fp8(Ah, sah, Bh, sbh, off, int(e), rows)
+        C0 = to_f64(wl.C0[e][rows]) if wl.accumulate else None
+        ref = oracle.apply_output_mode(W, wl.accumulate, C0)
+        got = to_f64(out[e][torch.from_numpy(rows).to(out.device)])
+        if wl.out_dtype == torch.float32:
+            err = rel_frob(got, ref)
+            assert err <= FP32_REL_FROB, f"{wl.name} expert {e}: rel Frobenius {err:.3e}"
+        else:
+            rms = np.sqrt(np.mean(W * W)) if np.any(W) else np.sqrt(np.mean(ref * ref))
+            assert_bf16_close(got[None], ref[None], f"{wl.name} expert {e}", rms=np.array([rms]))
+
+
+def empty_experts(wl):
+    return [e for e, c in enumerate(wl.counts) if c == 0]
+
+
+def nonempty_experts(wl):
+    return [e for e, c in enumerate(wl.counts) if c > 0]
+
+
+def test_full_balanced_bf16():
+    wl = workloads.make_workload("balanced", seed=1, device=DEV)
+    out = run_bf16(wl)
+    check_sampled(wl, out, nonempty_experts(wl))
+
+
+def test_full_skewed_accumulate():
+    wl = workloads.make_workload("skewed", seed=1, device=DEV)
+    out = run_bf16(wl)
+    for e in empty_experts(wl):
+        assert torch.equal(out[e].view(torch.int32), wl.C0[e].view(torch.int32)), f"expert {e} touched"
+    check_sampled(wl, out, nonempty_experts(wl), rows_per_expert=4)
+
+
+def test_full_fp8():
+    wl = workloads.make_workload("fp8", seed=1, device=DEV)
+    out = run_fp8(wl)
+    check_sampled(wl, out, nonempty_experts(wl)[::2], rows_per_expert=4)
+
+
+def test_full_fp8_native_within_its_bound():
+    wl = workloads.make_workload("fp8", seed=1, device=DEV)
+    out = run_fp8(wl, out_dtype=torch.float32, native=True)
+    Ah, Bh, sah, sbh, off = wl.A.cpu(), wl.B.cpu(), wl.sfa.cpu(), wl.sfb.cpu(), wl.offsets.cpu()
+    for e in nonempty_experts(wl)[::4]:
+        rows = sample_rows(wl.hidden, 4, e)
+        ref = oracle.wgrad_rows_fp8(Ah, sah, Bh, sbh, off, e, rows)
+        got = to_f64(out[e][torch.from_numpy(rows).to(out.device)])
+        err = rel_frob(got, ref)
+        assert err <= NATIVE_FP8_REL_FROB, f"expert {e}: {err:.3e}"
+
+
+def test_full_many_small():
+    wl = workloads.make_workload("many_small", seed=1, device=DEV)
+    out = run_bf16(wl)
+    emp = empty_experts(wl)
+    idx = torch.tensor(emp, device=DEV)
+    z = out.index_select(0, idx)
+    assert torch.count_nonzero(z).item() == 0 and not torch.signbit(z).any().item()
+    del z
+    ne = nonempty_experts(wl)
+    rng = np.random.default_rng(0)
+    pick = sorted(set([ne[0], ne[-1]] + rng.choice(ne, 16, replace=False).tolist()))
+    check_sampled(wl, out, pick, rows_per_expert=4)
