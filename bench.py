@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the K-grouped MoE weight-gradient GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one kgw_wgrad_* call over one batch of seeded synthetic input
+already resident in HBM: offsets decode, tile scheduling, zero-fill, operand
+staging, the MFMA K loop and the epilogue all run inside that one launch.
+The headline workload is the balanced bf16 fc2 weight gradient (E=8,
+hidden 4096, N 2048, n_e = roundup256(4096*U(0.7,1.3)), seed 1, bf16 output,
+overwrite).  Useful work = 2 * hidden * N * tokens_sum FLOP.
+
+Prints ONE JSON line.  `roofline.achieved` divides the useful FLOP of one
+launch by the launch's average duration, timed with HIP events recorded on
+the launch stream around every timed launch.  `roofline.traffic` comes from
+the rocprofv3 counter summary committed under profiles/ for this workload,
+and is null when the kernel sources changed after those counters were taken.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`secondary` reports the other workloads (the 32-expert skewed-accumulate,
+fp8 and many-small-expert configs, and the tiny one) with the same timing.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of MFMA peak, K-grouped MoE wgrad (bf16 and fp8), 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+HEADLINE = "balanced"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "grouped_gemm_expert_offsets_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_traffic(workload: str):
+    """HBM bytes per launch from profiles/<...>.md, if taken on the current kernel sources."""
+    cur = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        if f"workload: {workload}" not in text:
+            continue
+        m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+        m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+        if m_hash and m_bytes and m_hash.group(1) == cur:
+            return float(m_bytes.group(1)), os.path.relpath(path, ROOT)
+    return None, None
+
+
+def algorithmic_bytes(wl) -> float:
+    """Read A and B once, write the output once (read it too when accumulating), plus scales."""
+    import torch
+    H, N, T, E = wl.hidden, wl.n, wl.tokens_sum, wl.num_experts
+    el_in = 1 if wl.kind == "fp8" else 2
+    el_out = 4 if wl.out_dtype == torch.float32 else 2
+    b = (H * T + T * N) * el_in + E * H * N * el_out * (2 if wl.accumulate else 1)
+    if wl.kind == "fp8":
+        b += (T // 128) * (H + N)
+    return float(b)
+
+
+def make_call(wl, out, native=False):
+    import grouped_gemm_expert_offsets_amd as kgw
+    if wl.kind == "bf16":
+        return lambda: kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=wl.accumulate)
+    fn = kgw.kgw_wgrad_fp8_native if native else kgw.kgw_wgrad_fp8
+    return lambda: fn(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, accumulate=wl.accumulate)
+
+
+def time_call(call, steps: int, warmup: int):
+    """Wall time of `steps` back-to-back calls plus HIP-event time of each launch."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        call()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms / steps, launch_ms
+
+
+def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1):
+    import torch
+    import workloads
+    wl = workloads.make_workload(name, seed=seed, device="cuda")
+    out = wl.C0 if wl.accumulate else torch.empty((wl.num_experts, wl.hidden, wl.n), dtype=wl.out_dtype,
+                                                  device="cuda")
+    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup)
+    launch_ms.sort()
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    res = {
+        "workload": name + ("_native" if native else ""),
+        "ms_per_step": ms_step,
+        "launch_ms_mean": mean_launch,
+        "launch_ms_median": launch_ms[len(launch_ms) // 2],
+        "launch_ms_min": launch_ms[0],
+        "launch_ms_max": launch_ms[-1],
+        "tflops": wl.flops / (mean_launch * 1e-3) / 1e12,
+        "flops_per_launch": wl.flops,
+        "algorithmic_bytes": algorithmic_bytes(wl),
+    }
+    peak = PEAK_FP8_TFLOPS if wl.kind == "fp8" else PEAK_BF16_TFLOPS
+    res["frac_of_mfma_peak"] = res["tflops"] / peak
+    res["hbm_gbps_algorithmic"] = res["algorithmic_bytes"] / (mean_launch * 1e-3) / 1e9
+    res["frac_of_hbm_peak"] = res["hbm_gbps_algorithmic"] / PEAK_HBM_GBPS
+    del wl, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(target_seconds: float):
+    """Time the CPU oracle on the first rows of expert 0 of the headline workload."""
+    import numpy as np
+    import oracle
+    import workloads
+    wl = workloads.make_workload(HEADLINE, seed=1, device="cuda")
+    A, B, off = wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu()
+    n_e = wl.counts[0]
+    t0 = time.perf_counter()
+    oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(4))
+    rate_est = 2.0 * 4 * wl.n * n_e / max(time.perf_counter() - t0, 1e-6)
+    rows = int(min(wl.hidden, max(8, target_seconds * rate_est / (2.0 * wl.n * n_e))))
+    t0 = time.perf_counter()
+    oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(rows))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * wl.n * n_e
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of expert 0 (n_e={n_e}) of the {HEADLINE} workload, all N={wl.n} "
+                  f"columns: {flops:.3e} FLOP in {dt:.1f} s (fp64 C oracle, OpenMP over rows)",
+        "seconds": dt,
+    }
+
+
+def copy_calibration(gib: float = 1.0):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 2, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--native-fp8", action="store_true", help="time kgw_wgrad_fp8_native for fp8 workloads")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the K-grouped wgrad kernel runs on one device and this build has "
+              "no multi-GPU path (expert parallelism would run the same kernel per GPU on its local experts).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import grouped_gemm_expert_offsets_amd as kgw
+    kgw.load_library()
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    head = run_workload(args.workload, args.steps, args.warmup, native=args.native_fp8)
+    import workloads
+    spec = workloads.config_spec(args.workload.replace("_native", ""), 1)
+    traffic, traffic_src = profile_traffic(head["workload"])
+    kind = spec["kind"]
+    peak = PEAK_FP8_TFLOPS if kind == "fp8" else PEAK_BF16_TFLOPS
+    line = {
+        "metric": METRIC,
+        "value": head["flops_per_launch"] / (head["ms_per_step"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if kind == "fp8" else "bf16",
+        "data": "synthetic (seeded; shapes and count distributions of the pages' MoE workloads)",
+        "config": {
+            "workload": workloads.DESCRIPTIONS[args.workload.replace("_native", "")],
+            "num_experts": len(spec["counts"]),
+            "hidden": spec["hidden"],
+            "n": spec["n"],
+            "tokens_sum": int(sum(spec["counts"])),
+            "counts": spec["counts"] if len(spec["counts"]) <= 32 else "see workloads.config_spec",
+            "seed": 1,
+            "out_dtype": str(spec["out_dtype"]).replace("torch.", ""),
+            "accumulate": spec["accumulate"],
+            "parallelism": "single GPU",
+        },
+        "frac_of_mfma_peak": head["flops_per_launch"] / (head["ms_per_step"] * 1e-3) / 1e12 / peak,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": head["tflops"],
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": head["tflops"] / peak,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "algorithmic_bytes": head["algorithmic_bytes"],
+            "kernel": "wgrad_bf16_kernel" if kind == "bf16" else "wgrad_fp8_kernel",
+            "launch_ms_mean": head["launch_ms_mean"],
+            "launch_ms_min": head["launch_ms_min"],
+            "launch_ms_max": head["launch_ms_max"],
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_secondary:
+        sec = []
+        for name, native in (("tiny", False), ("skewed", False), ("fp8", False), ("fp8", True),
+                             ("many_small", False)):
+            if name == args.workload:
+                continue
+            r = run_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), native=native)
+            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,14 +13,23 @@
 // zero-fills its tile in overwrite mode and does nothing in accumulate mode
 // (section "Operation": an empty expert produces zero when overwriting).
 //
-// Inside an item (MFMA tile 32x32x16, fp32 accumulation as the page's BF16
-// contract requires):
+// Inside an item (MFMA 32x32x16, fp32 accumulation as the page's BF16 contract
+// requires):
 //   - 4 waves, each owning a 128 (M) x 128 (N) quarter of the tile; the MFMA
 //     computes the transposed block Wgrad^T so that every lane ends up holding
 //     four consecutive N values of one output row (16-byte stores);
-//   - K step of 64 tokens; A and B tiles are staged through registers into a
-//     double-buffered LDS ring with XOR swizzles (A rows: 16-byte chunk ^
-//     ((row>>1)&7); B rows: chunk ^ 4*(k&3)), which keeps both the stores and
+//   - K step of 32 tokens.  Operands reach LDS through direct global->LDS
+//     loads (no register staging): A in three 64-token stages (each A row
+//     then moves as one full 128-byte line; half-line rows cost the L2 twice
+//     per byte) and B in three 32-token stages, so loads run up to four
+//     (A) and two (B) steps ahead.
+//     The fragments of step s+1 are read from LDS while the second half of
+//     step s's MFMAs runs, so the MFMAs never wait on LDS latency; one
+//     barrier per step, placed between the two halves, both publishes the
+//     next stage and frees the stage just consumed;
+//   - the XOR swizzles live on the global-address side: each lane of a direct
+//     load fetches the chunk that belongs at its LDS slot.  A rows (128 B):
+//     16-byte chunk ^ ((row>>1)&7); B rows (512 B): chunk ^ 4*(k&3).  Both keep
 //     the fragment reads free of bank conflicts;
 //   - A is token-contiguous, so its fragments are plain 16-byte LDS reads; B is
 //     N-contiguous, so its fragments come from transposing ds_read_b64_tr_b16.
@@ -33,23 +42,30 @@ namespace {
 
 constexpr int BM = kBf16BM, BN = kBf16BN, BK = kBf16BK;
 constexpr int NT = 256;
-constexpr int A_STAGE = BM * BK * 2;        // 32 KiB: 256 rows x 128 B
-constexpr int B_STAGE = BK * BN * 2;        // 32 KiB: 64 rows x 512 B
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int LDS_TILES = 2 * STAGE;        // double buffer
+// A is staged 64 tokens (two K steps) at a time, so every A row moves as one
+// full 128-byte line; B is staged one 32-token step at a time.
+constexpr int NA = 3;                       // A ring: 3 stages of 2 K steps
+constexpr int NB = 3;                       // B ring: 3 stages of 1 K step
+constexpr int A_STAGE = BM * 2 * BK * 2;    // 32 KiB: 256 rows x 128 B
+constexpr int B_STAGE = BK * BN * 2;        // 16 KiB: 32 rows x 512 B
+constexpr int B_RING = NA * A_STAGE;        // byte offset of the B ring
+constexpr int LDS_TILES = NA * A_STAGE + NB * B_STAGE;  // 144 KiB
 constexpr int GROUP_M = 4;
+constexpr int A_LOADS = 8;                  // direct loads per wave per A stage
+constexpr int B_LOADS = 4;                  // direct loads per wave per B stage
 
-static_assert(BM == 256 && BN == 256 && BK == 64, "index math below assumes 256x256x64");
+static_assert(BM == 256 && BN == 256 && BK == 32, "index math below assumes 256x256x32");
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[LDS_TILES + kMaxExperts * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TILES + kMaxExperts * 4];
     lds_char* tiles = (lds_char*)smem;
     int32_t* s_end = (int32_t*)(smem + LDS_TILES);
+    const uint32_t tiles_addr = lds_addr(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1;
     const int wn = wave >> 1;
     const int64_t T = p.tokens_sum, H = p.hidden, N = p.n;
@@ -62,16 +78,21 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     }
     __syncthreads();
 
-    // LDS store offsets of this thread's 8 A chunks and 8 B chunks (fixed per thread).
-    // A chunk c = tid + 256*pp: row (tid>>3) + 32*pp, chunk tid&7.
-    const uint32_t a_lds0 = (uint32_t)(tid >> 3) * 128u + (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-    // B chunk c = tid + 256*pp: k-row (tid>>5) + 8*pp, chunk tid&31.
-    const uint32_t b_lds0 = (uint32_t)(tid >> 5) * 512u + (uint32_t)(((tid & 31) ^ (((tid >> 5) & 3) << 2)) << 4);
+    // Direct-load slots of this lane.  A: wave instruction t (0..7) fills LDS
+    // rows 64*wave + 8*t + (lane>>3), 16-byte slot lane&7, which holds logical
+    // chunk (lane&7) ^ ((row>>1)&7).  B: instruction t (0..3) fills k-rows
+    // 8*wave + 2*t + (lane>>5), slot lane&31 = logical chunk slot ^ 4*(k&3).
+    int a_q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) a_q[t] = (lane & 7) ^ ((4 * t + (lane >> 4)) & 7);
+    int b_q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b_q[t] = (lane & 31) ^ (((2 * t + (lane >> 5)) & 3) << 2);
 
     // Fragment read offsets (fixed per lane).
     const int l32 = lane & 31, lhi = lane >> 5;
     const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u;
-    const int a_sw = (lane >> 1) & 7;
+    const int a_sw = (l32 >> 1) & 7;
     const int g16 = lane >> 4, i16 = lane & 15;
     uint32_t b_frag[4];
 #pragma unroll
@@ -92,29 +113,50 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
-        int32_t begin = e ? s_end[e - 1] : 0;
-        const int32_t end = max(begin, s_end[e]);
-        begin &= ~(BK - 1);
-        const int ksteps = (end - begin) / BK;
+        // Token range (uniform across the workgroup; read from LDS, hence readfirstlane).
+        int32_t begin = __builtin_amdgcn_readfirstlane(e ? s_end[e - 1] : 0);
+        const int32_t end = max(begin, __builtin_amdgcn_readfirstlane(s_end[e]));
+        // The loop below takes K steps in pairs: a range is used in whole
+        // 64-token units (every well-formed count is a multiple of 256).
+        begin &= ~(2 * BK - 1);
+        const int ksteps = ((end - begin) / (2 * BK)) * 2;
         if (ksteps == 0) {
             if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, e, m0, n0, tid);
             continue;
         }
 
-        // Global offsets of this thread's chunks, relative to the tile origin at token `begin`.
-        const uint16_t* Abase = (const uint16_t*)p.A + m0 * T + begin;
-        const uint16_t* Bbase = (const uint16_t*)p.B + (int64_t)begin * N + n0;
+        const char* Abase = (const char*)p.A + (m0 * T + begin) * 2;
+        const char* Bbase = (const char*)p.B + ((int64_t)begin * N + n0) * 2;
         const int rows_valid = (int)min<int64_t>(BM, H - m0);
         const int cols_valid = (int)min<int64_t>(BN, N - n0);
-        uint32_t a_voff[8], b_voff[8];
+        uint32_t a_voff[8], b_voff[4];
 #pragma unroll
-        for (int pp = 0; pp < 8; ++pp) {
-            const int row = min((tid >> 3) + 32 * pp, rows_valid - 1);
-            a_voff[pp] = (uint32_t)row * (uint32_t)(T * 2) + (uint32_t)(tid & 7) * 16u;
+        for (int t = 0; t < 8; ++t) {
+            const int row = min(64 * wave + 8 * t + (lane >> 3), rows_valid - 1);
+            a_voff[t] = (uint32_t)row * (uint32_t)(T * 2) + (uint32_t)a_q[t] * 16u;
         }
-        const uint32_t bcol = (uint32_t)min((tid & 31) * 8, cols_valid - 8) * 2u;
 #pragma unroll
-        for (int pp = 0; pp < 8; ++pp) b_voff[pp] = (uint32_t)((tid >> 5) + 8 * pp) * (uint32_t)(N * 2) + bcol;
+        for (int t = 0; t < 4; ++t) {
+            const int krow = 8 * wave + 2 * t + (lane >> 5);
+            b_voff[t] = (uint32_t)krow * (uint32_t)(N * 2) + (uint32_t)min(8 * b_q[t], cols_valid - 8) * 2u;
+        }
+
+        // Direct loads.  A stage a (steps 2a, 2a+1) goes to A slot a % NA, B step s
+        // to B slot s % NB.  Stages past the expert's range use an empty buffer
+        // range: the loads fetch nothing (the slot is never read by an MFMA),
+        // which keeps the loop below free of branches and its vmcnt counts uniform.
+        auto issue_a = [&](int a) {
+            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave) * 1024u;
+            const i32x4 r = rsrc_words(Abase + (int64_t)a * (4 * BK), 2 * a < ksteps ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+            for (int t = 0; t < A_LOADS; ++t) dma_16B(r, a_voff[t], dst + t * 1024u);
+        };
+        auto issue_b = [&](int s) {
+            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (s % NB) * B_STAGE) + (uint32_t)(4 * wave) * 1024u;
+            const i32x4 r = rsrc_words(Bbase + (int64_t)s * BK * N * 2, s < ksteps ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+            for (int t = 0; t < B_LOADS; ++t) dma_16B(r, b_voff[t], dst + t * 1024u);
+        };
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -124,56 +166,116 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-        i32x4 ra[8], rb[8];
-        auto gload = [&](int s) {
-            const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (int64_t)s * BK, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (int64_t)s * BK * N, 0xFFFFFFFFu);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) ra[pp] = buffer_load_16B(rA, a_voff[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) rb[pp] = buffer_load_16B(rB, b_voff[pp]);
+        // Fragments of one K step: A[ks][i] (M blocks); B[ks][j] (N blocks) as the
+        // two transposed 4-token halves that form one MFMA operand.
+        struct Frags {
+            i32x4 a[2][4];
+            i16x4 blo[2][4];
+            i16x4 bhi[2][4];
         };
-        auto lstore = [&](int buf) {
-            lds_char* As = tiles + buf * STAGE;
-            lds_char* Bs = As + A_STAGE;
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(As, a_lds0 + pp * 4096u, ra[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(Bs, b_lds0 + pp * 4096u, rb[pp]);
+        // Fragment read number r (0..23) of step s: per k sub-step ks, the four
+        // A blocks then the eight transposed B halves.
+        auto read_one = [&](int s, int r, Frags& f) {
+            const int ks = r / 12, q = r % 12;
+            if (q < 4) {
+                const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
+                const uint32_t a_chunk = (uint32_t)(((4 * (s & 1) + 2 * ks + lhi) ^ a_sw) << 4);
+                f.a[ks][q] = lds_load_16B(As, a_frag_row + q * 4096u + a_chunk);
+            } else {
+                const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
+                const int j = (q - 4) >> 1, hi = (q - 4) & 1;
+                const i16x4 v = lds_read_tr16(Bs, b_frag[j] + ks * 8192u + hi * 2048u);
+                if (hi) f.bhi[ks][j] = v;
+                else f.blo[ks][j] = v;
+            }
         };
-        auto compute = [&](int buf) {
-            const lds_char* As = tiles + buf * STAGE;
-            const lds_char* Bs = As + A_STAGE;
+        auto read_all = [&](int s, Frags& f) {
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const uint32_t a_chunk = (uint32_t)(((2 * ks + lhi) ^ a_sw) << 4);
-                i32x4 af[4], bf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) af[i] = lds_load_16B(As, a_frag_row + i * 4096u + a_chunk);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const i16x4 lo = lds_read_tr16(Bs, b_frag[j] + ks * 8192u);
-                    const i16x4 hi = lds_read_tr16(Bs, b_frag[j] + ks * 8192u + 2048u);
-                    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    bf[j] = __builtin_bit_cast(i32x4, v);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] = mfma_bf16_32x32x16(bf[j], af[i], acc[j][i]);
+            for (int r = 0; r < 24; ++r) read_one(s, r, f);
+        };
+        // MFMA number k (0..15) of sub-step ks: N block k/4 times M block k%4.
+        auto mfma_one = [&](const Frags& f, int ks, int k) {
+            const int j = k >> 2, i = k & 3;
+            const i16x4 lo = f.blo[ks][j], hi = f.bhi[ks][j];
+            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[j][i] = mfma_bf16_32x32x16(__builtin_bit_cast(i32x4, v), f.a[ks][i], acc[j][i]);
+        };
+        auto dma_one = [&](int s, bool odd, int d) {
+            // d < B_LOADS: B step s+NB; then (odd steps) A stage (s+1)/2 + NA-1.
+            if (d < B_LOADS) {
+                const int sb = s + NB;
+                const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) +
+                                     (uint32_t)(4 * wave + d) * 1024u;
+                const i32x4 r = rsrc_words(Bbase + (int64_t)sb * BK * N * 2, sb < ksteps ? 0xFFFFFFFFu : 0u);
+                dma_16B(r, b_voff[d], dst);
+            } else if (odd) {
+                const int a = (s + 1) / 2 + NA - 1, t = d - B_LOADS;
+                const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
+                const i32x4 r = rsrc_words(Abase + (int64_t)a * (4 * BK), 2 * a < ksteps ? 0xFFFFFFFFu : 0u);
+                dma_16B(r, a_voff[t], dst);
             }
         };
 
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int s = 0; s < ksteps; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < ksteps) gload(s + 1);
-            compute(cur);
-            if (s + 1 < ksteps) lstore(cur ^ 1);
-            __syncthreads();
+        // The partial vmcnt waits count only this item's direct loads, so the
+        // previous item's output stores must have drained first.
+        wait_vmcnt<0>();
+        // Prologue in steady-state issue order: A0 B0 A1 B1 B2 A2.  Step 0
+        // needs A0 and B0; 24 loads were issued after B0.
+        issue_a(0);
+        issue_b(0);
+        issue_a(1);
+        issue_b(1);
+        issue_b(2);
+        issue_a(2);
+        wait_vmcnt<2 * A_LOADS + 2 * B_LOADS>();
+        barrier_no_fence();
+        Frags f0, f1;
+        read_all(0, f0);
+
+        // Step s with its fragments in `cur`:
+        //   once this wave's reads of step s and its loads of step s+1 are done,
+        //   a barrier publishes step s+1 and certifies that every wave is done
+        //   reading step s, whose slots then take B step s+3 and, after an odd
+        //   step (the second of its A stage), A stage (s+1)/2 + 2;
+        //   sub-step 0's 16 MFMAs, each followed by one of those direct loads;
+        //   sub-step 1's 16 MFMAs, each followed by one or two of the 24
+        //   fragment reads of step s+1 (so the LDS latency hides behind MFMAs).
+        // With B issued before A, the loads of step s+1 are complete once at most
+        // 12 later loads remain outstanding, at every step (traced from the
+        // prologue order above).  sched_barrier(0) pins this interleaving; the
+        // compiler would otherwise cluster the memory operations.
+        auto body = [&](int s, bool odd, Frags& cur, Frags& nxt) {
+            wait_lgkmcnt0();
+            wait_vmcnt<A_LOADS + B_LOADS>();
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                mfma_one(cur, 0, k);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k < B_LOADS + A_LOADS) dma_one(s, odd, k);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                mfma_one(cur, 1, k);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k < 8) {
+                    read_one(s + 1, 2 * k, nxt);
+                    read_one(s + 1, 2 * k + 1, nxt);
+                } else {
+                    read_one(s + 1, 8 + k, nxt);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        for (int s = 0; s < ksteps; s += 2) {
+            body(s, false, f0, f1);
+            body(s + 1, true, f1, f0);
         }
+        // Every wave must be done reading the ring before the next item refills it.
+        wait_lgkmcnt0();
+        barrier_no_fence();
 
         store_wave_tile<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc);
     }

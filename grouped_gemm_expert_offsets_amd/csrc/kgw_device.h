@@ -32,6 +32,49 @@ __device__ __forceinline__ uint8_t buffer_load_u8(__amdgpu_buffer_rsrc_t r, uint
     return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
 }
 
+// Buffer resource of a raw byte buffer as four SGPR words (for inline asm).
+// Loads at byte offsets >= num_bytes return zero without touching memory.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t num_bytes = 0xFFFFFFFFu) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r = {(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)num_bytes, kBufferWord3};
+    r[0] = __builtin_amdgcn_readfirstlane(r[0]);
+    r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+    r[2] = __builtin_amdgcn_readfirstlane(r[2]);
+    return r;
+}
+
+// LDS byte address of a __shared__ location (wave-uniform callers only).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// Direct global -> LDS load (buffer_load_dwordx4 ... lds): every lane fetches 16
+// bytes at byte offset `voff` of the buffer and the wave's 64 results land
+// contiguously in LDS at byte address `lds_dst` + 16 * lane (`lds_dst` is
+// wave-uniform and travels in M0).  Issued as inline asm so the compiler does
+// not track it: otherwise it must assume the write may alias any LDS read and
+// waits for all such loads (vmcnt(0)) before every read, which would collapse
+// the multi-stage ring.  Callers order these loads with wait_vmcnt + barrier.
+__device__ __forceinline__ void dma_16B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left unconstrained); gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// Workgroup barrier without the memory fence __syncthreads() adds: the fence
+// would wait for every outstanding direct-to-LDS load, collapsing the pipeline.
+// Callers order their own memory with wait_vmcnt / lgkmcnt waits.
+__device__ __forceinline__ void barrier_no_fence() { __builtin_amdgcn_s_barrier(); }
+
 // LDS accessors on explicit address-space-3 pointers (ds_read / ds_write).
 __device__ __forceinline__ void lds_store_16B(lds_char* base, uint32_t off, i32x4 v) {
     *reinterpret_cast<__attribute__((address_space(3))) i32x4*>(base + off) = v;

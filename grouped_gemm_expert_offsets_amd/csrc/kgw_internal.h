@@ -28,7 +28,7 @@ struct GroupedParams {
 };
 
 // Tile shape of the bf16 and fp8 kernels (output tile BM x BN, K step BK).
-constexpr int kBf16BM = 256, kBf16BN = 256, kBf16BK = 64;
+constexpr int kBf16BM = 256, kBf16BN = 256, kBf16BK = 32;
 constexpr int kFp8BM = 256, kFp8BN = 256, kFp8BK = 128;
 
 hipError_t launch_wgrad_bf16(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
