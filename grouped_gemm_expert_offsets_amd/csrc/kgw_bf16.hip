@@ -22,7 +22,8 @@
 //     loads (no register staging): A in three 64-token stages (each A row
 //     then moves as one full 128-byte line; half-line rows cost the L2 twice
 //     per byte) and B in three 32-token stages, so loads run up to four
-//     (A) and two (B) steps ahead.
+//     (A) and three (B) steps ahead.  The rings take all 160 KiB of LDS; the
+//     per-expert token ranges come from scalar loads of the offsets.
 //     The fragments of step s+1 are read from LDS while the second half of
 //     step s's MFMAs runs, so the MFMAs never wait on LDS latency; one
 //     barrier per step, placed between the two halves, both publishes the
@@ -45,11 +46,11 @@ constexpr int NT = 256;
 // A is staged 64 tokens (two K steps) at a time, so every A row moves as one
 // full 128-byte line; B is staged one 32-token step at a time.
 constexpr int NA = 3;                       // A ring: 3 stages of 2 K steps
-constexpr int NB = 3;                       // B ring: 3 stages of 1 K step
+constexpr int NB = 4;                       // B ring: 4 stages of 1 K step
 constexpr int A_STAGE = BM * 2 * BK * 2;    // 32 KiB: 256 rows x 128 B
 constexpr int B_STAGE = BK * BN * 2;        // 16 KiB: 32 rows x 512 B
 constexpr int B_RING = NA * A_STAGE;        // byte offset of the B ring
-constexpr int LDS_TILES = NA * A_STAGE + NB * B_STAGE;  // 144 KiB
+constexpr int LDS_TILES = NA * A_STAGE + NB * B_STAGE;  // 160 KiB: all of the CU's LDS
 constexpr int GROUP_M = 4;
 constexpr int A_LOADS = 8;                  // direct loads per wave per A stage
 constexpr int B_LOADS = 4;                  // direct loads per wave per B stage
@@ -58,9 +59,8 @@ static_assert(BM == 256 && BN == 256 && BK == 32, "index math below assumes 256x
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[LDS_TILES + kMaxExperts * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TILES];
     lds_char* tiles = (lds_char*)smem;
-    int32_t* s_end = (int32_t*)(smem + LDS_TILES);
     const uint32_t tiles_addr = lds_addr(smem);
 
     const int tid = threadIdx.x;
@@ -69,14 +69,6 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     const int wm = wave & 1;
     const int wn = wave >> 1;
     const int64_t T = p.tokens_sum, H = p.hidden, N = p.n;
-
-    // Clamped offsets: every token range used below lies inside [0, tokens_sum).
-    for (int e = tid; e < p.num_experts; e += NT) {
-        int64_t v = p.offsets[e];
-        v = v < 0 ? 0 : (v > T ? T : v);
-        s_end[e] = (int32_t)v;
-    }
-    __syncthreads();
 
     // Direct-load slots of this lane.  A: wave instruction t (0..7) fills LDS
     // rows 64*wave + 8*t + (lane>>3), 16-byte slot lane&7, which holds logical
@@ -113,9 +105,12 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
-        // Token range (uniform across the workgroup; read from LDS, hence readfirstlane).
-        int32_t begin = __builtin_amdgcn_readfirstlane(e ? s_end[e - 1] : 0);
-        const int32_t end = max(begin, __builtin_amdgcn_readfirstlane(s_end[e]));
+        // Token range, clamped into [0, tokens_sum] (uniform: scalar loads of the
+        // offsets, which stay hot in L2; the LDS is all taken by the rings).
+        const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
+        const int64_t raw_end = p.offsets[e];
+        int32_t begin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
+        const int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
         // The loop below takes K steps in pairs: a range is used in whole
         // 64-token units (every well-formed count is a multiple of 256).
         begin &= ~(2 * BK - 1);
@@ -219,15 +214,16 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         // The partial vmcnt waits count only this item's direct loads, so the
         // previous item's output stores must have drained first.
         wait_vmcnt<0>();
-        // Prologue in steady-state issue order: A0 B0 A1 B1 B2 A2.  Step 0
-        // needs A0 and B0; 24 loads were issued after B0.
+        // Prologue in steady-state issue order: A0 B0 B1 A1 B2 B3 A2.  Step 0
+        // needs A0 and B0; 28 loads were issued after B0.
         issue_a(0);
         issue_b(0);
-        issue_a(1);
         issue_b(1);
+        issue_a(1);
         issue_b(2);
+        issue_b(3);
         issue_a(2);
-        wait_vmcnt<2 * A_LOADS + 2 * B_LOADS>();
+        wait_vmcnt<2 * A_LOADS + 3 * B_LOADS>();
         barrier_no_fence();
         Frags f0, f1;
         read_all(0, f0);
@@ -235,18 +231,19 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         // Step s with its fragments in `cur`:
         //   once this wave's reads of step s and its loads of step s+1 are done,
         //   a barrier publishes step s+1 and certifies that every wave is done
-        //   reading step s, whose slots then take B step s+3 and, after an odd
+        //   reading step s, whose slots then take B step s+4 and, after an odd
         //   step (the second of its A stage), A stage (s+1)/2 + 2;
         //   sub-step 0's 16 MFMAs, each followed by one of those direct loads;
         //   sub-step 1's 16 MFMAs, each followed by one or two of the 24
         //   fragment reads of step s+1 (so the LDS latency hides behind MFMAs).
         // With B issued before A, the loads of step s+1 are complete once at most
-        // 12 later loads remain outstanding, at every step (traced from the
-        // prologue order above).  sched_barrier(0) pins this interleaving; the
+        // 24 (even s) or 16 (odd s) later loads remain outstanding (traced from
+        // the prologue order above).  sched_barrier(0) pins this interleaving; the
         // compiler would otherwise cluster the memory operations.
         auto body = [&](int s, bool odd, Frags& cur, Frags& nxt) {
             wait_lgkmcnt0();
-            wait_vmcnt<A_LOADS + B_LOADS>();
+            if (odd) wait_vmcnt<A_LOADS + 2 * B_LOADS>();
+            else wait_vmcnt<2 * A_LOADS + 2 * B_LOADS>();
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
