@@ -21,8 +21,8 @@
 //   - K step of 32 tokens.  Operands reach LDS through direct global->LDS
 //     loads (no register staging): A in three 64-token stages (each A row
 //     then moves as one full 128-byte line; half-line rows cost the L2 twice
-//     per byte) and B in three 32-token stages, so loads run up to four
-//     (A) and three (B) steps ahead.  The rings take all 160 KiB of LDS; the
+//     per byte) and B in four 32-token stages, so loads run up to four
+//     steps ahead.  The rings take all 160 KiB of LDS; the
 //     per-expert token ranges come from scalar loads of the offsets.
 //     The fragments of step s+1 are read from LDS while the second half of
 //     step s's MFMAs runs, so the MFMAs never wait on LDS latency; one
@@ -33,7 +33,10 @@
 //     16-byte chunk ^ ((row>>1)&7); B rows (512 B): chunk ^ 4*(k&3).  Both keep
 //     the fragment reads free of bank conflicts;
 //   - A is token-contiguous, so its fragments are plain 16-byte LDS reads; B is
-//     N-contiguous, so its fragments come from transposing ds_read_b64_tr_b16.
+//     N-contiguous, so its fragments come from transposing ds_read_b64_tr_b16;
+//   - the finished tile leaves through the (then idle) ring: each wave
+//     transposes its accumulators through 32 KiB of LDS so that the global
+//     stores write whole row segments.
 #include "kgw_device.h"
 #include "kgw_internal.h"
 #include "kgw_tile_io.h"
@@ -270,11 +273,15 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
             body(s, false, f0, f1);
             body(s + 1, true, f1, f0);
         }
-        // Every wave must be done reading the ring before the next item refills it.
+        // The ring becomes the output staging area: every wave must be done
+        // reading it and every direct load (the empty ones past the range
+        // included) must have landed.
+        wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
-
-        store_wave_tile<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc);
+        store_wave_tile_staged<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        // The next item's direct loads overwrite the staging areas.
+        barrier_no_fence();
     }
 }
 

@@ -72,8 +72,14 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 
 
 // Workgroup barrier without the memory fence __syncthreads() adds: the fence
 // would wait for every outstanding direct-to-LDS load, collapsing the pipeline.
-// Callers order their own memory with wait_vmcnt / lgkmcnt waits.
-__device__ __forceinline__ void barrier_no_fence() { __builtin_amdgcn_s_barrier(); }
+// Callers order their own memory with wait_vmcnt / lgkmcnt waits.  The empty
+// asm statements keep the compiler from moving memory accesses across the
+// barrier (the barrier intrinsic itself does not order memory).
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // LDS accessors on explicit address-space-3 pointers (ds_read / ds_write).
 __device__ __forceinline__ void lds_store_16B(lds_char* base, uint32_t off, i32x4 v) {

@@ -76,4 +76,66 @@ __device__ __forceinline__ void store_wave_tile(const GroupedParams& p, int e, i
     }
 }
 
+// Same output as store_wave_tile, staged through `stage`, a 32 KiB LDS region
+// private to the calling wave (16-byte aligned, free of other traffic).  The
+// MFMA layout gives each lane one row and four columns per register group, so
+// direct stores scatter 16 bytes over 32 rows per instruction; after a
+// transpose through LDS every store instruction writes two whole row segments
+// (2 x 512 B fp32, 2 x 256 B bf16), and accumulate mode reads the old values
+// the same way.  The accumulators go through LDS as fp32 in two passes of 64
+// rows (bf16 output is rounded once, after the optional add).  The LDS image
+// holds rows of 32 16-byte chunks with chunk c of row r at slot c ^ (r & 31),
+// so both the scattered writes and the row reads spread over all banks.  The
+// caller must keep other waves' LDS traffic out of `stage` until this returns
+// (its LDS reads are complete once its last store is issued).
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, int e, int64_t mb, int64_t nb,
+                                                       int lane, const f32x16 (&acc)[4][4], lds_char* stage) {
+    const int64_t H = p.hidden, N = p.n;
+    const int l32 = lane & 31, lhi = lane >> 5;
+    const int c_read = lane & 31;
+    const int64_t nn = nb + 4 * c_read;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * pass + ii;
+            const int r = 32 * ii + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = 8 * j + 2 * g + lhi;   // columns 32j + 8g + 4lhi .. +3
+                    const f32x4 w = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
+                                     acc[j][i][4 * g + 3]};
+                    lds_store_16B(stage, (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)), __builtin_bit_cast(i32x4, w));
+                }
+        }
+#pragma unroll 8
+        for (int q = 0; q < 32; ++q) {
+            const int r = 2 * q + (lane >> 5);
+            f32x4 v = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + ((c_read ^ (r & 31)) << 4))));
+            const int64_t m = mb + 64 * pass + r;
+            if (m >= H || nn >= N) continue;
+            const int64_t idx = ((int64_t)e * H + m) * N + nn;
+            if constexpr (OUT_BF16) {
+                i32x2* dst = (i32x2*)((char*)p.out + idx * 2);
+                if (p.accumulate) {
+                    const i32x2 old = *dst;
+                    v[0] += bf16_lo((uint32_t)old[0]);
+                    v[1] += bf16_hi((uint32_t)old[0]);
+                    v[2] += bf16_lo((uint32_t)old[1]);
+                    v[3] += bf16_hi((uint32_t)old[1]);
+                }
+                const i32x2 w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+                *dst = w;
+            } else {
+                f32x4* dst = (f32x4*)((char*)p.out + idx * 4);
+                if (p.accumulate) v += *dst;
+                *dst = v;
+            }
+        }
+    }
+}
+
 }  // namespace kgw
