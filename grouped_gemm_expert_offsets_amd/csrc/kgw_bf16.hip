@@ -26,8 +26,12 @@
 //     per-expert token ranges come from scalar loads of the offsets.
 //     The fragments of step s+1 are read from LDS while the second half of
 //     step s's MFMAs runs, so the MFMAs never wait on LDS latency; one
-//     barrier per step, placed between the two halves, both publishes the
-//     next stage and frees the stage just consumed;
+//     barrier per step both publishes the next stage and frees the stage
+//     just consumed.  Each wave issues eight 1 KiB loads per step, one after
+//     every fourth MFMA: the CU's path from L2 moves about 60 B per clock,
+//     and a burst of loads from all four waves at once queues there and
+//     stalls their MFMA issue (one wave per SIMD has no other wave to cover
+//     the stall);
 //   - the XOR swizzles live on the global-address side: each lane of a direct
 //     load fetches the chunk that belongs at its LDS slot.  A rows (128 B):
 //     16-byte chunk ^ ((row>>1)&7); B rows (512 B): chunk ^ 4*(k&3).  Both keep
@@ -139,21 +143,34 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
             b_voff[t] = (uint32_t)krow * (uint32_t)(N * 2) + (uint32_t)min(8 * b_q[t], cols_valid - 8) * 2u;
         }
 
-        // Direct loads.  A stage a (steps 2a, 2a+1) goes to A slot a % NA, B step s
-        // to B slot s % NB.  Stages past the expert's range use an empty buffer
-        // range: the loads fetch nothing (the slot is never read by an MFMA),
-        // which keeps the loop below free of branches and its vmcnt counts uniform.
-        auto issue_a = [&](int a) {
-            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave) * 1024u;
+        // Direct loads.  A stage a (steps 2a, 2a+1) goes to A slot a % NA in two
+        // halves of four loads per wave, B step s to B slot s % NB.  Stages past
+        // the expert's range use an empty buffer range: the loads fetch nothing
+        // (the slot is never read by an MFMA), which keeps the loop below free of
+        // branches and its vmcnt counts uniform.
+        auto dma_a = [&](int a, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
             const i32x4 r = rsrc_words(Abase + (int64_t)a * (4 * BK), 2 * a < ksteps ? 0xFFFFFFFFu : 0u);
-#pragma unroll
-            for (int t = 0; t < A_LOADS; ++t) dma_16B(r, a_voff[t], dst + t * 1024u);
+            dma_16B(r, a_voff[t], dst);
         };
-        auto issue_b = [&](int s) {
-            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (s % NB) * B_STAGE) + (uint32_t)(4 * wave) * 1024u;
-            const i32x4 r = rsrc_words(Bbase + (int64_t)s * BK * N * 2, s < ksteps ? 0xFFFFFFFFu : 0u);
-#pragma unroll
-            for (int t = 0; t < B_LOADS; ++t) dma_16B(r, b_voff[t], dst + t * 1024u);
+        auto dma_b = [&](int sb, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) + (uint32_t)(4 * wave + t) * 1024u;
+            const i32x4 r = rsrc_words(Bbase + (int64_t)sb * BK * N * 2, sb < ksteps ? 0xFFFFFFFFu : 0u);
+            dma_16B(r, b_voff[t], dst);
+        };
+        // The loads of step s (also for the prologue's virtual steps s < 0), in
+        // issue order: B step s+4, then half of an A stage -- for odd s the first
+        // half of A stage (s+5)/2, for even s the second half of A stage (s+4)/2.
+        // Every slot written this way was last read by the fragment reads made
+        // during step s-1 or earlier.
+        auto dma_step = [&](int s, int d) {
+            if (d < B_LOADS) {
+                if (s + NB >= 0) dma_b(s + NB, d);
+            } else if (s & 1) {
+                dma_a((s + 5) / 2, d - B_LOADS);
+            } else {
+                dma_a((s + 4) / 2, d);
+            }
         };
 
         f32x16 acc[4][4];
@@ -198,35 +215,19 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
             const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             acc[j][i] = mfma_bf16_32x32x16(__builtin_bit_cast(i32x4, v), f.a[ks][i], acc[j][i]);
         };
-        auto dma_one = [&](int s, bool odd, int d) {
-            // d < B_LOADS: B step s+NB; then (odd steps) A stage (s+1)/2 + NA-1.
-            if (d < B_LOADS) {
-                const int sb = s + NB;
-                const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) +
-                                     (uint32_t)(4 * wave + d) * 1024u;
-                const i32x4 r = rsrc_words(Bbase + (int64_t)sb * BK * N * 2, sb < ksteps ? 0xFFFFFFFFu : 0u);
-                dma_16B(r, b_voff[d], dst);
-            } else if (odd) {
-                const int a = (s + 1) / 2 + NA - 1, t = d - B_LOADS;
-                const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
-                const i32x4 r = rsrc_words(Abase + (int64_t)a * (4 * BK), 2 * a < ksteps ? 0xFFFFFFFFu : 0u);
-                dma_16B(r, a_voff[t], dst);
-            }
-        };
-
         // The partial vmcnt waits count only this item's direct loads, so the
         // previous item's output stores must have drained first.
         wait_vmcnt<0>();
-        // Prologue in steady-state issue order: A0 B0 B1 A1 B2 B3 A2.  Step 0
-        // needs A0 and B0; 28 loads were issued after B0.
-        issue_a(0);
-        issue_b(0);
-        issue_b(1);
-        issue_a(1);
-        issue_b(2);
-        issue_b(3);
-        issue_a(2);
-        wait_vmcnt<2 * A_LOADS + 3 * B_LOADS>();
+        // Prologue: the loads of virtual steps -5..-1 (A0 B0 A0' B1 A1 B2 A1' B3
+        // A2).  Step 0's fragments need A stage 0 and B step 0; 24 loads were
+        // issued after the second half of A stage 0.
+#pragma unroll
+        for (int d = B_LOADS; d < 2 * B_LOADS; ++d) dma_step(-5, d);
+#pragma unroll
+        for (int v = -4; v < 0; ++v)
+#pragma unroll
+            for (int d = 0; d < 2 * B_LOADS; ++d) dma_step(v, d);
+        wait_vmcnt<6 * B_LOADS>();
         barrier_no_fence();
         Frags f0, f1;
         read_all(0, f0);
@@ -234,37 +235,36 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         // Step s with its fragments in `cur`:
         //   once this wave's reads of step s and its loads of step s+1 are done,
         //   a barrier publishes step s+1 and certifies that every wave is done
-        //   reading step s, whose slots then take B step s+4 and, after an odd
-        //   step (the second of its A stage), A stage (s+1)/2 + 2;
-        //   sub-step 0's 16 MFMAs, each followed by one of those direct loads;
-        //   sub-step 1's 16 MFMAs, each followed by one or two of the 24
-        //   fragment reads of step s+1 (so the LDS latency hides behind MFMAs).
-        // With B issued before A, the loads of step s+1 are complete once at most
-        // 24 (even s) or 16 (odd s) later loads remain outstanding (traced from
-        // the prologue order above).  sched_barrier(0) pins this interleaving; the
+        //   reading step s;
+        //   32 MFMAs, every fourth one followed by one of the step's eight direct
+        //   loads (spread out so that the four waves do not queue their loads at
+        //   the memory unit at once, which would stall their MFMA issue), and the
+        //   last 16 followed by the 24 fragment reads of step s+1 (so the LDS
+        //   latency hides behind MFMAs).
+        // Step s+1 needs B step s+1 (issued during step s-3, first of its eight
+        // loads) and, for odd s, A stage (s+1)/2 (second half issued during step
+        // s-3, last of its loads): at most 20 (even s) or 16 (odd s) later loads
+        // may remain outstanding.  sched_barrier(0) pins this interleaving; the
         // compiler would otherwise cluster the memory operations.
         auto body = [&](int s, bool odd, Frags& cur, Frags& nxt) {
             wait_lgkmcnt0();
-            if (odd) wait_vmcnt<A_LOADS + 2 * B_LOADS>();
-            else wait_vmcnt<2 * A_LOADS + 2 * B_LOADS>();
+            if (odd) wait_vmcnt<4 * B_LOADS>();
+            else wait_vmcnt<5 * B_LOADS>();
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                mfma_one(cur, 0, k);
+            for (int k = 0; k < 32; ++k) {
+                mfma_one(cur, k >> 4, k & 15);
                 __builtin_amdgcn_sched_barrier(0);
-                if (k < B_LOADS + A_LOADS) dma_one(s, odd, k);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                mfma_one(cur, 1, k);
-                __builtin_amdgcn_sched_barrier(0);
-                if (k < 8) {
-                    read_one(s + 1, 2 * k, nxt);
-                    read_one(s + 1, 2 * k + 1, nxt);
-                } else {
-                    read_one(s + 1, 8 + k, nxt);
+                if ((k & 3) == 0) dma_step(s, k >> 2);
+                if (k >= 16) {
+                    const int q = k - 16;
+                    if (q < 8) {
+                        read_one(s + 1, 2 * q, nxt);
+                        read_one(s + 1, 2 * q + 1, nxt);
+                    } else {
+                        read_one(s + 1, 8 + q, nxt);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
