@@ -7,28 +7,37 @@
 // bits below it are kept (1 + 2^-12 survives, 1 + 2^-14 loses the small
 // term); groups and the fp32 accumulator are added in full fp32.  On
 // block-quantised Gaussian operands this gives a relative Frobenius error of
-// about 1.5e-5 against the exact sum.  The default fp8 kernel
-// (kgw_fp8_exact.hip) avoids this by converting to bf16 and using the bf16
-// MFMA; this one is the opt-in fast path.
+// about 1.5e-5 against the exact sum: far below the resolution of a bf16
+// output, above the 1e-5 asked of an fp32 output.  kgw_fp8_exact.hip converts
+// to bf16 and uses the bf16 MFMA instead.
 //
 // Same operation and work decomposition as the bf16 kernel (cuDNN "Grouped GEMM
 // + WGrad (Unified)", section "Operation"); the operands are fp8 with per-block
 // 1x128 power-of-two scales (llm-infra-atlas "05 Grouped GEMM", section 3),
-// the blocks running along the contracted token axis.
+// the blocks running along the contracted token axis.  The scales are applied
+// inside the MFMA: each lane hands the instruction the scale byte of its row
+// (A) or column (B).  Every 64-token MFMA lies inside one 128-token block, so
+// each output row m uses the single byte sfa[block][m] and each column n the
+// single byte sfb[block][n]: the products are qa*qb*2^(ea-127)*2^(eb-127) with
+// no dequantisation pass.
 //
-// The K step is one scale block (128 tokens).  The scales are applied inside
-// the MFMA: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies each lane's operand by
-// 2^(byte-127) of the scale byte it is given.  Because every 64-token MFMA
-// lies inside one 128-token block, each output row m uses the single byte
-// sfa[block][m] and each column n the single byte sfb[block][n], so the
-// products are exactly qa*qb*2^(ea-127)*2^(eb-127) with no dequantisation
-// pass and no rounding beyond the fp32 accumulation.
-//
-//   - A tile 256 x 128 bytes (token-contiguous rows): fragments are two
-//     16-byte LDS reads (rows swizzled: chunk ^ ((row>>1)&7));
-//   - B tile 128 x 256 bytes (N-contiguous rows): fragments are four
-//     transposing ds_read_b64_tr_b8 (rows swizzled: chunk ^ 2*(k&7));
-//   - double-buffered LDS ring, register staging, 4 waves of 128x128.
+// Pipeline (the bf16 kernel's, in bytes): K step of 64 tokens = 16 MFMAs of
+// 32x32x64 per wave (4 waves, each 128x128 of the 256x256 tile).  Direct
+// global->LDS loads, no register staging:
+//   - A in 128-token stages (256 rows x 128 B, one scale block, every row a
+//     full 128-byte line) in a 3-slot ring, swizzle chunk ^ ((row>>1)&7);
+//     fragments are two 16-byte LDS reads;
+//   - B in 64-token stages (64 rows x 256 B) in a 3-slot ring, swizzle
+//     chunk ^ 2*(k&7); fragments are four transposing ds_read_b64_tr_b8;
+//   - the scale bytes of each block travel with its A stage into a 3-slot
+//     scale ring: byte-wide direct loads, each lane's byte landing as one
+//     zero-extended dword (so a lane reads its scale as a ready MFMA operand
+//     and any hidden / n is handled byte by byte);
+//   - each wave issues ten loads per step (B step s+3, half an A stage, two
+//     scale loads), spread over its 16 MFMAs; one barrier per step; the
+//     fragments of step s+1 are read during the second half of step s;
+//   - the finished tile leaves through the idle rings (LDS transpose, whole
+//     row segments per store).
 #include "kgw_device.h"
 #include "kgw_internal.h"
 #include "kgw_tile_io.h"
@@ -36,52 +45,73 @@
 namespace kgw {
 namespace {
 
-constexpr int BM = kFp8BM, BN = kFp8BN, BK = kFp8BK;
+constexpr int BM = kFp8BM, BN = kFp8BN;
+constexpr int KS = 64;                      // tokens per K step (one MFMA deep)
 constexpr int NT = 256;
-constexpr int A_STAGE = BM * BK;            // 32 KiB: 256 rows x 128 B
-constexpr int B_STAGE = BK * BN;            // 32 KiB: 128 rows x 256 B
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int LDS_TILES = 2 * STAGE;
+constexpr int NA = 3;                       // A ring: 3 stages of 128 tokens (2 K steps)
+constexpr int NB = 3;                       // B ring: 3 stages of 64 tokens (1 K step)
+constexpr int A_STAGE = BM * 2 * KS;        // 32 KiB: 256 rows x 128 B
+constexpr int B_STAGE = KS * BN;            // 16 KiB: 64 rows x 256 B
+constexpr int SC_WAVE = 1024;               // per wave and block: 128 sa + 128 sb dwords
+constexpr int SC_STAGE = 4 * SC_WAVE;       // 4 KiB per block
+constexpr int B_RING = NA * A_STAGE;        // byte offsets of the rings
+constexpr int SC_RING = B_RING + NB * B_STAGE;
+constexpr int LDS_TOTAL = SC_RING + NA * SC_STAGE;   // 156 KiB
 constexpr int GROUP_M = 4;
+constexpr int B_LOADS = 4;                  // direct loads per wave per B stage
+constexpr int LOADS_PER_STEP = 10;          // 4 B + 4 A + 2 scale
 
-static_assert(BM == 256 && BN == 256 && BK == 128, "index math below assumes 256x256x128");
+static_assert(BM == 256 && BN == 256 && kFp8BK == 2 * KS, "index math below assumes 256x256, 128-token blocks");
+static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+static_assert(2 * 128 * 512 <= SC_RING, "output staging must fit below the scale ring");
+
+// Direct byte load to LDS: every lane fetches the byte at `voff` of the buffer;
+// lane L's byte lands zero-extended in the dword at `lds_dst` + 4 * L.
+__device__ __forceinline__ void dma_1B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
+}
+
+__device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
+}
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[LDS_TILES + kMaxExperts * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
-    int32_t* s_end = (int32_t*)(smem + LDS_TILES);
+    const uint32_t tiles_addr = lds_addr(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1;
     const int wn = wave >> 1;
     const int64_t T = p.tokens_sum, H = p.hidden, N = p.n;
 
-    for (int e = tid; e < p.num_experts; e += NT) {
-        int64_t v = p.offsets[e];
-        v = v < 0 ? 0 : (v > T ? T : v);
-        s_end[e] = (int32_t)v;
-    }
-    __syncthreads();
+    // Direct-load slots of this lane.  A: wave instruction t (0..7) fills LDS
+    // rows 64*wave + 8*t + (lane>>3), 16-byte slot lane&7, which holds logical
+    // chunk (lane&7) ^ ((row>>1)&7) -- that depends on t only through t&1.  B:
+    // instruction t (0..3) fills k-rows 16*wave + 4*t + (lane>>4), slot lane&15
+    // = logical chunk ^ 2*(k&7), again a function of t&1.
+    const int a_q0 = (lane & 7) ^ ((lane >> 4) & 7);
+    const int a_q1 = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+    const int b_q0 = (lane & 15) ^ (2 * ((lane >> 4) & 7));
+    const int b_q1 = (lane & 15) ^ (2 * ((4 + (lane >> 4)) & 7));
 
-    // A chunk c = tid + 256*pp: row (tid>>3) + 32*pp, 16-byte chunk tid&7.
-    const uint32_t a_lds0 = (uint32_t)(tid >> 3) * 128u + (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-    // B chunk c = tid + 256*pp: k-row (tid>>4) + 16*pp, 16-byte chunk tid&15.
-    const uint32_t b_lds0 = (uint32_t)(tid >> 4) * 256u + (uint32_t)(((tid & 15) ^ (2 * ((tid >> 4) & 7))) << 4);
-
+    // Fragment read offsets (fixed per lane).  A: row wm*128 + 32i + l32, the
+    // 32 tokens 32*lhi.. of the step's 64-token half of the stage.  B: lane l
+    // gets column 32j + l32 of the wave's half, tokens 32*lhi + 0..31, from four
+    // 8x16 transposed blocks; block j's offset is block 0's with the 16-byte
+    // chunk index XOR 2j (the unswizzled chunk 8wn + (g16&1) + 2j has no carry).
     const int l32 = lane & 31, lhi = lane >> 5;
     const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u;
-    const int a_sw = (lane >> 1) & 7;
+    const int a_sw = (l32 >> 1) & 7;
     const int g16 = lane >> 4, i16 = lane & 15;
-    uint32_t b_frag[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int krow = 32 * (g16 >> 1) + (i16 >> 1);
-        const int chunk = (8 * wn + 2 * j + (g16 & 1)) ^ (2 * (i16 >> 1));
-        b_frag[j] = (uint32_t)krow * 256u + (uint32_t)chunk * 16u + (uint32_t)(i16 & 1) * 8u;
-    }
+    const uint32_t b_frag0 = (uint32_t)(32 * (g16 >> 1) + (i16 >> 1)) * 256u +
+                             (uint32_t)((8 * wn + (g16 & 1)) ^ (2 * (i16 >> 1))) * 16u + (uint32_t)(i16 & 1) * 8u;
+    // Scale dwords of this wave: sa row r at 4r, sb column c at 512 + 4c.
+    const uint32_t sc_wave = (uint32_t)(SC_RING + wave * SC_WAVE);
 
     const int TT = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
@@ -94,10 +124,14 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
-        int32_t begin = e ? s_end[e - 1] : 0;
-        const int32_t end = max(begin, s_end[e]);
-        begin &= ~(BK - 1);
-        const int ksteps = (end - begin) / BK;
+        // Token range, clamped into [0, tokens_sum], used in whole 128-token blocks.
+        const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
+        const int64_t raw_end = p.offsets[e];
+        int32_t begin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
+        const int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        begin &= ~(2 * KS - 1);
+        const int nblocks = (end - begin) / (2 * KS);
+        const int ksteps = 2 * nblocks;
         if (ksteps == 0) {
             if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, e, m0, n0, tid);
             continue;
@@ -105,24 +139,65 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
 
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * T + begin;
         const uint8_t* Bbase = (const uint8_t*)p.B + (int64_t)begin * N + n0;
-        const uint8_t* SAbase = p.sfa + (int64_t)(begin / BK) * H;
-        const uint8_t* SBbase = p.sfb + (int64_t)(begin / BK) * N;
-        const int rows_valid = (int)min<int64_t>(BM, H - m0);
-        const int cols_valid = (int)min<int64_t>(BN, N - n0);
-        uint32_t a_voff[8], b_voff[8], sa_voff[4], sb_voff[4];
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) {
-            const int row = min((tid >> 3) + 32 * pp, rows_valid - 1);
-            a_voff[pp] = (uint32_t)row * (uint32_t)T + (uint32_t)(tid & 7) * 16u;
-        }
-        const uint32_t bcol = (uint32_t)min((tid & 15) * 16, cols_valid - 16);
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) b_voff[pp] = (uint32_t)((tid >> 4) + 16 * pp) * (uint32_t)N + bcol;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa_voff[i] = (uint32_t)(m0 + min(wm * 128 + 32 * i + l32, rows_valid - 1));
-            sb_voff[i] = (uint32_t)(n0 + min(wn * 128 + 32 * i + l32, cols_valid - 1));
-        }
+        const uint8_t* SAbase = p.sfa + (int64_t)(begin / (2 * KS)) * H;
+        const uint8_t* SBbase = p.sfb + (int64_t)(begin / (2 * KS)) * N;
+        // Rows of A past hidden and columns of B past n belong to outputs that are
+        // never stored; the buffer ranges below end at the last valid A row and at
+        // the end of B, so such lanes read zeros or bytes of B's next row, never
+        // memory outside the operands.
+        const int64_t a_rows_bytes = min<int64_t>(BM, H - m0) * T - begin;
+        const int64_t b_bytes = (T - begin) * N - n0;
+        const uint32_t a_voff0 = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)T;
+        const uint32_t b_voff0 = (uint32_t)(16 * wave + (lane >> 4)) * (uint32_t)N;
+        // Scale bytes: sa for rows m0 + wm*128 + 64h + lane, sb for columns
+        // n0 + wn*128 + 64h + lane (h = 0, 1); bytes past hidden / n read as 0
+        // through the buffer range and belong to rows / columns never stored.
+        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane);
+        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane);
+
+        // Direct loads.  A stage a (steps 2a, 2a+1; scale block a) goes to A slot
+        // a % NA, B step s to B slot s % NB.  Stages past the expert's range use
+        // an empty buffer range: the loads fetch nothing (the slot is never read
+        // by an MFMA), keeping the loop free of branches and its vmcnt counts
+        // uniform.
+        auto dma_a = [&](int a, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
+            const i32x4 r = rsrc_words(Abase + (int64_t)a * (2 * KS),
+                                       a < nblocks ? (uint32_t)(a_rows_bytes - (int64_t)a * (2 * KS)) : 0u);
+            const uint32_t voff = a_voff0 + (uint32_t)(8 * t) * (uint32_t)T + (uint32_t)((t & 1) ? a_q1 : a_q0) * 16u;
+            dma_16B(r, voff, dst);
+        };
+        auto dma_b = [&](int sb, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) + (uint32_t)(4 * wave + t) * 1024u;
+            const i32x4 r = rsrc_words(Bbase + (int64_t)sb * KS * N,
+                                       sb < ksteps ? (uint32_t)min<int64_t>(b_bytes - (int64_t)sb * KS * N, 0xFFFFFFFFll) : 0u);
+            const uint32_t voff = b_voff0 + (uint32_t)(4 * t) * (uint32_t)N + (uint32_t)((t & 1) ? b_q1 : b_q0) * 16u;
+            dma_16B(r, voff, dst);
+        };
+        // Scale load h (0, 1) of block a: operand B (sb) or A (sa).
+        auto dma_s = [&](int a, bool b_side, int h) {
+            const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((a % NA) * SC_STAGE) +
+                                 (b_side ? 512u : 0u) + (uint32_t)h * 256u;
+            const uint8_t* base = b_side ? SBbase + (int64_t)a * N : SAbase + (int64_t)a * H;
+            const uint32_t limit = a < nblocks ? (uint32_t)(b_side ? N : H) : 0u;
+            dma_1B(rsrc_words(base, limit), (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u, dst);
+        };
+        // The loads of step s (also for the prologue's virtual steps s < 0), in
+        // issue order: B step s+3, then half of an A stage and two scale loads
+        // of its block -- for odd s the first half of A stage (s+5)/2 and its sa
+        // bytes, for even s the second half of A stage (s+4)/2 and its sb bytes.
+        // Every slot written this way was last read during step s-1 or earlier.
+        auto dma_step = [&](int s, int d) {
+            if (d < B_LOADS) {
+                if (s + NB >= 0) dma_b(s + NB, d);
+            } else if (d < 2 * B_LOADS) {
+                if (s & 1) dma_a((s + 5) / 2, d - B_LOADS);
+                else dma_a((s + 4) / 2, d);
+            } else {
+                if (s & 1) dma_s((s + 5) / 2, false, d - 2 * B_LOADS);
+                else dma_s((s + 4) / 2, true, d - 2 * B_LOADS);
+            }
+        };
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -132,82 +207,102 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-        i32x4 ra[8], rb[8];
-        int sa_n[4], sb_n[4], sa_c[4], sb_c[4];
-        auto gload = [&](int s) {
-            const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (int64_t)s * BK, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (int64_t)s * BK * N, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rSA = make_rsrc(SAbase + (int64_t)s * H, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rSB = make_rsrc(SBbase + (int64_t)s * N, 0xFFFFFFFFu);
+        // Fragments of one K step plus the scales of its block: MFMA operands of
+        // 32 bytes (tokens 32*lhi + 0..31 of one row m or column n).
+        struct Frags {
+            i32x8 a[4];
+            i32x8 b[4];
+            int sa[4], sb[4];
+        };
+        // Fragment read number r (0..31) of step s: A halves (8), B pieces (16),
+        // then the block's scale dwords (8).
+        auto read_one = [&](int s, int r, Frags& f) {
+            if (r < 8) {
+                const int i = r >> 1, h = r & 1;
+                const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
+                const uint32_t chunk = (uint32_t)(((4 * (s & 1) + 2 * lhi + h) ^ a_sw) << 4);
+                const i32x4 v = lds_load_16B(As, a_frag_row + i * 4096u + chunk);
 #pragma unroll
-            for (int pp = 0; pp < 8; ++pp) ra[pp] = buffer_load_16B(rA, a_voff[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) rb[pp] = buffer_load_16B(rB, b_voff[pp]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sa_n[i] = buffer_load_u8(rSA, sa_voff[i]);
-                sb_n[i] = buffer_load_u8(rSB, sb_voff[i]);
+                for (int x = 0; x < 4; ++x) f.a[i][4 * h + x] = v[x];
+            } else if (r < 24) {
+                const int j = (r - 8) >> 2, q = (r - 8) & 3;
+                const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
+                const i32x2 v = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * j)) + q * 2048u);
+                f.b[j][2 * q] = v[0];
+                f.b[j][2 * q + 1] = v[1];
+            } else {
+                const lds_char* Sc = tiles + sc_wave + ((s >> 1) % NA) * SC_STAGE;
+                const int q = r - 24;
+                if (q < 4) f.sa[q] = lds_load_4B(Sc, (uint32_t)(4 * (32 * q + l32)));
+                else f.sb[q - 4] = lds_load_4B(Sc, (uint32_t)(512 + 4 * (32 * (q - 4) + l32)));
             }
         };
-        auto lstore = [&](int buf) {
-            lds_char* As = tiles + buf * STAGE;
-            lds_char* Bs = As + A_STAGE;
+        auto read_all = [&](int s, Frags& f) {
 #pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(As, a_lds0 + pp * 4096u, ra[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(Bs, b_lds0 + pp * 4096u, rb[pp]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sa_c[i] = sa_n[i];
-                sb_c[i] = sb_n[i];
-            }
+            for (int r = 0; r < 32; ++r) read_one(s, r, f);
         };
-        auto compute = [&](int buf) {
-            const lds_char* As = tiles + buf * STAGE;
-            const lds_char* Bs = As + A_STAGE;
-#pragma unroll
-            for (int ks = 0; ks < BK / 64; ++ks) {
-                const int q0 = 4 * ks + 2 * lhi;
-                const uint32_t c0 = (uint32_t)((q0 ^ a_sw) << 4);
-                const uint32_t c1 = (uint32_t)(((q0 + 1) ^ a_sw) << 4);
-                i32x8 af[4], bf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const i32x4 x = lds_load_16B(As, a_frag_row + i * 4096u + c0);
-                    const i32x4 y = lds_load_16B(As, a_frag_row + i * 4096u + c1);
-                    const i32x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-                    af[i] = v;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t base = b_frag[j] + ks * 16384u;
-                    const i32x2 t0 = lds_read_tr8(Bs, base);
-                    const i32x2 t1 = lds_read_tr8(Bs, base + 2048u);
-                    const i32x2 t2 = lds_read_tr8(Bs, base + 4096u);
-                    const i32x2 t3 = lds_read_tr8(Bs, base + 6144u);
-                    const i32x8 v = {t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
-                    bf[j] = v;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[j][i] = mfma_scale_e4m3_32x32x64(bf[j], af[i], acc[j][i], sb_c[j], sa_c[i]);
-            }
+        // MFMA number k (0..15): N block k/4 times M block k%4.
+        auto mfma_one = [&](const Frags& f, int k) {
+            const int j = k >> 2, i = k & 3;
+            acc[j][i] = mfma_scale_e4m3_32x32x64(f.b[j], f.a[i], acc[j][i], f.sb[j], f.sa[i]);
         };
 
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int s = 0; s < ksteps; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < ksteps) gload(s + 1);
-            compute(cur);
-            if (s + 1 < ksteps) lstore(cur ^ 1);
-            __syncthreads();
+        // The partial vmcnt waits count only this item's direct loads, so the
+        // previous item's output stores must have drained first.
+        wait_vmcnt<0>();
+        // Prologue: the loads of virtual steps -5..-1.  Step 0's fragments need
+        // A stage 0 with its scales and B step 0; 26 loads were issued after B 0.
+#pragma unroll
+        for (int v = -5; v < 0; ++v)
+#pragma unroll
+            for (int d = 0; d < LOADS_PER_STEP; ++d) dma_step(v, d);
+        wait_vmcnt<26>();
+        barrier_no_fence();
+        Frags f0, f1;
+        read_all(0, f0);
+
+        // Step s with its fragments in `cur`: once this wave's reads of step s
+        // and the loads step s+1 needs are done, a barrier publishes step s+1 and
+        // certifies that every wave is done reading step s.  Step s+1 needs B
+        // step s+1 (issued first in step s-2) and, for odd s, A stage (s+1)/2 and
+        // its scales (completed in step s-3): at most 16 later loads may remain.
+        // 16 MFMAs, the step's ten loads spread among them (one or two MFMAs
+        // apart), the 32 fragment reads of step s+1 after the last eight.
+        // sched_barrier(0) pins this interleaving.
+        auto body = [&](int s, Frags& cur, Frags& nxt) {
+            wait_lgkmcnt0();
+            wait_vmcnt<16>();
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                mfma_one(cur, k);
+                __builtin_amdgcn_sched_barrier(0);
+                // loads d at MFMAs 0,1,3,4,6,8,9,11,12,14
+                constexpr int slot_of[LOADS_PER_STEP] = {0, 1, 3, 4, 6, 8, 9, 11, 12, 14};
+#pragma unroll
+                for (int d = 0; d < LOADS_PER_STEP; ++d)
+                    if (slot_of[d] == k) dma_step(s, d);
+                if (k >= 8) {
+#pragma unroll
+                    for (int r = 4 * (k - 8); r < 4 * (k - 7); ++r) read_one(s + 1, r, nxt);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        for (int s = 0; s < ksteps; s += 2) {
+            body(s, f0, f1);
+            body(s + 1, f1, f0);
         }
-
-        store_wave_tile<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc);
+        // The rings become the output staging area: every wave must be done
+        // reading them and every direct load (the empty ones past the range
+        // included) must have landed.
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier_no_fence();
+        store_wave_tile_staged<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        // The next item's direct loads overwrite the staging areas.
+        barrier_no_fence();
     }
 }
 
