@@ -16,14 +16,21 @@
 // rounding, unlike the native fp8 MFMA whose internal sum drops low-order bits
 // (see kgw_fp8_native.hip).
 //
-//   - K step = one scale block of 128 tokens; per K step each lane needs one
-//     scale per fragment: sfa[block][m] for its four M blocks and
-//     sfb[block][n] for its four N blocks;
-//   - A tile 256 x 128 bytes (token-contiguous rows, chunk ^ ((row>>1)&7)):
-//     fragments are 8-byte LDS reads;
-//   - B tile 128 x 256 bytes (N-contiguous rows, chunk ^ 2*(k&7)): fragments
-//     are transposing ds_read_b64_tr_b8 reads, 8 tokens of one column per lane;
-//   - double-buffered LDS ring, register staging, 4 waves of 128x128.
+// Loads and LDS layout are those of the native fp8 kernel (both kernels move
+// the same bytes): A in 128-token stages (256 rows x 128 B, one scale block)
+// in a 3-slot ring, B in 64-token stages (64 rows x 256 B) in a 3-slot ring,
+// the block's scale bytes by byte-wide direct loads into a 3-slot scale ring,
+// ten direct loads per wave per 64-token step spread over its MFMAs, one
+// barrier per step.  Inside a step the wave runs four 16-token groups of 16
+// bf16 MFMAs (32x32x16; 4 waves, each 128x128 of the 256x256 tile):
+//   - raw fp8 fragments of step s+1 (8-byte A reads, transposing
+//     ds_read_b64_tr_b8 B reads) are read from LDS group by group during the
+//     same group of step s, the block's scale dwords during group 0;
+//   - the eight fragments of group g+1 are converted while group g's MFMAs run
+//     (two converted sets alternate), and group 0 of step s+1 while group 3
+//     runs, so the conversions hide behind the MFMAs;
+//   - the finished tile leaves through the idle rings (LDS transpose, whole
+//     row segments per store).
 #include "kgw_device.h"
 #include "kgw_internal.h"
 #include "kgw_tile_io.h"
@@ -31,53 +38,72 @@
 namespace kgw {
 namespace {
 
-constexpr int BM = kFp8BM, BN = kFp8BN, BK = kFp8BK;
+constexpr int BM = kFp8BM, BN = kFp8BN;
+constexpr int KS = 64;                      // tokens per K step
 constexpr int NT = 256;
-constexpr int A_STAGE = BM * BK;            // 32 KiB: 256 rows x 128 B
-constexpr int B_STAGE = BK * BN;            // 32 KiB: 128 rows x 256 B
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int LDS_TILES = 2 * STAGE;
+constexpr int NA = 3;                       // A ring: 3 stages of 128 tokens (2 K steps)
+constexpr int NB = 3;                       // B ring: 3 stages of 64 tokens (1 K step)
+constexpr int A_STAGE = BM * 2 * KS;        // 32 KiB: 256 rows x 128 B
+constexpr int B_STAGE = KS * BN;            // 16 KiB: 64 rows x 256 B
+constexpr int SC_WAVE = 1024;               // per wave and block: 128 sa + 128 sb dwords
+constexpr int SC_STAGE = 4 * SC_WAVE;       // 4 KiB per block
+constexpr int B_RING = NA * A_STAGE;        // byte offsets of the rings
+constexpr int SC_RING = B_RING + NB * B_STAGE;
+constexpr int LDS_TOTAL = SC_RING + NA * SC_STAGE;   // 156 KiB
 constexpr int GROUP_M = 4;
+constexpr int B_LOADS = 4;                  // direct loads per wave per B stage
+constexpr int LOADS_PER_STEP = 10;          // 4 B + 4 A + 2 scale
 
-static_assert(BM == 256 && BN == 256 && BK == 128, "index math below assumes 256x256x128");
+static_assert(BM == 256 && BN == 256 && kFp8BK == 2 * KS, "index math below assumes 256x256, 128-token blocks");
+static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+static_assert(2 * 128 * 512 <= SC_RING, "output staging must fit below the scale ring");
+
+// Direct byte load to LDS: every lane fetches the byte at `voff` of the buffer;
+// lane L's byte lands zero-extended in the dword at `lds_dst` + 4 * L.
+__device__ __forceinline__ void dma_1B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
+}
+
+__device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
+}
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[LDS_TILES + kMaxExperts * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
-    int32_t* s_end = (int32_t*)(smem + LDS_TILES);
+    const uint32_t tiles_addr = lds_addr(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1;
     const int wn = wave >> 1;
     const int64_t T = p.tokens_sum, H = p.hidden, N = p.n;
 
-    for (int e = tid; e < p.num_experts; e += NT) {
-        int64_t v = p.offsets[e];
-        v = v < 0 ? 0 : (v > T ? T : v);
-        s_end[e] = (int32_t)v;
-    }
-    __syncthreads();
+    // Direct-load slots (as in the native fp8 kernel).  A: wave instruction t
+    // (0..7) fills LDS rows 64*wave + 8*t + (lane>>3), 16-byte slot lane&7 =
+    // logical chunk ^ ((row>>1)&7), a function of t&1.  B: instruction t (0..3)
+    // fills k-rows 16*wave + 4*t + (lane>>4), slot lane&15 = chunk ^ 2*(k&7).
+    const int a_q0 = (lane & 7) ^ ((lane >> 4) & 7);
+    const int a_q1 = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+    const int b_q0 = (lane & 15) ^ (2 * ((lane >> 4) & 7));
+    const int b_q1 = (lane & 15) ^ (2 * ((4 + (lane >> 4)) & 7));
 
-    // A chunk c = tid + 256*pp: row (tid>>3) + 32*pp, 16-byte chunk tid&7.
-    const uint32_t a_lds0 = (uint32_t)(tid >> 3) * 128u + (uint32_t)(((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-    // B chunk c = tid + 256*pp: k-row (tid>>4) + 16*pp, 16-byte chunk tid&15.
-    const uint32_t b_lds0 = (uint32_t)(tid >> 4) * 256u + (uint32_t)(((tid & 15) ^ (2 * ((tid >> 4) & 7))) << 4);
-
-    // Fragment of K sub-step ks (16 tokens): lane holds tokens 16ks + 8*lhi + 0..7.
+    // Fragment reads of 16-token group g (tokens 16g + 8*lhi + 0..7 of the
+    // step).  A: row wm*128 + 32i + l32, 8 bytes at token offset 64*(s&1) +
+    // 16g + 8*lhi of the stage row: 16-byte chunk 4*(s&1) + g, half lhi.  B:
+    // column 32j + l32 of the wave's half, one transposed 8x16 block at k-rows
+    // 16g + 8*lhi + 0..7; block j's offset is block 0's with the chunk XOR 2j.
     const int l32 = lane & 31, lhi = lane >> 5;
     const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u + (uint32_t)lhi * 8u;
-    const int a_sw = (lane >> 1) & 7;
+    const int a_sw = (l32 >> 1) & 7;
     const int g16 = lane >> 4, i16 = lane & 15;
-    uint32_t b_frag[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int krow = 8 * (g16 >> 1) + (i16 >> 1);
-        const int chunk = (8 * wn + 2 * j + (g16 & 1)) ^ (2 * (i16 >> 1));
-        b_frag[j] = (uint32_t)krow * 256u + (uint32_t)chunk * 16u + (uint32_t)(i16 & 1) * 8u;
-    }
+    const uint32_t b_frag0 = (uint32_t)(8 * (g16 >> 1) + (i16 >> 1)) * 256u +
+                             (uint32_t)((8 * wn + (g16 & 1)) ^ (2 * (i16 >> 1))) * 16u + (uint32_t)(i16 & 1) * 8u;
+    // Scale dwords of this wave: sa row r at 4r, sb column c at 512 + 4c.
+    const uint32_t sc_wave = (uint32_t)(SC_RING + wave * SC_WAVE);
 
     const int TT = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
@@ -90,10 +116,14 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
-        int32_t begin = e ? s_end[e - 1] : 0;
-        const int32_t end = max(begin, s_end[e]);
-        begin &= ~(BK - 1);
-        const int ksteps = (end - begin) / BK;
+        // Token range, clamped into [0, tokens_sum], used in whole 128-token blocks.
+        const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
+        const int64_t raw_end = p.offsets[e];
+        int32_t begin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
+        const int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        begin &= ~(2 * KS - 1);
+        const int nblocks = (end - begin) / (2 * KS);
+        const int ksteps = 2 * nblocks;
         if (ksteps == 0) {
             if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, e, m0, n0, tid);
             continue;
@@ -101,24 +131,62 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * T + begin;
         const uint8_t* Bbase = (const uint8_t*)p.B + (int64_t)begin * N + n0;
-        const uint8_t* SAbase = p.sfa + (int64_t)(begin / BK) * H;
-        const uint8_t* SBbase = p.sfb + (int64_t)(begin / BK) * N;
-        const int rows_valid = (int)min<int64_t>(BM, H - m0);
-        const int cols_valid = (int)min<int64_t>(BN, N - n0);
-        uint32_t a_voff[8], b_voff[8], sa_voff[4], sb_voff[4];
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) {
-            const int row = min((tid >> 3) + 32 * pp, rows_valid - 1);
-            a_voff[pp] = (uint32_t)row * (uint32_t)T + (uint32_t)(tid & 7) * 16u;
-        }
-        const uint32_t bcol = (uint32_t)min((tid & 15) * 16, cols_valid - 16);
-#pragma unroll
-        for (int pp = 0; pp < 8; ++pp) b_voff[pp] = (uint32_t)((tid >> 4) + 16 * pp) * (uint32_t)N + bcol;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa_voff[i] = (uint32_t)(m0 + min(wm * 128 + 32 * i + l32, rows_valid - 1));
-            sb_voff[i] = (uint32_t)(n0 + min(wn * 128 + 32 * i + l32, cols_valid - 1));
-        }
+        const uint8_t* SAbase = p.sfa + (int64_t)(begin / (2 * KS)) * H;
+        const uint8_t* SBbase = p.sfb + (int64_t)(begin / (2 * KS)) * N;
+        // Rows of A past hidden and columns of B past n belong to outputs that are
+        // never stored; the buffer ranges end at the last valid A row and at the
+        // end of B, so such lanes read zeros or bytes of B's next row, never
+        // memory outside the operands.
+        const int64_t a_rows_bytes = min<int64_t>(BM, H - m0) * T - begin;
+        const int64_t b_bytes = (T - begin) * N - n0;
+        const uint32_t a_voff0 = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)T;
+        const uint32_t b_voff0 = (uint32_t)(16 * wave + (lane >> 4)) * (uint32_t)N;
+        // Scale bytes: sa for rows m0 + wm*128 + 64h + lane, sb for columns
+        // n0 + wn*128 + 64h + lane (h = 0, 1); bytes past hidden / n read as 0
+        // through the buffer range and belong to rows / columns never stored.
+        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane);
+        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane);
+
+        // Direct loads, as in the native fp8 kernel: A stage a (steps 2a, 2a+1;
+        // scale block a) to A slot a % NA, B step s to B slot s % NB; stages past
+        // the expert's range use an empty buffer range (the loads fetch nothing).
+        auto dma_a = [&](int a, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
+            const i32x4 r = rsrc_words(Abase + (int64_t)a * (2 * KS),
+                                       a < nblocks ? (uint32_t)(a_rows_bytes - (int64_t)a * (2 * KS)) : 0u);
+            const uint32_t voff = a_voff0 + (uint32_t)(8 * t) * (uint32_t)T + (uint32_t)((t & 1) ? a_q1 : a_q0) * 16u;
+            dma_16B(r, voff, dst);
+        };
+        auto dma_b = [&](int sb, int t) {
+            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) + (uint32_t)(4 * wave + t) * 1024u;
+            const i32x4 r = rsrc_words(Bbase + (int64_t)sb * KS * N,
+                                       sb < ksteps ? (uint32_t)min<int64_t>(b_bytes - (int64_t)sb * KS * N, 0xFFFFFFFFll) : 0u);
+            const uint32_t voff = b_voff0 + (uint32_t)(4 * t) * (uint32_t)N + (uint32_t)((t & 1) ? b_q1 : b_q0) * 16u;
+            dma_16B(r, voff, dst);
+        };
+        auto dma_s = [&](int a, bool b_side, int h) {
+            const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((a % NA) * SC_STAGE) +
+                                 (b_side ? 512u : 0u) + (uint32_t)h * 256u;
+            const uint8_t* base = b_side ? SBbase + (int64_t)a * N : SAbase + (int64_t)a * H;
+            const uint32_t limit = a < nblocks ? (uint32_t)(b_side ? N : H) : 0u;
+            dma_1B(rsrc_words(base, limit), (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u, dst);
+        };
+        // The loads of step s (also for the prologue's virtual steps s < 0), in
+        // issue order: B step s+3, then half of an A stage and two scale loads
+        // of its block -- for odd s the first half of A stage (s+5)/2 and its sa
+        // bytes, for even s the second half of A stage (s+4)/2 and its sb bytes.
+        // Every slot written this way was last read during step s-1 or earlier.
+        auto dma_step = [&](int s, int d) {
+            if (d < B_LOADS) {
+                if (s + NB >= 0) dma_b(s + NB, d);
+            } else if (d < 2 * B_LOADS) {
+                if (s & 1) dma_a((s + 5) / 2, d - B_LOADS);
+                else dma_a((s + 4) / 2, d);
+            } else {
+                if (s & 1) dma_s((s + 5) / 2, false, d - 2 * B_LOADS);
+                else dma_s((s + 4) / 2, true, d - 2 * B_LOADS);
+            }
+        };
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -128,68 +196,129 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-        i32x4 ra[8], rb[8];
-        uint32_t sa_n[4], sb_n[4];
-        float fa[4], fb[4];
-        auto gload = [&](int s) {
-            const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (int64_t)s * BK, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (int64_t)s * BK * N, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rSA = make_rsrc(SAbase + (int64_t)s * H, 0xFFFFFFFFu);
-            const __amdgpu_buffer_rsrc_t rSB = make_rsrc(SBbase + (int64_t)s * N, 0xFFFFFFFFu);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) ra[pp] = buffer_load_16B(rA, a_voff[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) rb[pp] = buffer_load_16B(rB, b_voff[pp]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sa_n[i] = buffer_load_u8(rSA, sa_voff[i]);
-                sb_n[i] = buffer_load_u8(rSB, sb_voff[i]);
+        // Raw fp8 fragments of one K step ([block][group], 8 bytes each) plus
+        // the block's scales; and one group's converted bf16 operands.
+        struct Raw {
+            i32x2 a[4][4];
+            i32x2 b[4][4];
+            int sa[4], sb[4];
+            float fa[4], fb[4];
+        };
+        struct Conv {
+            i32x4 a[4];
+            i32x4 b[4];
+        };
+        // Read (g, m) of step s, made after MFMA m of group g: for m < 8 raw
+        // fragment m of group g (A block m, then B block m-4); in group 0, for
+        // m >= 8 the block's scale dword m-8 (sa blocks 0-3, then sb 0-3).
+        auto read_one = [&](int s, int g, int m, Raw& f) {
+            if (m >= 8) {
+                if (g != 0) return;
+                const lds_char* Sc = tiles + sc_wave + ((s >> 1) % NA) * SC_STAGE;
+                const int x = m - 8;
+                if (x < 4) f.sa[x] = lds_load_4B(Sc, (uint32_t)(4 * (32 * x + l32)));
+                else f.sb[x - 4] = lds_load_4B(Sc, (uint32_t)(512 + 4 * (32 * (x - 4) + l32)));
+            } else if (m < 4) {
+                const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
+                const uint32_t chunk = (uint32_t)(((4 * (s & 1) + g) ^ a_sw) << 4);
+                f.a[m][g] = lds_load_8B(As, a_frag_row + m * 4096u + chunk);
+            } else {
+                const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
+                f.b[m - 4][g] = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * (m - 4))) + (uint32_t)g * 4096u);
             }
         };
-        auto lstore = [&](int buf) {
-            lds_char* As = tiles + buf * STAGE;
-            lds_char* Bs = As + A_STAGE;
+        auto scales_to_float = [&](Raw& f) {
 #pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(As, a_lds0 + pp * 4096u, ra[pp]);
-#pragma unroll
-            for (int pp = 0; pp < 8; ++pp) lds_store_16B(Bs, b_lds0 + pp * 4096u, rb[pp]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fa[i] = e8m0_to_f32(sa_n[i]);
-                fb[i] = e8m0_to_f32(sb_n[i]);
+            for (int x = 0; x < 4; ++x) {
+                f.fa[x] = e8m0_to_f32((uint32_t)f.sa[x]);
+                f.fb[x] = e8m0_to_f32((uint32_t)f.sb[x]);
             }
         };
-        auto compute = [&](int buf) {
-            const lds_char* As = tiles + buf * STAGE;
-            const lds_char* Bs = As + A_STAGE;
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const uint32_t a_chunk = (uint32_t)((ks ^ a_sw) << 4);
-                i32x4 af[4], bf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    af[i] = cvt_e4m3x8_bf16(lds_load_8B(As, a_frag_row + i * 4096u + a_chunk), fa[i]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bf[j] = cvt_e4m3x8_bf16(lds_read_tr8(Bs, b_frag[j] + ks * 4096u), fb[j]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][i] = mfma_bf16_32x32x16(bf[j], af[i], acc[j][i]);
-            }
+        // Conversion number c (0..7) of group g: A block c, then B block c-4.
+        auto convert_one = [&](const Raw& f, int g, int c, Conv& cv) {
+            if (c < 4) cv.a[c] = cvt_e4m3x8_bf16(f.a[c][g], f.fa[c]);
+            else cv.b[c - 4] = cvt_e4m3x8_bf16(f.b[c - 4][g], f.fb[c - 4]);
+        };
+        // MFMA number m (0..15) of a group: N block m/4 times M block m%4.
+        auto mfma_one = [&](const Conv& cv, int m) {
+            const int j = m >> 2, i = m & 3;
+            acc[j][i] = mfma_bf16_32x32x16(cv.b[j], cv.a[i], acc[j][i]);
         };
 
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int s = 0; s < ksteps; ++s) {
-            const int cur = s & 1;
-            if (s + 1 < ksteps) gload(s + 1);
-            compute(cur);
-            if (s + 1 < ksteps) lstore(cur ^ 1);
-            __syncthreads();
+        // The partial vmcnt waits count only this item's direct loads, so the
+        // previous item's output stores must have drained first.
+        wait_vmcnt<0>();
+        // Prologue: the loads of virtual steps -5..-1.  Step 0's fragments need
+        // A stage 0 with its scales and B step 0; 26 loads were issued after B 0.
+#pragma unroll
+        for (int v = -5; v < 0; ++v)
+#pragma unroll
+            for (int d = 0; d < LOADS_PER_STEP; ++d) dma_step(v, d);
+        wait_vmcnt<26>();
+        barrier_no_fence();
+        Raw r0, r1;
+        Conv c0, c1;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) read_one(0, g, m, r0);
+        wait_lgkmcnt0();
+        scales_to_float(r0);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) convert_one(r0, 0, c, c0);
+
+        // Step s, its raw fragments in `cur` and group 0 already converted in c0:
+        // once this wave's reads and the loads step s+1 needs are done, a barrier
+        // publishes step s+1 (B step s+1 issued first in step s-2, A stage
+        // (s+1)/2 and its scales completed in step s-3: at most 16 later loads
+        // may remain) and certifies that every wave is done reading step s.
+        // Then 64 MFMAs in four groups; after MFMA k = 16g + m: direct load k/6
+        // when k%6 == 2, read (g, m) of step s+1 (group g's raw fragments, and
+        // the scales in group 0), and every other MFMA one conversion for the
+        // next group (group 0 of step s+1 during group 3, once its reads and
+        // scales are in).  sched_barrier(0) pins the interleaving.
+        auto body = [&](int s, Raw& cur, Raw& nxt) {
+            wait_lgkmcnt0();
+            wait_vmcnt<16>();
+            barrier_no_fence();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                Conv& cv = (g & 1) ? c1 : c0;
+                Conv& cn = (g & 1) ? c0 : c1;
+                if (g == 3) {
+                    wait_lgkmcnt0();
+                    scales_to_float(nxt);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int k = 16 * g + m;
+                    mfma_one(cv, m);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (k % 6 == 2 && k / 6 < LOADS_PER_STEP) dma_step(s, k / 6);
+                    read_one(s + 1, g, m, nxt);
+                    if (m & 1) {
+                        if (g < 3) convert_one(cur, g + 1, m >> 1, cn);
+                        else convert_one(nxt, 0, m >> 1, cn);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        for (int s = 0; s < ksteps; s += 2) {
+            body(s, r0, r1);
+            body(s + 1, r1, r0);
         }
-
-        store_wave_tile<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc);
+        // The rings become the output staging area: every wave must be done
+        // reading them and every direct load (the empty ones past the range
+        // included) must have landed.
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier_no_fence();
+        store_wave_tile_staged<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        // The next item's direct loads overwrite the staging areas.
+        barrier_no_fence();
     }
 }
 
