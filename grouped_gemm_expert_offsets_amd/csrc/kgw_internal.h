@@ -6,8 +6,9 @@
 
 namespace kgw {
 
-// Largest expert count whose clamped offsets fit the kernels' LDS table.
-constexpr int kMaxExperts = 4096;
+// Largest expert count the library accepts (the kernels read each expert's
+// token range with scalar loads of the offsets; nothing is sized by it).
+constexpr int kMaxExperts = 65536;
 
 struct GroupedParams {
     const void* A;          // (hidden, tokens_sum), token axis contiguous

@@ -104,7 +104,7 @@ def test_bf16_argument_errors(lib):
     assert call_bf16(lib, out=FAKE + 4) == kgw.KGW_ERROR_MISALIGNED
     assert call_bf16(lib, N=500) == kgw.KGW_ERROR_MISALIGNED
     assert call_bf16(lib, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
-    assert call_bf16(lib, E=5000) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_bf16(lib, E=65537) == kgw.KGW_ERROR_UNSUPPORTED
 
 
 def test_fp8_argument_errors(lib):

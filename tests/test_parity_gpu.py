@@ -163,6 +163,37 @@ def test_malformed_offsets_stay_in_bounds():
     assert np.array_equal(to_f64(out[0]), W[0])
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_more_experts_than_4096(kind):
+    # 5000 experts, four with tokens (two past index 4096): the item list spans all of them,
+    # the non-empty ones are bit-exact on integer inputs and every empty one is +0.0.
+    E, hidden, n = 5000, 256, 64
+    counts = [0] * E
+    for e, c in ((0, 256), (1234, 512), (4097, 256), (4999, 768)):
+        counts[e] = c
+    wl = workloads.make_operands(counts, hidden, n, kind, torch.float32, False, seed=51, device=DEV,
+                                 integer_range=4)
+    out = nan_filled((E, hidden, n), torch.float32)
+    if kind == "bf16":
+        run_bf16(wl, out=out)
+    else:
+        run_fp8(wl, out=out)
+    ne = [e for e, c in enumerate(counts) if c]
+    mask = torch.ones(E, dtype=torch.bool, device=DEV)
+    mask[torch.tensor(ne, device=DEV)] = False
+    z = out[mask]
+    assert torch.count_nonzero(z).item() == 0 and not torch.signbit(z).any().item()
+    del z
+    rows = np.arange(hidden)
+    off = wl.offsets.cpu()
+    for e in ne:
+        if kind == "bf16":
+            ref = oracle.wgrad_rows_bf16(wl.A.cpu(), wl.B.cpu(), off, e, rows)
+        else:
+            ref = oracle.wgrad_rows_fp8(wl.A.cpu(), wl.sfa.cpu(), wl.B.cpu(), wl.sfb.cpu(), off, e, rows)
+        assert np.array_equal(to_f64(out[e]), ref), f"expert {e}"
+
+
 # ----------------------------------------------------------------------------
 # fp8 block-scaled path
 # ----------------------------------------------------------------------------
