@@ -100,6 +100,19 @@ def _stream_ptr(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _workspace(E: int, hidden: int, n: int, T: int, fp8: bool, device, stream, split_k: bool):
+    """Device workspace for the call (None when it runs in one pass or split_k is False)."""
+    if not split_k:
+        return None, 0
+    nbytes = kgw_workspace_bytes(E, hidden, n, T, fp8)
+    if nbytes == 0:
+        return None, 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)   # keep it alive for the launch stream's pending work
+    return ws, nbytes
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -135,10 +148,12 @@ def _check_offsets(offsets: torch.Tensor, device):
 
 def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out: Optional[torch.Tensor] = None,
                    *, out_dtype: torch.dtype = torch.float32, accumulate: bool = False, validate: bool = False,
-                   stream=None) -> torch.Tensor:
+                   stream=None, split_k: bool = True) -> torch.Tensor:
     """bf16 A (hidden, tokens_sum) token-contiguous, B (tokens_sum, n) row-major -> out (E, hidden, n).
 
-    validate=True first checks the offsets on the host (one synchronising copy).
+    validate=True first checks the offsets on the host (one synchronising copy).  The
+    workspace kgw_workspace_bytes asks for is allocated here; split_k=False passes none
+    (one pass).
     """
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise ValueError("kgw_wgrad_bf16 takes bfloat16 A and B")
@@ -159,29 +174,31 @@ def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out:
     out = _prepare_out(out, E, hidden, n, out_dtype, accumulate, device)
     if validate:
         kgw_validate_offsets(offsets, T, BF16_TOKEN_ALIGN, stream=stream)
+    ws, ws_bytes = _workspace(E, hidden, n, T, False, device, stream, split_k)
     st = load_library().kgw_wgrad_bf16(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
-                                       int(bool(accumulate)), None, 0, _stream_ptr(stream))
+                                       int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, "kgw_wgrad_bf16")
     return out
 
 
 def kgw_wgrad_fp8(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
                   out: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.bfloat16,
-                  accumulate: bool = False, validate: bool = False, stream=None) -> torch.Tensor:
+                  accumulate: bool = False, validate: bool = False, stream=None, split_k: bool = True) -> torch.Tensor:
     """e4m3 A (hidden, T) with UE8M0 sfa (T/128, hidden); e4m3 B (T, n) with sfb (T/128, n)."""
-    return _fp8_call("kgw_wgrad_fp8", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream)
+    return _fp8_call("kgw_wgrad_fp8", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream,
+                     split_k)
 
 
 def kgw_wgrad_fp8_native(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor,
                          offsets: torch.Tensor, out: Optional[torch.Tensor] = None, *,
                          out_dtype: torch.dtype = torch.bfloat16, accumulate: bool = False, validate: bool = False,
-                         stream=None) -> torch.Tensor:
+                         stream=None, split_k: bool = True) -> torch.Tensor:
     """kgw_wgrad_fp8 on the native scaled fp8 MFMA (faster, ~13-bit in-group alignment; see include/kgw.h)."""
     return _fp8_call("kgw_wgrad_fp8_native", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate,
-                     stream)
+                     stream, split_k)
 
 
-def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream):
+def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream, split_k):
     fp8_types = (torch.uint8, torch.float8_e4m3fn)
     if A.dtype not in fp8_types or B.dtype not in fp8_types:
         raise ValueError(f"{name} takes e4m3fn (or raw uint8) A and B")
@@ -210,8 +227,9 @@ def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validat
     if validate:
         kgw_validate_offsets(offsets, T, FP8_TOKEN_ALIGN, stream=stream)
     fn = getattr(load_library(), name)
+    ws, ws_bytes = _workspace(E, hidden, n, T, True, device, stream, split_k)
     st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
-            int(bool(accumulate)), None, 0, _stream_ptr(stream))
+            int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, name)
     return out
 

@@ -106,8 +106,14 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     const int slot = xcd_slot(blockIdx.x, G, p.num_xcds);
 
     for (int item = slot; item < p.num_items; item += G) {
-        const int e = item / TT;
-        const int local = item - e * TT;
+        // Items run expert-major, then K chunk (one unless the K range is split),
+        // then tile; chunk c of expert e writes output slab c*E + e (the split-K
+        // partials; slab e itself when unsplit).
+        const int ec = item / TT;
+        const int local = item - ec * TT;
+        const int e = ec / p.split;
+        const int c = ec - e * p.split;
+        const int eo = c * p.num_experts + e;
         int tm, tn;
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
@@ -117,13 +123,20 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
         const int64_t raw_end = p.offsets[e];
         int32_t begin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
-        const int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        if (p.split > 1) {
+            // chunk c of the range: split_unit-aligned pieces of ceil(count / split)
+            const int32_t len = ((end - begin + p.split - 1) / p.split + kSplitUnit - 1) & ~(kSplitUnit - 1);
+            const int32_t cb = (int32_t)min<int64_t>(end, (int64_t)begin + (int64_t)c * len);
+            end = (int32_t)min<int64_t>(end, (int64_t)cb + len);
+            begin = cb;
+        }
         // The loop below takes K steps in pairs: a range is used in whole
         // 64-token units (every well-formed count is a multiple of 256).
         begin &= ~(2 * BK - 1);
         const int ksteps = ((end - begin) / (2 * BK)) * 2;
         if (ksteps == 0) {
-            if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, e, m0, n0, tid);
+            if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, eo, m0, n0, tid);
             continue;
         }
 
@@ -279,7 +292,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
-        store_wave_tile_staged<OUT_BF16>(p, e, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        store_wave_tile_staged<OUT_BF16>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         // The next item's direct loads overwrite the staging areas.
         barrier_no_fence();
     }

@@ -70,9 +70,43 @@ kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, 
 
 enum class Kernel { kBf16, kFp8, kFp8Native };
 
+// Split-K: cut every expert's token range into `split` chunks when the output
+// tiles alone would leave most CUs idle (few experts, small hidden x n) and the
+// experts hold enough tokens for each chunk to stay busy.  The partials go to
+// the workspace as fp32 slabs shaped like the output.
+constexpr int64_t kMaxSplit = 16;
+constexpr int kDefaultCus = 256;                     // MI355X, when no device is visible
+constexpr int64_t kMinChunkTokens = 1024;            // average tokens per chunk
+constexpr size_t kMaxSplitWorkspace = (size_t)1 << 30;
+
+struct SplitPlan {
+    int32_t split = 1;
+    size_t bytes = 0;
+};
+
+SplitPlan split_plan(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, bool fp8, int num_cus) {
+    SplitPlan plan;
+    if (num_experts < 1 || hidden <= 0 || n <= 0 || tokens_sum <= 0 || num_cus <= 0) return plan;
+    const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
+    const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
+    const int64_t items = ((hidden + bm - 1) / bm) * ((n + bn - 1) / bn) * num_experts;
+    if (2 * items > num_cus) return plan;
+    int64_t s = num_cus / items;
+    if (s > kMaxSplit) s = kMaxSplit;
+    const int64_t by_tokens = tokens_sum / ((int64_t)num_experts * kMinChunkTokens);
+    if (s > by_tokens) s = by_tokens;
+    if (s < 2) return plan;
+    const size_t bytes = (size_t)s * (size_t)num_experts * (size_t)hidden * (size_t)n * sizeof(float);
+    if (bytes > kMaxSplitWorkspace) return plan;
+    plan.split = (int32_t)s;
+    plan.bytes = bytes;
+    return plan;
+}
+
 kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
                  const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
-                 int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate, void* stream) {
+                 int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate, void* workspace,
+                 size_t workspace_bytes, void* stream) {
     const bool fp8 = kernel != Kernel::kBf16;
     const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
     const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
@@ -106,14 +140,31 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     p.num_items = p.tiles_m * p.tiles_n * num_experts;
     p.accumulate = accumulate;
     p.num_xcds = d.num_xcds;
+    p.split = 1;
+    bool out_bf16 = out_dtype == KGW_OUT_BF16;
+
+    // Split-K when planned and the caller's workspace holds the partials;
+    // otherwise one pass (same result up to the order of the fp32 additions).
+    const SplitPlan plan = split_plan(num_experts, hidden, n, tokens_sum, fp8, d.num_cus);
+    const bool split = plan.split > 1 && workspace && workspace_bytes >= plan.bytes && aligned16(workspace);
+    if (split) {
+        p.split = plan.split;
+        p.num_items *= plan.split;
+        p.out = workspace;
+        p.accumulate = 0;
+        out_bf16 = false;
+    }
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
-    const bool out_bf16 = out_dtype == KGW_OUT_BF16;
     hipError_t err;
     switch (kernel) {
         case Kernel::kBf16: err = kgw::launch_wgrad_bf16(p, out_bf16, grid, (hipStream_t)stream); break;
         case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_bf16, grid, (hipStream_t)stream); break;
         default: err = kgw::launch_wgrad_fp8_native(p, out_bf16, grid, (hipStream_t)stream); break;
     }
+    if (err == hipSuccess && split)
+        err = kgw::launch_splitk_reduce((const float*)workspace, offsets, num_experts, hidden, n, tokens_sum,
+                                        plan.split, out, out_dtype == KGW_OUT_BF16, accumulate, d.num_cus,
+                                        (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 
@@ -124,39 +175,30 @@ extern "C" {
 kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
                             int64_t hidden, int64_t n, int64_t tokens_sum, void* out, int32_t out_dtype,
                             int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return run(Kernel::kBf16, A, nullptr, B, nullptr, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, stream);
+               accumulate, workspace, workspace_bytes, stream);
 }
 
 kgw_status_t kgw_wgrad_fp8(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
                            const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                            int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return run(Kernel::kFp8, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, stream);
+               accumulate, workspace, workspace_bytes, stream);
 }
 
 kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
                                   const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                                   int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return run(Kernel::kFp8Native, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, stream);
+               accumulate, workspace, workspace_bytes, stream);
 }
 
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int32_t fp8) {
-    (void)num_experts;
-    (void)hidden;
-    (void)n;
-    (void)tokens_sum;
-    (void)fp8;
-    return 0;
+    DeviceProps d;
+    const int cus = current_props(&d) == KGW_SUCCESS ? d.num_cus : kDefaultCus;
+    return split_plan(num_experts, hidden, n, tokens_sum, fp8 != 0, cus).bytes;
 }
 
 kgw_status_t kgw_validate_offsets_host(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,

@@ -88,8 +88,15 @@ typedef enum {
  *                  left untouched, bit for bit);
  *               0: out[e]  = Wgrad[e] (an empty expert is written with +0.0).
  *            Section "Operation" of the cuDNN page defines both modes.
- *   workspace, workspace_bytes  reserved; pass NULL and 0 (kgw_workspace_bytes
- *            returns 0 for every shape this version supports).
+ *   workspace, workspace_bytes  device scratch for split-K, owned by the caller:
+ *            at least kgw_workspace_bytes(...) bytes, 16-byte aligned, not
+ *            used by another call at the same time; it needs no initial
+ *            contents.  When that size is 0 (most shapes) or the workspace is
+ *            NULL or smaller, the call runs in one pass.  With it, each
+ *            expert's token range is cut into chunks whose fp32 partials land
+ *            in the workspace and a second pass sums them in chunk order before
+ *            applying the output mode once: the result differs from the
+ *            one-pass result only by the order of the fp32 additions.
  *
  * Sizes: 1 <= num_experts <= 65536; hidden, n >= 0; tokens_sum >= 0 and a
  * multiple of 256; n a multiple of 8; tokens_sum < 2^31 (int32 offsets).
@@ -147,9 +154,13 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call needs for this shape
- * (fp8 != 0 selects the fp8 entry point).  0 means none; this version always
- * returns 0.
+ * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape
+ * on the current device (fp8 != 0 selects the fp8 entry points; 256 compute
+ * units are assumed when no device is visible).  It is nonzero only when the
+ * output tiles alone would leave more than half of the compute units idle and
+ * the experts average at least 2048 tokens: then the call splits each expert's
+ * token range into 2..16 chunks (split-K) and needs
+ * chunks * num_experts * hidden * n * 4 bytes, at most 1 GiB.  0 means one pass.
  */
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                            int32_t fp8);

@@ -47,6 +47,23 @@ def test_workspace_is_zero(lib):
     assert kgw.kgw_workspace_bytes(32, 7168, 4096, 264320, fp8=True) == 0
 
 
+def test_workspace_bytes_split_k_plan():
+    # the five workload shapes have enough tiles to fill the chip: one pass, no workspace
+    import workloads
+    for name in workloads.CONFIG_NAMES:
+        spec = workloads.config_spec(name, 1)
+        assert kgw.kgw_workspace_bytes(len(spec["counts"]), spec["hidden"], spec["n"], sum(spec["counts"]),
+                                       fp8=spec["kind"] == "fp8") == 0, name
+    # few tiles and many tokens: split-K into chunks * E * hidden * n fp32 partials
+    # (256 CUs when no device is visible: 4 tiles -> up to 16 chunks, 8 by tokens/(E*1024))
+    assert kgw.kgw_workspace_bytes(2, 256, 512, 16384) == 8 * 2 * 256 * 512 * 4
+    assert kgw.kgw_workspace_bytes(2, 256, 512, 16384, fp8=True) == 8 * 2 * 256 * 512 * 4
+    # too few tokens per expert for two chunks of 1024 on average
+    assert kgw.kgw_workspace_bytes(2, 256, 512, 4096 - 256) == 0
+    # more than half of the CUs already have a tile
+    assert kgw.kgw_workspace_bytes(1, 256 * 16, 256 * 9, 1 << 20) == 0
+
+
 def validate(offsets, tokens_sum, align=256):
     return kgw.kgw_validate_offsets_host(offsets, tokens_sum, align)
 

@@ -195,6 +195,75 @@ def test_more_experts_than_4096(kind):
 
 
 # ----------------------------------------------------------------------------
+# split-K: few output tiles, many tokens -> chunked K with an fp32 workspace
+# ----------------------------------------------------------------------------
+SPLIT_COUNTS = [4096, 0, 8192, 256]     # E=4; partial M and N tiles below: 2 x 2 tiles per expert
+
+
+def _split_case(kind, out_dtype, accumulate, seed, integer_range=None):
+    wl = workloads.make_operands(SPLIT_COUNTS, 320, 384, kind, out_dtype, accumulate, seed=seed, device=DEV,
+                                 integer_range=integer_range)
+    assert kgw.kgw_workspace_bytes(4, 320, 384, sum(SPLIT_COUNTS), fp8=kind == "fp8") > 0, "case must split"
+    return wl
+
+
+def _run(wl, out, path, split_k):
+    if wl.kind == "bf16":
+        kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=wl.accumulate, split_k=split_k)
+    else:
+        fn = kgw.kgw_wgrad_fp8_native if path == "native" else kgw.kgw_wgrad_fp8
+        fn(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, accumulate=wl.accumulate, split_k=split_k)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_split_k_random(kind, out_dtype, accumulate):
+    wl = _split_case(kind, out_dtype, accumulate, seed=61)
+    out = wl.C0.clone() if accumulate else nan_filled((4, 320, 384), out_dtype)
+    _run(wl, out, "exact", True)
+    W = oracle_dense(wl)
+    ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
+    got = to_f64(out)
+    if accumulate:
+        assert torch.equal(out[1].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                           wl.C0[1].view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+    else:
+        assert np.all(got[1] == 0.0) and not np.any(np.signbit(got[1]))
+    if out_dtype == torch.float32:
+        assert_fp32_close(got, ref, f"split-K {kind} fp32")
+    else:
+        assert_bf16_close(got, ref, f"split-K {kind} bf16")
+
+
+@pytest.mark.parametrize("path", ["exact", "native"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_split_k_integer_bit_exact_and_same_as_one_pass(kind, path):
+    if kind == "bf16" and path == "native":
+        pytest.skip("native applies to fp8 only")
+    wl = _split_case(kind, torch.float32, False, seed=62, integer_range=4)
+    split = nan_filled((4, 320, 384), torch.float32)
+    _run(wl, split, path, True)
+    one = nan_filled((4, 320, 384), torch.float32)
+    _run(wl, one, path, False)
+    W = oracle_dense(wl)
+    assert np.array_equal(to_f64(split), W)
+    assert torch.equal(split, one)
+
+
+def test_split_k_native_random_within_its_bound():
+    wl = _split_case("fp8", torch.float32, False, seed=63)
+    out = nan_filled((4, 320, 384), torch.float32)
+    _run(wl, out, "native", True)
+    W = oracle_dense(wl)
+    got = to_f64(out)
+    for e in (0, 2, 3):
+        assert rel_frob(got[e], W[e]) <= NATIVE_FP8_REL_FROB
+    assert np.all(got[1] == 0.0)
+
+
+# ----------------------------------------------------------------------------
 # fp8 block-scaled path
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
