@@ -80,14 +80,15 @@ __device__ __forceinline__ void store_wave_tile(const GroupedParams& p, int e, i
 // private to the calling wave (16-byte aligned, free of other traffic).  The
 // MFMA layout gives each lane one row and four columns per register group, so
 // direct stores scatter 16 bytes over 32 rows per instruction; after a
-// transpose through LDS every store instruction writes two whole row segments
-// (2 x 512 B fp32, 2 x 256 B bf16), and accumulate mode reads the old values
-// the same way.  The accumulators go through LDS as fp32 in two passes of 64
-// rows (bf16 output is rounded once, after the optional add).  The LDS image
-// holds rows of 32 16-byte chunks with chunk c of row r at slot c ^ (r & 31),
-// so both the scattered writes and the row reads spread over all banks.  The
-// caller must keep other waves' LDS traffic out of `stage` until this returns
-// (its LDS reads are complete once its last store is issued).
+// transpose through LDS every store instruction writes whole row segments
+// (fp32: 2 rows x 512 B; bf16: 8 values per lane, 4 rows x 256 B), and
+// accumulate mode reads the old values the same way.  The accumulators go
+// through LDS as fp32 in two passes of 64 rows (bf16 output is rounded once,
+// after the optional add).  The LDS image holds rows of 32 16-byte chunks with
+// chunk c of row r at slot c ^ (r & 31), so both the scattered writes and the
+// row reads spread over all banks.  The caller must keep other waves' LDS
+// traffic out of `stage` until this returns (its LDS reads are complete once
+// its last store is issued).
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, int e, int64_t mb, int64_t nb,
                                                        int lane, const f32x16 (&acc)[4][4], lds_char* stage) {
@@ -111,26 +112,40 @@ __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, i
                     lds_store_16B(stage, (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)), __builtin_bit_cast(i32x4, w));
                 }
         }
-#pragma unroll 8
-        for (int q = 0; q < 32; ++q) {
-            const int r = 2 * q + (lane >> 5);
-            f32x4 v = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + ((c_read ^ (r & 31)) << 4))));
-            const int64_t m = mb + 64 * pass + r;
-            if (m >= H || nn >= N) continue;
-            const int64_t idx = ((int64_t)e * H + m) * N + nn;
-            if constexpr (OUT_BF16) {
-                i32x2* dst = (i32x2*)((char*)p.out + idx * 2);
+        if constexpr (OUT_BF16) {
+            // each lane: 8 consecutive columns (two chunks) -> one 16-byte store;
+            // an instruction writes four rows of 256 B
+            const int c2 = lane & 15;
+            const int64_t nn8 = nb + 8 * c2;
+#pragma unroll 4
+            for (int q = 0; q < 16; ++q) {
+                const int r = 4 * q + (lane >> 4);
+                const f32x4 v0 = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + (((2 * c2) ^ (r & 31)) << 4))));
+                const f32x4 v1 = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + (((2 * c2 + 1) ^ (r & 31)) << 4))));
+                const int64_t m = mb + 64 * pass + r;
+                if (m >= H || nn8 >= N) continue;
+                float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                i32x4* dst = (i32x4*)((char*)p.out + (((int64_t)e * H + m) * N + nn8) * 2);
                 if (p.accumulate) {
-                    const i32x2 old = *dst;
-                    v[0] += bf16_lo((uint32_t)old[0]);
-                    v[1] += bf16_hi((uint32_t)old[0]);
-                    v[2] += bf16_lo((uint32_t)old[1]);
-                    v[3] += bf16_hi((uint32_t)old[1]);
+                    const i32x4 old = *dst;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        v[2 * h] += bf16_lo((uint32_t)old[h]);
+                        v[2 * h + 1] += bf16_hi((uint32_t)old[h]);
+                    }
                 }
-                const i32x2 w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+                const i32x4 w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
+                                 (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
                 *dst = w;
-            } else {
-                f32x4* dst = (f32x4*)((char*)p.out + idx * 4);
+            }
+        } else {
+#pragma unroll 8
+            for (int q = 0; q < 32; ++q) {
+                const int r = 2 * q + (lane >> 5);
+                f32x4 v = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + ((c_read ^ (r & 31)) << 4))));
+                const int64_t m = mb + 64 * pass + r;
+                if (m >= H || nn >= N) continue;
+                f32x4* dst = (f32x4*)((char*)p.out + (((int64_t)e * H + m) * N + nn) * 4);
                 if (p.accumulate) v += *dst;
                 *dst = v;
             }
