@@ -66,6 +66,12 @@ def _load():
     lib.oracle_wgrad_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p]
     lib.oracle_wgrad_fp8.restype = ctypes.c_int
     lib.oracle_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
+    lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e8m0_for_amax.restype = ctypes.c_uint8
+    lib.oracle_e8m0_for_amax.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_fp8_tokens.restype = ctypes.c_int
+    lib.oracle_quantize_fp8_tokens.argtypes = [p, i64, i64, ctypes.c_int, p, p]
     _lib = lib
     return lib
 
@@ -190,6 +196,36 @@ def wgrad_fp8(A, sfa, B, sfb, offsets) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle: malformed offsets")
     return out
+
+
+def e4m3fn_encode(v: float) -> int:
+    """e4m3fn byte of v, round to nearest, ties to even (0x7F for NaN or beyond 448)."""
+    return int(_load().oracle_e4m3fn_encode(float(v)))
+
+
+def e8m0_for_amax(amax: float) -> int:
+    """Biased UE8M0 exponent of the smallest 2^k with amax <= 448 * 2^k, clamped to [1, 254]
+    (127 for 0, 255 for NaN/inf)."""
+    return int(_load().oracle_e8m0_for_amax(float(amax)))
+
+
+def quantize_fp8_tokens(x, token_axis: int):
+    """Quantise bf16 x (rows, cols) to e4m3fn with one UE8M0 scale per 128 tokens.
+
+    token_axis 1: tokens along the columns (A (hidden, tokens)), scales (cols/128, rows);
+    token_axis 0: tokens along the rows (B (tokens, n)), scales (rows/128, cols).
+    Returns (q uint8 in x's layout, s uint8).
+    """
+    xb = _u16(x)
+    rows, cols = xb.shape
+    tokens = cols if token_axis else rows
+    other = rows if token_axis else cols
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((tokens // 128, other), dtype=np.uint8)
+    rc = _load().oracle_quantize_fp8_tokens(_ptr(xb), rows, cols, int(token_axis), _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("the token length must be a multiple of 128")
+    return q, s
 
 
 def apply_output_mode(W: np.ndarray, accumulate: bool, C0: Optional[np.ndarray] = None) -> np.ndarray:

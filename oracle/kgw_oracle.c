@@ -162,3 +162,89 @@ int oracle_wgrad_fp8(const uint8_t* A, const uint8_t* sfa, const uint8_t* B, con
     free(rows);
     return rc;
 }
+
+/*
+ * Token-axis fp8 quantiser (llm-infra-atlas "05 Grouped GEMM", section 3: one
+ * power-of-two UE8M0 scale per 1x128 block; for the k-grouped weight gradient
+ * the blocks run along the token axis, section 5.2).  The pages leave the
+ * choice of the scale open; the reading used here takes, per block, the
+ * smallest power of two 2^k with amax <= 448 * 2^k (448 = largest e4m3fn),
+ * stores the biased exponent k + 127 clamped to [1, 254] (127 for an all-zero
+ * block, 255 = the E8M0 NaN code for a block holding a NaN or an infinity),
+ * and encodes every element as e4m3fn(x / 2^k), rounded to nearest, ties to
+ * even.  In a NaN/infinity block every element is the e4m3fn NaN 0x7F.
+ */
+
+/* e4m3fn encoding of v, round to nearest with ties to even, sign kept (also
+ * for zero); NaN and magnitudes that round above 448 give 0x7F. */
+uint8_t oracle_e4m3fn_encode(double v) {
+    if (isnan(v)) return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double mag = fabs(v);
+    if (mag == 0.0) return sign;
+    if (mag < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; a result of 8 quanta is the
+         * smallest normal 2^-6, whose code 0x08 continues the count */
+        double n = mag * 512.0;              /* exact: power-of-two scaling */
+        double m = nearbyint(n);             /* default rounding: nearest, ties to even */
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int ex;
+    frexp(mag, &ex);                         /* mag = f * 2^ex, f in [0.5, 1) */
+    int E = ex - 1;                          /* mag in [2^E, 2^(E+1)) */
+    double n = ldexp(mag, 3 - E);            /* in [8, 16), exact */
+    double m = nearbyint(n);
+    if (m == 16.0) {
+        m = 8.0;
+        E += 1;
+    }
+    const int field = E + 7;
+    if (field > 15 || (field == 15 && (int)m - 8 == 7)) return 0x7F;  /* beyond 448 */
+    return (uint8_t)(sign | (uint8_t)(field << 3) | (uint8_t)((int)m - 8));
+}
+
+/* Biased UE8M0 exponent for a block whose largest magnitude is amax. */
+uint8_t oracle_e8m0_for_amax(double amax) {
+    if (isnan(amax) || isinf(amax)) return 0xFF;
+    if (amax == 0.0) return 127;
+    int k = (int)ceil(log2(amax / 448.0));
+    while (amax > ldexp(448.0, k)) ++k;          /* exact comparisons settle log2's rounding */
+    while (amax <= ldexp(448.0, k - 1)) --k;
+    int e = k + 127;
+    if (e < 1) e = 1;
+    if (e > 254) e = 254;
+    return (uint8_t)e;
+}
+
+/* x: bf16 bits, (rows, cols) row-major.  token_axis 1: tokens run along the
+ * columns (A of the weight gradient, (hidden, tokens)), scales s are
+ * (cols/128, rows); token_axis 0: tokens run along the rows (B, (tokens, n)),
+ * scales (rows/128, cols).  q: e4m3fn bytes in x's layout.  Returns 0, or -1
+ * when the token length is not a multiple of 128. */
+int oracle_quantize_fp8_tokens(const uint16_t* x, int64_t rows, int64_t cols, int token_axis, uint8_t* q,
+                               uint8_t* s) {
+    const int64_t tokens = token_axis ? cols : rows;
+    const int64_t other = token_axis ? rows : cols;
+    if (tokens % 128 != 0) return -1;
+    const int64_t nblocks = tokens / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < other; ++o) {
+        for (int64_t b = 0; b < nblocks; ++b) {
+            double amax = 0.0;
+            int bad = 0;
+            for (int64_t t = 128 * b; t < 128 * b + 128; ++t) {
+                const int64_t idx = token_axis ? o * cols + t : t * cols + o;
+                const double v = oracle_bf16_value(x[idx]);
+                if (isnan(v) || isinf(v)) bad = 1;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            const uint8_t e = bad ? 0xFF : oracle_e8m0_for_amax(amax);
+            s[b * other + o] = e;
+            for (int64_t t = 128 * b; t < 128 * b + 128; ++t) {
+                const int64_t idx = token_axis ? o * cols + t : t * cols + o;
+                q[idx] = bad ? 0x7F : oracle_e4m3fn_encode(ldexp(oracle_bf16_value(x[idx]), 127 - (int)e));
+            }
+        }
+    }
+    return 0;
+}

@@ -278,3 +278,116 @@ def test_bf16_ulp_is_spacing(oracle_lib):
     bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
     nxt = (bits + 1).view(torch.bfloat16).double().numpy()
     np.testing.assert_array_equal(nxt - x, oracle.bf16_ulp(x))
+
+
+# ----------------------------------------------------------------------------
+# token-axis fp8 quantiser (llm-infra-atlas "05 Grouped GEMM", section 3: 1x128
+# blocks, UE8M0 scales; reading: smallest 2^k with amax <= 448 * 2^k, RNE)
+# ----------------------------------------------------------------------------
+def _e4m3_codes_positive():
+    """(code, value) of every finite non-negative e4m3fn code, increasing."""
+    out = []
+    for b in range(0x7F):               # 0x7F is NaN
+        out.append((b, oracle.e4m3fn_value(b)))
+    return out
+
+
+def test_e4m3fn_encode_inverts_the_decoder():
+    for b in range(256):
+        if b & 0x7F == 0x7F:
+            continue
+        v = oracle.e4m3fn_value(b)
+        assert oracle.e4m3fn_encode(v) == b, hex(b)
+
+
+def test_e4m3fn_encode_rounds_to_nearest_ties_to_even():
+    codes = _e4m3_codes_positive()
+    for (b0, v0), (b1, v1) in zip(codes, codes[1:]):
+        mid = (v0 + v1) / 2.0
+        even = b0 if (b0 & 1) == 0 else b1          # the code with the even last mantissa bit
+        assert oracle.e4m3fn_encode(mid) == even, (hex(b0), hex(b1))
+        assert oracle.e4m3fn_encode(-mid) == even | 0x80
+        eps = (v1 - v0) / 64.0
+        assert oracle.e4m3fn_encode(mid - eps) == b0
+        assert oracle.e4m3fn_encode(mid + eps) == b1
+    assert oracle.e4m3fn_encode(448.0) == 0x7E
+    assert oracle.e4m3fn_encode(float("nan")) == 0x7F
+    assert oracle.e4m3fn_encode(-0.0) == 0x80
+
+
+def test_e4m3fn_encode_matches_torch_float8_conversion():
+    # a library routine with the same rounding: torch's float32 -> float8_e4m3fn cast
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(20000, generator=g) * torch.exp2(torch.randint(-12, 9, (20000,), generator=g).float())
+    x = x.clamp(-448.0, 448.0)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3fn_encode(float(v)) for v in x.numpy()], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e8m0_for_amax_is_the_smallest_sufficient_power_of_two():
+    rng = np.random.default_rng(6)
+    amax = np.exp2(rng.uniform(-120, 120, 2000)) * rng.uniform(1, 2, 2000)
+    for a in amax:
+        e = oracle.e8m0_for_amax(float(a))
+        k = e - 127
+        assert a <= 448.0 * 2.0 ** k
+        if e > 1:                                      # minimal unless clamped at the bottom
+            assert a > 448.0 * 2.0 ** (k - 1)
+    assert oracle.e8m0_for_amax(448.0) == 127
+    assert oracle.e8m0_for_amax(np.nextafter(448.0, 1e9)) == 128
+    assert oracle.e8m0_for_amax(1.0) == 119            # 1 <= 448 * 2^-8 = 1.75
+    assert oracle.e8m0_for_amax(0.0) == 127
+    assert oracle.e8m0_for_amax(1e-45) == 1            # clamped
+    assert oracle.e8m0_for_amax(float("inf")) == 255
+    assert oracle.e8m0_for_amax(float("nan")) == 255
+
+
+@pytest.mark.parametrize("token_axis", [0, 1])
+def test_quantizer_matches_the_independent_generator_implementation(token_axis):
+    # workloads.quantize_token_blocks (torch float8 cast, float64 log2) is written separately
+    g = torch.Generator().manual_seed(7)
+    shape = (200, 384) if token_axis else (384, 200)
+    x = (torch.randn(shape, generator=g) * torch.exp2(torch.randint(-20, 20, (1, shape[1]), generator=g).float())
+         ).to(torch.bfloat16)
+    q_ref, s_ref = workloads.quantize_token_blocks(x, token_axis=token_axis)
+    q, s = oracle.quantize_fp8_tokens(x, token_axis)
+    assert np.array_equal(s, s_ref.numpy())
+    assert np.array_equal(q, q_ref.numpy())
+
+
+@pytest.mark.parametrize("token_axis", [0, 1])
+def test_quantizer_dequantised_values_are_within_half_an_e4m3_step(token_axis):
+    g = torch.Generator().manual_seed(8)
+    shape = (64, 256) if token_axis else (256, 64)
+    x = torch.randn(shape, generator=g).to(torch.bfloat16)
+    q, s = oracle.quantize_fp8_tokens(x, token_axis)
+    xs = x.float().numpy().astype(np.float64)
+    deq = np.vectorize(oracle.e4m3fn_value)(q)
+    scale = np.exp2(s.astype(np.float64) - 127)
+    scale_full = np.repeat(scale, 128, axis=0)            # (tokens, other)
+    if token_axis:
+        scale_full = scale_full.T
+    v = deq * scale_full
+    # within half a step of e4m3 at the element's own binade (3 mantissa bits), or of the
+    # subnormal step 2^-9 * scale
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(xs), 1e-300))) - 3), np.exp2(-9) * scale_full)
+    assert np.all(np.abs(v - xs) <= step / 2 + 1e-300)
+    # every block's largest element, scaled, lies in (224, 448], so after rounding in [224, 448]
+    tok_major = deq if not token_axis else deq.T                    # (tokens, other)
+    bmax = np.abs(tok_major).reshape(-1, 128, tok_major.shape[1]).max(axis=1)
+    assert np.all(bmax >= 224) and np.all(bmax <= 448)
+
+
+def test_quantizer_special_blocks():
+    x = torch.randn(256, 4).to(torch.bfloat16)
+    x[:128, 0] = 0.0                                      # all-zero block
+    x[130, 1] = float("nan")                              # NaN block
+    x[5, 2] = float("inf")                                # inf block
+    q, s = oracle.quantize_fp8_tokens(x, 0)
+    assert s[0, 0] == 127 and np.all(q[:128, 0] == 0)
+    assert s[1, 1] == 255 and np.all(q[128:, 1] == 0x7F)
+    assert s[0, 2] == 255 and np.all(q[:128, 2] == 0x7F)
+    assert s[1, 0] != 255 and s[0, 3] != 255
+    with pytest.raises(ValueError):
+        oracle.quantize_fp8_tokens(x[:200], 0)
