@@ -17,7 +17,8 @@ the rocprofv3 counter summary committed under profiles/ for this workload,
 and is null when the kernel sources changed after those counters were taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `secondary` reports the other workloads (the 32-expert skewed-accumulate,
-fp8 and many-small-expert configs, and the tiny one) with the same timing.
+fp8 and many-small-expert configs, and the tiny one) with the same timing,
+and the on-device fp8 quantiser on the fp8 workload's operand shapes.
 """
 from __future__ import annotations
 
@@ -135,6 +136,34 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
     res["hbm_gbps_algorithmic"] = res["algorithmic_bytes"] / (mean_launch * 1e-3) / 1e9
     res["frac_of_hbm_peak"] = res["hbm_gbps_algorithmic"] / PEAK_HBM_GBPS
     del wl, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_quantize(token_axis: int, steps: int, warmup: int):
+    """kgw_quantize_fp8 on the fp8 workload's bf16 operand shape (A: (hidden, tokens_sum),
+    token_axis 1; B: (tokens_sum, n), token_axis 0).  HBM-bound: 2 bytes read and 1 written per
+    element plus one scale byte per 128."""
+    import torch
+    import grouped_gemm_expert_offsets_amd as kgw
+    import workloads
+    spec = workloads.config_spec("fp8", 1)
+    T, H, N = sum(spec["counts"]), spec["hidden"], spec["n"]
+    shape = (H, T) if token_axis else (T, N)
+    g = torch.Generator(device="cuda").manual_seed(1)
+    x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_quantize_fp8(x, token_axis), steps, warmup)
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    nbytes = 3.0 * x.numel() + x.numel() / 128
+    res = {
+        "workload": f"quantize_fp8_{'A' if token_axis else 'B'} {shape[0]}x{shape[1]} bf16 (fp8 workload operand)",
+        "ms_per_step": ms_step,
+        "launch_ms_mean": mean_launch,
+        "algorithmic_bytes": nbytes,
+        "hbm_gbps_algorithmic": nbytes / (mean_launch * 1e-3) / 1e9,
+    }
+    res["frac_of_hbm_peak"] = res["hbm_gbps_algorithmic"] / PEAK_HBM_GBPS
+    del x
     torch.cuda.empty_cache()
     return res
 
@@ -284,6 +313,9 @@ def main():
             if name == args.workload:
                 continue
             r = run_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), native=native)
+            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+        for axis in (1, 0):
+            r = run_quantize(axis, max(5, args.steps // 2), max(2, args.warmup // 2))
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         line["secondary"] = sec
     if not args.no_cpu_baseline:

@@ -25,7 +25,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_workspace_bytes", "kgw_validate_offsets",
+    "kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_quantize_fp8", "kgw_workspace_bytes",
+    "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
     "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16",
@@ -48,8 +49,9 @@ library_path = os.path.join(_HERE, "libkgw.so")
 _lib = None
 
 # Every symbol include/kgw.h declares.
-EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_workspace_bytes", "kgw_validate_offsets_host",
-                    "kgw_validate_offsets", "kgw_status_string", "kgw_device_info")
+EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_quantize_fp8",
+                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
+                    "kgw_device_info")
 
 
 def load_library():
@@ -68,6 +70,8 @@ def load_library():
     lib.kgw_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_native.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_native.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_quantize_fp8.restype = ctypes.c_int
+    lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, p, p, p]
     lib.kgw_workspace_bytes.restype = sz
     lib.kgw_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.kgw_validate_offsets_host.restype = ctypes.c_int
@@ -232,6 +236,28 @@ def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validat
             int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, name)
     return out
+
+
+def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 x (rows, cols) -> (e4m3fn bytes as uint8 (rows, cols), UE8M0 scale bytes).
+
+    token_axis 1: tokens along the columns (A (hidden, tokens)), scales (cols/128, rows);
+    token_axis 0: tokens along the rows (B (tokens, n)), scales (rows/128, cols).
+    """
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("kgw_quantize_fp8 takes a contiguous 2-D bfloat16 tensor")
+    if token_axis not in (0, 1):
+        raise ValueError("token_axis must be 0 or 1")
+    rows, cols = x.shape
+    tokens, other = (cols, rows) if token_axis else (rows, cols)
+    if tokens % FP8_TOKEN_ALIGN != 0:
+        raise ValueError(f"the token length ({tokens}) must be a multiple of {FP8_TOKEN_ALIGN}")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((tokens // FP8_TOKEN_ALIGN, other), dtype=torch.uint8, device=x.device)
+    st = load_library().kgw_quantize_fp8(_ptr(x), rows, cols, int(token_axis), _ptr(q), _ptr(s),
+                                         _stream_ptr(stream))
+    _check(st, "kgw_quantize_fp8")
+    return q, s
 
 
 def kgw_workspace_bytes(num_experts: int, hidden: int, n: int, tokens_sum: int, fp8: bool = False) -> int:

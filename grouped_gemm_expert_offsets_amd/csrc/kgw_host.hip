@@ -195,6 +195,26 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
                accumulate, workspace, workspace_bytes, stream);
 }
 
+kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
+                              uint8_t* scales, void* stream) {
+    if (token_axis != 0 && token_axis != 1) return KGW_ERROR_INVALID_VALUE;
+    if (rows < 0 || cols < 0) return KGW_ERROR_INVALID_VALUE;
+    const int64_t tokens = token_axis ? cols : rows;
+    if (tokens % 128 != 0) return KGW_ERROR_INVALID_VALUE;
+    if (rows == 0 || cols == 0) return KGW_SUCCESS;
+    if (!x || !q || !scales) return KGW_ERROR_INVALID_VALUE;
+    if (cols % 8 != 0 || !aligned16(x) || !aligned16(q)) return KGW_ERROR_MISALIGNED;
+    if (!token_axis && ((uintptr_t)scales & 7u)) return KGW_ERROR_MISALIGNED;
+    if (rows * cols >= ((int64_t)1 << 40)) return KGW_ERROR_UNSUPPORTED;
+    DeviceProps d;
+    kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    const hipError_t err = kgw::launch_quantize_fp8(x, rows, cols, token_axis, q, scales, d.num_cus,
+                                                    (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int32_t fp8) {
     DeviceProps d;
     const int cus = current_props(&d) == KGW_SUCCESS ? d.num_cus : kDefaultCus;

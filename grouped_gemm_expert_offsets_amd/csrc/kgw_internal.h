@@ -44,6 +44,8 @@ hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t
                                 int64_t n, int64_t tokens_sum, int32_t split, void* out, bool out_bf16,
                                 int32_t accumulate, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
+                               uint8_t* s, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8_native(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
 
 }  // namespace kgw

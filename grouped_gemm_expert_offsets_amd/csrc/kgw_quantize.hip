@@ -1,0 +1,205 @@
+// Token-axis fp8 quantiser (gfx950): bf16 -> OCP e4m3fn bytes plus one UE8M0
+// scale byte per 128 tokens, the operand format the fp8 weight-gradient
+// kernels consume (llm-infra-atlas "05 Grouped GEMM", section 3: 1x128
+// blocks, power-of-two UE8M0 scales; for the k-grouped weight gradient the
+// blocks run along the contracted token axis, section 5.2).
+//
+// Per block: amax = the largest |x|; the scale is the smallest power of two
+// 2^k with amax <= 448 * 2^k (448 = largest e4m3fn), stored as the biased
+// exponent k + 127 clamped to [1, 254] (127 for an all-zero block); every
+// element becomes e4m3fn(x * 2^-k), rounded to nearest, ties to even
+// (v_cvt_pk_fp8_f32; x * 2^-k is exact in fp32).  A block holding a NaN or an
+// infinity gets scale byte 0xFF (the E8M0 NaN) and NaN bytes 0x7F.
+//
+// Roofline: HBM.  Per element 2 bytes read and 1 written, plus one scale byte
+// per 128 elements; both layouts read every input byte once:
+//   - tokens contiguous (A of the weight gradient, (hidden, tokens)): a lane
+//     holds 8 tokens (16-byte load), 16 lanes one 128-token block; the block
+//     maximum is reduced across the 16 lanes; 8-byte stores;
+//   - tokens along the rows (B, (tokens, n)): a wave holds a 128-row x 64-column
+//     block in registers (lane: 8 columns of 16 rows, each load 8 rows x 128
+//     bytes), reduces each column over its 16 rows and then across the 8 lanes
+//     that share the column, and stores from registers.
+#include "kgw_device.h"
+#include "kgw_internal.h"
+
+namespace kgw {
+namespace {
+
+constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
+
+// Biased UE8M0 exponent of the smallest 2^k with amax <= 448 * 2^k, from the
+// fp32 bits of amax (amax = 1.f * 2^E; 448 = 1.75 * 2^8: k = E - 8 when
+// 1.f <= 1.75, else E - 7), clamped to [1, 254]; 127 for zero.
+__device__ __forceinline__ uint32_t e8m0_for_amax(float amax) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+    if (bits == 0u) return 127u;
+    const int E = (int)(bits >> 23) - 127;               // subnormal amax gives -127: clamps to 1
+    const int k = E - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    const int e = k + 127;
+    return (uint32_t)(e < 1 ? 1 : (e > 254 ? 254 : e));
+}
+
+// 2^(127 - e) as an fp32, for e in [1, 254] (normal for every e a finite bf16
+// block can produce; e = 254 would need amax above the bf16 range).
+__device__ __forceinline__ float inv_scale(uint32_t e) {
+    const uint32_t field = 254u - e;
+    return __builtin_bit_cast(float, field == 0u ? 0x00400000u : (field << 23));
+}
+
+__device__ __forceinline__ bool not_finite(float v) {
+    return (__builtin_bit_cast(uint32_t, v) & 0x7F800000u) == 0x7F800000u;
+}
+
+// Four fp32 -> four e4m3fn bytes (little-endian order).
+__device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+}
+
+// tokens along the columns: x (rows, cols), q same layout, s (cols/128, rows).
+__global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* x, int64_t rows, int64_t cols,
+                                                          uint8_t* q, uint8_t* s) {
+    const int lane = threadIdx.x & 63;
+    const int64_t chunks = (cols + 511) / 512;           // 512 tokens (four blocks) per wave step
+    const int64_t units = rows * chunks;
+    const int64_t wave0 = (int64_t)blockIdx.x * NWAVE + (threadIdx.x >> 6);
+    for (int64_t u = wave0; u < units; u += (int64_t)gridDim.x * NWAVE) {
+        const int64_t r = u / chunks;
+        const int64_t c = u - r * chunks;
+        const int64_t t0 = c * 512 + 8 * lane;          // this lane's first token
+        const bool active = t0 < cols;                   // cols is a multiple of 128
+        f32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+        if (active) {
+            const i32x4 raw = *(const i32x4*)(x + r * cols + t0);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t w = (uint32_t)raw[h];
+                const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+                if (h < 2) { lo[2 * h] = v0; lo[2 * h + 1] = v1; }
+                else { hi[2 * h - 4] = v0; hi[2 * h - 3] = v1; }
+            }
+        }
+        float amax = 0.0f;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
+            bad |= not_finite(lo[i]) | not_finite(hi[i]);
+        }
+        // reduce over the 16 lanes of the block (xor 1, 2, 4, 8 stays in the group)
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+            amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+            bad |= __shfl_xor((int)bad, m, 64) != 0;
+        }
+        if (!active) continue;
+        const uint32_t e = bad ? 255u : e8m0_for_amax(amax);
+        i32x2 out;
+        if (bad) {
+            out[0] = 0x7F7F7F7F;
+            out[1] = 0x7F7F7F7F;
+        } else {
+            const float f = inv_scale(e);
+            out[0] = cvt4(lo[0] * f, lo[1] * f, lo[2] * f, lo[3] * f);
+            out[1] = cvt4(hi[0] * f, hi[1] * f, hi[2] * f, hi[3] * f);
+        }
+        *(i32x2*)(q + r * cols + t0) = out;
+        if ((lane & 15) == 0) s[(t0 / 128) * rows + r] = (uint8_t)e;
+    }
+}
+
+// tokens along the rows: x (rows, cols), q same layout, s (rows/128, cols).
+// Lane l: columns 8*(l & 7) .. +7 of the wave's 64, rows (l >> 3) + 8*i, i < 16.
+__global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* x, int64_t rows, int64_t cols,
+                                                          uint8_t* q, uint8_t* s) {
+    const int lane = threadIdx.x & 63;
+    const int64_t cchunks = (cols + 63) / 64;
+    const int64_t units = (rows / 128) * cchunks;
+    const int64_t wave0 = (int64_t)blockIdx.x * NWAVE + (threadIdx.x >> 6);
+    const int rsub = lane >> 3;
+    for (int64_t u = wave0; u < units; u += (int64_t)gridDim.x * NWAVE) {
+        const int64_t b = u / cchunks;
+        const int64_t n0 = (u - b * cchunks) * 64 + 8 * (lane & 7);
+        const bool active = n0 < cols;                   // cols is a multiple of 8
+        i32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t row = 128 * b + rsub + 8 * i;
+            if (active) v[i] = *(const i32x4*)(x + row * cols + n0);
+            else v[i] = i32x4{0, 0, 0, 0};
+        }
+        // per column (8 per lane): max over this lane's 16 rows, then over the
+        // 8 lanes with the same column group (xor 8, 16, 32)
+        float amax[8];
+        int bad = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax[j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float a = bf16_lo((uint32_t)v[i][h]), c = bf16_hi((uint32_t)v[i][h]);
+                amax[2 * h] = fmaxf(amax[2 * h], fabsf(a));
+                amax[2 * h + 1] = fmaxf(amax[2 * h + 1], fabsf(c));
+                bad |= (not_finite(a) ? 1 : 0) << (2 * h);
+                bad |= (not_finite(c) ? 1 : 0) << (2 * h + 1);
+            }
+#pragma unroll
+        for (int m = 8; m < 64; m <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], m, 64));
+            bad |= __shfl_xor(bad, m, 64);
+        }
+        if (!active) continue;
+        uint32_t e[8];
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            e[j] = ((bad >> j) & 1) ? 255u : e8m0_for_amax(amax[j]);
+            f[j] = inv_scale(e[j] == 255u ? 127u : e[j]);
+        }
+        if (rsub == 0) {
+            const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
+                              (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
+            *(i32x2*)(s + b * cols + n0) = sw;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float val[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                val[2 * h] = bf16_lo((uint32_t)v[i][h]) * f[2 * h];
+                val[2 * h + 1] = bf16_hi((uint32_t)v[i][h]) * f[2 * h + 1];
+            }
+            i32x2 out = {cvt4(val[0], val[1], val[2], val[3]), cvt4(val[4], val[5], val[6], val[7])};
+            // NaN/infinity columns: every byte of the block is NaN
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if ((bad >> j) & 1) out[j >> 2] = (out[j >> 2] & ~(0xFF << (8 * (j & 3)))) | (0x7F << (8 * (j & 3)));
+            const int64_t row = 128 * b + rsub + 8 * i;
+            *(i32x2*)(q + row * cols + n0) = out;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
+                               uint8_t* s, int num_cus, hipStream_t stream) {
+    const int64_t units = token_axis ? rows * ((cols + 511) / 512) : (rows / 128) * ((cols + 63) / 64);
+    int64_t blocks = (units + NWAVE - 1) / NWAVE;
+    const int64_t cap = (int64_t)num_cus * 16;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    if (token_axis)
+        hipLaunchKernelGGL(quantize_tokens_cols, dim3((unsigned)blocks), dim3(NT), 0, stream, (const uint16_t*)x,
+                           rows, cols, (uint8_t*)q, s);
+    else
+        hipLaunchKernelGGL(quantize_tokens_rows, dim3((unsigned)blocks), dim3(NT), 0, stream, (const uint16_t*)x,
+                           rows, cols, (uint8_t*)q, s);
+    return hipGetLastError();
+}
+
+}  // namespace kgw

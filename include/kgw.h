@@ -154,6 +154,37 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kgw_quantize_fp8 -- produce the fp8 operands of kgw_wgrad_fp8 from bf16 on the
+ * device: OCP e4m3fn bytes plus one UE8M0 scale byte per 128 tokens, the
+ * blocks running along the token axis (llm-infra-atlas "05 Grouped GEMM",
+ * section 3: 1x128 blocks with power-of-two UE8M0 scales, fp8 consumed
+ * directly; section 5.2: the weight gradient contracts over tokens).  The pages
+ * do not fix how the scale is chosen; here, per block, the scale is the
+ * smallest power of two 2^k with amax <= 448 * 2^k (amax = largest |x| of the
+ * block, 448 = largest e4m3fn), its byte k + 127 clamped to [1, 254] (127 for
+ * an all-zero block), and every element is e4m3fn(x / 2^k) rounded to
+ * nearest, ties to even.  A block holding a NaN or an infinity gets scale byte
+ * 0xFF (NaN) and NaN elements (0x7F).
+ *
+ *   x       bf16 (rows, cols), row-major, device, 16-byte aligned.
+ *   token_axis  1: tokens along the columns -- A of the weight gradient,
+ *           (hidden, tokens_sum); scales (cols/128, rows).
+ *           0: tokens along the rows -- B, (tokens_sum, n); scales
+ *           (rows/128, cols).
+ *   q       uint8 (rows, cols), same layout as x, device, 16-byte aligned.
+ *   scales  uint8 as above (mn-major, the layout kgw_wgrad_fp8 takes), device;
+ *           8-byte aligned when token_axis == 0.
+ *   stream  hipStream_t (NULL = default stream); asynchronous.
+ *
+ * The token length (cols for token_axis 1, rows for 0) must be a multiple of
+ * 128 (else KGW_ERROR_INVALID_VALUE) and cols a multiple of 8
+ * (KGW_ERROR_MISALIGNED).  rows or cols == 0 does nothing.  Every output byte
+ * is a function of x alone: results are bit-for-bit reproducible.
+ */
+kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
+                              uint8_t* scales, void* stream);
+
+/*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape
  * on the current device (fp8 != 0 selects the fp8 entry points; 256 compute
  * units are assumed when no device is visible).  It is nonzero only when the
