@@ -14,8 +14,8 @@
 // Roofline: HBM.  Per element 2 bytes read and 1 written, plus one scale byte
 // per 128 elements; both layouts read every input byte once:
 //   - tokens contiguous (A of the weight gradient, (hidden, tokens)): a lane
-//     holds 8 tokens (16-byte load), 16 lanes one 128-token block; the block
-//     maximum is reduced across the 16 lanes; 8-byte stores;
+//     holds 16 tokens (two 16-byte loads), 8 lanes one 128-token block; the
+//     block maximum is reduced across the 8 lanes; 16-byte stores;
 //   - tokens along the rows (B, (tokens, n)): a wave holds a 128-row x 64-column
 //     block in registers (lane: 8 columns of 16 rows, each load 8 rows x 128
 //     bytes), reduces each column over its 16 rows and then across the 8 lanes
@@ -59,54 +59,58 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
 }
 
 // tokens along the columns: x (rows, cols), q same layout, s (cols/128, rows).
+// Lane l: tokens 16l .. 16l+15 of the wave's 1024 (two 16-byte loads, one
+// 16-byte store); 8 lanes make one 128-token block.
 __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* x, int64_t rows, int64_t cols,
                                                           uint8_t* q, uint8_t* s) {
     const int lane = threadIdx.x & 63;
-    const int64_t chunks = (cols + 511) / 512;           // 512 tokens (four blocks) per wave step
+    const int64_t chunks = (cols + 1023) / 1024;         // 1024 tokens (eight blocks) per wave step
     const int64_t units = rows * chunks;
     const int64_t wave0 = (int64_t)blockIdx.x * NWAVE + (threadIdx.x >> 6);
     for (int64_t u = wave0; u < units; u += (int64_t)gridDim.x * NWAVE) {
         const int64_t r = u / chunks;
         const int64_t c = u - r * chunks;
-        const int64_t t0 = c * 512 + 8 * lane;          // this lane's first token
+        const int64_t t0 = c * 1024 + 16 * lane;        // this lane's first token
         const bool active = t0 < cols;                   // cols is a multiple of 128
-        f32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
         if (active) {
-            const i32x4 raw = *(const i32x4*)(x + r * cols + t0);
+            const i32x4 r0 = *(const i32x4*)(x + r * cols + t0);
+            const i32x4 r1 = *(const i32x4*)(x + r * cols + t0 + 8);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const uint32_t w = (uint32_t)raw[h];
-                const float v0 = bf16_lo(w), v1 = bf16_hi(w);
-                if (h < 2) { lo[2 * h] = v0; lo[2 * h + 1] = v1; }
-                else { hi[2 * h - 4] = v0; hi[2 * h - 3] = v1; }
+                v[2 * h] = bf16_lo((uint32_t)r0[h]);
+                v[2 * h + 1] = bf16_hi((uint32_t)r0[h]);
+                v[8 + 2 * h] = bf16_lo((uint32_t)r1[h]);
+                v[8 + 2 * h + 1] = bf16_hi((uint32_t)r1[h]);
             }
         }
         float amax = 0.0f;
-        bool bad = false;
+        int bad = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
-            bad |= not_finite(lo[i]) | not_finite(hi[i]);
+        for (int i = 0; i < 16; ++i) {
+            amax = fmaxf(amax, fabsf(v[i]));
+            bad |= not_finite(v[i]) ? 1 : 0;
         }
-        // reduce over the 16 lanes of the block (xor 1, 2, 4, 8 stays in the group)
+        // reduce over the 8 lanes of the block (xor 1, 2, 4 stays in the group)
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
+        for (int m = 1; m < 8; m <<= 1) {
             amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-            bad |= __shfl_xor((int)bad, m, 64) != 0;
+            bad |= __shfl_xor(bad, m, 64);
         }
         if (!active) continue;
         const uint32_t e = bad ? 255u : e8m0_for_amax(amax);
-        i32x2 out;
+        i32x4 out;
         if (bad) {
-            out[0] = 0x7F7F7F7F;
-            out[1] = 0x7F7F7F7F;
+            out = i32x4{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
         } else {
             const float f = inv_scale(e);
-            out[0] = cvt4(lo[0] * f, lo[1] * f, lo[2] * f, lo[3] * f);
-            out[1] = cvt4(hi[0] * f, hi[1] * f, hi[2] * f, hi[3] * f);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) out[h] = cvt4(v[4 * h] * f, v[4 * h + 1] * f, v[4 * h + 2] * f, v[4 * h + 3] * f);
         }
-        *(i32x2*)(q + r * cols + t0) = out;
-        if ((lane & 15) == 0) s[(t0 / 128) * rows + r] = (uint8_t)e;
+        *(i32x4*)(q + r * cols + t0) = out;
+        if ((lane & 7) == 0) s[(t0 / 128) * rows + r] = (uint8_t)e;
     }
 }
 
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* x, in
 
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
                                uint8_t* s, int num_cus, hipStream_t stream) {
-    const int64_t units = token_axis ? rows * ((cols + 511) / 512) : (rows / 128) * ((cols + 63) / 64);
+    const int64_t units = token_axis ? rows * ((cols + 1023) / 1024) : (rows / 128) * ((cols + 63) / 64);
     int64_t blocks = (units + NWAVE - 1) / NWAVE;
     const int64_t cap = (int64_t)num_cus * 16;
     if (blocks > cap) blocks = cap;
