@@ -29,7 +29,7 @@ __all__ = [
     "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
-    "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16",
+    "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16", "KGW_OUT_FP16",
     "BF16_TOKEN_ALIGN", "FP8_TOKEN_ALIGN", "library_path", "load_library",
 ]
 
@@ -41,6 +41,7 @@ KGW_ERROR_UNSUPPORTED = 4
 KGW_ERROR_DEVICE = 5
 KGW_OUT_FP32 = 0
 KGW_OUT_BF16 = 1
+KGW_OUT_FP16 = 2
 BF16_TOKEN_ALIGN = 256
 FP8_TOKEN_ALIGN = 128
 
@@ -126,7 +127,9 @@ def _out_code(dtype: torch.dtype) -> int:
         return KGW_OUT_FP32
     if dtype == torch.bfloat16:
         return KGW_OUT_BF16
-    raise ValueError(f"output dtype must be float32 or bfloat16, got {dtype}")
+    if dtype == torch.float16:
+        return KGW_OUT_FP16
+    raise ValueError(f"output dtype must be float32, bfloat16 or float16, got {dtype}")
 
 
 def _prepare_out(out, E, hidden, n, out_dtype, accumulate, device):

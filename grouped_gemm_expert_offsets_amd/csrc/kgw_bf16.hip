@@ -64,7 +64,7 @@ constexpr int B_LOADS = 4;                  // direct loads per wave per B stage
 
 static_assert(BM == 256 && BN == 256 && BK == 32, "index math below assumes 256x256x32");
 
-template <bool OUT_BF16>
+template <int OUT>
 __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TILES];
     lds_char* tiles = (lds_char*)smem;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         begin &= ~(2 * BK - 1);
         const int ksteps = ((end - begin) / (2 * BK)) * 2;
         if (ksteps == 0) {
-            if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, eo, m0, n0, tid);
+            if (!p.accumulate) zero_tile<OUT, BM, BN, NT>(p, eo, m0, n0, tid);
             continue;
         }
 
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
-        store_wave_tile_staged<OUT_BF16>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        store_wave_tile_staged<OUT>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         // The next item's direct loads overwrite the staging areas.
         barrier_no_fence();
     }
@@ -300,11 +300,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
 
 }  // namespace
 
-hipError_t launch_wgrad_bf16(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream) {
-    if (out_bf16)
-        hipLaunchKernelGGL(wgrad_bf16_kernel<true>, dim3(grid), dim3(NT), 0, stream, p);
+hipError_t launch_wgrad_bf16(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+    if (out_kind == kOutBf16)
+        hipLaunchKernelGGL(wgrad_bf16_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
+    else if (out_kind == kOutF16)
+        hipLaunchKernelGGL(wgrad_bf16_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(wgrad_bf16_kernel<false>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL(wgrad_bf16_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -146,6 +146,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
+// IEEE binary16, round to nearest even (v_cvt_f16_f32; overflow gives infinity).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const _Float16 l = (_Float16)lo, h = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Output element kinds (the values of kgw_out_dtype_t).
+constexpr int kOutF32 = 0, kOutBf16 = 1, kOutF16 = 2;
+
+// Pack / unpack two values of a 16-bit output kind.
+template <int OUT>
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    static_assert(OUT == kOutBf16 || OUT == kOutF16, "16-bit output kinds only");
+    if constexpr (OUT == kOutBf16) return pack_bf16x2(lo, hi);
+    else return pack_f16x2(lo, hi);
+}
+template <int OUT>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+    if constexpr (OUT == kOutBf16) return bf16_lo(w);
+    else return f16_lo(w);
+}
+template <int OUT>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+    if constexpr (OUT == kOutBf16) return bf16_hi(w);
+    else return f16_hi(w);
+}
+
 // Workgroups are dealt round-robin over the XCDs; give the workgroups of one
 // XCD a contiguous run of logical slots so that concurrently running tiles on
 // one XCD share operand panels in that XCD's L2.

@@ -76,7 +76,7 @@ __device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
     return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
 }
 
-template <bool OUT_BF16>
+template <int OUT>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         const int nblocks = (end - begin) / (2 * KS);
         const int ksteps = 2 * nblocks;
         if (ksteps == 0) {
-            if (!p.accumulate) zero_tile<OUT_BF16, BM, BN, NT>(p, eo, m0, n0, tid);
+            if (!p.accumulate) zero_tile<OUT, BM, BN, NT>(p, eo, m0, n0, tid);
             continue;
         }
 
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
-        store_wave_tile_staged<OUT_BF16>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
+        store_wave_tile_staged<OUT>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         // The next item's direct loads overwrite the staging areas.
         barrier_no_fence();
     }
@@ -321,11 +321,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
 
 }  // namespace
 
-hipError_t launch_wgrad_fp8_native(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream) {
-    if (out_bf16)
-        hipLaunchKernelGGL(wgrad_fp8_native_kernel<true>, dim3(grid), dim3(NT), 0, stream, p);
+hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+    if (out_kind == kOutBf16)
+        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
+    else if (out_kind == kOutF16)
+        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(wgrad_fp8_native_kernel<false>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/kgw.h"
+#include "kgw_device.h"
 #include "kgw_internal.h"
 
 namespace {
@@ -49,7 +50,8 @@ kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, 
                           int32_t out_dtype, int32_t accumulate, int64_t token_align, int64_t n_align,
                           int64_t bm, int64_t bn) {
     if (num_experts < 1 || hidden < 0 || n < 0 || tokens_sum < 0) return KGW_ERROR_INVALID_VALUE;
-    if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16) return KGW_ERROR_INVALID_VALUE;
+    if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16 && out_dtype != KGW_OUT_FP16)
+        return KGW_ERROR_INVALID_VALUE;
     if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
     if (!offsets) return KGW_ERROR_INVALID_VALUE;
     const bool has_output = hidden > 0 && n > 0;
@@ -112,6 +114,8 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
     const int64_t talign = fp8 ? KGW_FP8_TOKEN_ALIGN : KGW_BF16_TOKEN_ALIGN;
     const int64_t nalign = fp8 ? 16 : 8;
+    static_assert(KGW_OUT_FP32 == kgw::kOutF32 && KGW_OUT_BF16 == kgw::kOutBf16 && KGW_OUT_FP16 == kgw::kOutF16,
+                  "output kind codes");
     kgw_status_t st = check_common(A, B, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
                                    accumulate, talign, nalign, bm, bn);
     if (st != KGW_SUCCESS) return st;
@@ -141,7 +145,7 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     p.accumulate = accumulate;
     p.num_xcds = d.num_xcds;
     p.split = 1;
-    bool out_bf16 = out_dtype == KGW_OUT_BF16;
+    int out_kind = out_dtype;              // KGW_OUT_* values are the kernels' output kinds
 
     // Split-K when planned and the caller's workspace holds the partials;
     // otherwise one pass (same result up to the order of the fp32 additions).
@@ -152,18 +156,18 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
         p.num_items *= plan.split;
         p.out = workspace;
         p.accumulate = 0;
-        out_bf16 = false;
+        out_kind = kgw::kOutF32;
     }
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
     hipError_t err;
     switch (kernel) {
-        case Kernel::kBf16: err = kgw::launch_wgrad_bf16(p, out_bf16, grid, (hipStream_t)stream); break;
-        case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_bf16, grid, (hipStream_t)stream); break;
-        default: err = kgw::launch_wgrad_fp8_native(p, out_bf16, grid, (hipStream_t)stream); break;
+        case Kernel::kBf16: err = kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream); break;
+        case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream); break;
+        default: err = kgw::launch_wgrad_fp8_native(p, out_kind, grid, (hipStream_t)stream); break;
     }
     if (err == hipSuccess && split)
         err = kgw::launch_splitk_reduce((const float*)workspace, offsets, num_experts, hidden, n, tokens_sum,
-                                        plan.split, out, out_dtype == KGW_OUT_BF16, accumulate, d.num_cus,
+                                        plan.split, out, out_dtype, accumulate, d.num_cus,
                                         (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }

@@ -16,7 +16,7 @@ struct GroupedParams {
     const uint8_t* sfa;     // fp8 only: (tokens_sum/128, hidden) UE8M0 bytes
     const uint8_t* sfb;     // fp8 only: (tokens_sum/128, n) UE8M0 bytes
     const int32_t* offsets; // (num_experts,) inclusive cumulative token counts
-    void* out;              // (num_experts, hidden, n) fp32 or bf16
+    void* out;              // (num_experts, hidden, n) fp32, bf16 or fp16
     int64_t hidden;
     int64_t n;
     int64_t tokens_sum;
@@ -37,15 +37,15 @@ constexpr int kSplitUnit = 256;
 constexpr int kBf16BM = 256, kBf16BN = 256, kBf16BK = 32;
 constexpr int kFp8BM = 256, kFp8BN = 256, kFp8BK = 128;
 
-hipError_t launch_wgrad_bf16(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_wgrad_bf16(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 // Split-K second pass: out[e] (=|+=) the sum over c = 0..split-1, in order, of the fp32
 // partial slabs ws[c*E + e]; in accumulate mode an expert without tokens is left as is.
 hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t num_experts, int64_t hidden,
-                                int64_t n, int64_t tokens_sum, int32_t split, void* out, bool out_bf16,
+                                int64_t n, int64_t tokens_sum, int32_t split, void* out, int out_kind,
                                 int32_t accumulate, int num_cus, hipStream_t stream);
-hipError_t launch_wgrad_fp8(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
                                uint8_t* s, int num_cus, hipStream_t stream);
-hipError_t launch_wgrad_fp8_native(const GroupedParams& p, bool out_bf16, int grid, hipStream_t stream);
+hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

@@ -5,7 +5,7 @@
 //     out[e] (=|+=) ((P_0 + P_1) + P_2) + ... + P_{split-1}
 // in chunk order, then applies the output mode once (cuDNN "Grouped GEMM +
 // WGrad (Unified)", section "Operation": overwrite, or accumulate onto the
-// caller's output; bf16 output rounded once, after the add).  In accumulate
+// caller's output; a 16-bit output rounded once, after the add).  In accumulate
 // mode an expert without tokens is left untouched, as in the one-pass kernels.
 //
 // Roofline: HBM.  Per output element it reads split fp32 partials (and the old
@@ -20,7 +20,7 @@ namespace {
 
 constexpr int NT = 256;
 
-template <bool OUT_BF16>
+template <int OUT>
 __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* ws, const int32_t* offsets, int32_t E,
                                                            int64_t H, int64_t N, int64_t T, int32_t split,
                                                            void* out, int32_t accumulate) {
@@ -39,16 +39,16 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* ws, cons
         }
         f32x4 acc = *(const f32x4*)(ws + idx);
         for (int c = 1; c < split; ++c) acc += *(const f32x4*)(ws + (int64_t)c * chunk_stride + idx);
-        if constexpr (OUT_BF16) {
+        if constexpr (OUT != kOutF32) {
             i32x2* dst = (i32x2*)((char*)out + idx * 2);
             if (accumulate) {
                 const i32x2 old = *dst;
-                acc[0] += bf16_lo((uint32_t)old[0]);
-                acc[1] += bf16_hi((uint32_t)old[0]);
-                acc[2] += bf16_lo((uint32_t)old[1]);
-                acc[3] += bf16_hi((uint32_t)old[1]);
+                acc[0] += half_lo<OUT>((uint32_t)old[0]);
+                acc[1] += half_hi<OUT>((uint32_t)old[0]);
+                acc[2] += half_lo<OUT>((uint32_t)old[1]);
+                acc[3] += half_hi<OUT>((uint32_t)old[1]);
             }
-            const i32x2 w = {(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
+            const i32x2 w = {(int)pack_half2<OUT>(acc[0], acc[1]), (int)pack_half2<OUT>(acc[2], acc[3])};
             *dst = w;
         } else {
             f32x4* dst = (f32x4*)((char*)out + idx * 4);
@@ -61,18 +61,21 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* ws, cons
 }  // namespace
 
 hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t num_experts, int64_t hidden,
-                                int64_t n, int64_t tokens_sum, int32_t split, void* out, bool out_bf16,
+                                int64_t n, int64_t tokens_sum, int32_t split, void* out, int out_kind,
                                 int32_t accumulate, int num_cus, hipStream_t stream) {
     const int64_t total4 = (int64_t)num_experts * hidden * n / 4;
     int64_t blocks = (total4 + NT - 1) / NT;
     const int64_t cap = (int64_t)num_cus * 8;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    if (out_bf16)
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, ws, offsets,
+    if (out_kind == kOutBf16)
+        hipLaunchKernelGGL(splitk_reduce_kernel<kOutBf16>, dim3((unsigned)blocks), dim3(NT), 0, stream, ws, offsets,
+                           num_experts, hidden, n, tokens_sum, split, out, accumulate);
+    else if (out_kind == kOutF16)
+        hipLaunchKernelGGL(splitk_reduce_kernel<kOutF16>, dim3((unsigned)blocks), dim3(NT), 0, stream, ws, offsets,
                            num_experts, hidden, n, tokens_sum, split, out, accumulate);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, ws, offsets,
+        hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(NT), 0, stream, ws, offsets,
                            num_experts, hidden, n, tokens_sum, split, out, accumulate);
     return hipGetLastError();
 }

@@ -1,5 +1,5 @@
 // Output side shared by the kernels: zero-filling a tile of an empty expert and
-// writing a wave's accumulators (overwrite or accumulate, fp32 or bf16).
+// writing a wave's accumulators (overwrite or accumulate; fp32, bf16 or fp16).
 #pragma once
 
 #include "kgw_device.h"
@@ -9,9 +9,9 @@ namespace kgw {
 
 // Overwrite-mode output of an expert without tokens: +0.0 over the tile
 // [m0, m0+BM) x [n0, n0+BN) of out[e], clipped to (hidden, n).
-template <bool OUT_BF16, int BM, int BN, int NT>
+template <int OUT, int BM, int BN, int NT>
 __device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t m0, int64_t n0, int tid) {
-    constexpr int ESIZE = OUT_BF16 ? 2 : 4;
+    constexpr int ESIZE = OUT == kOutF32 ? 4 : 2;
     constexpr int PER_CHUNK = 16 / ESIZE;
     const int rows = (int)min<int64_t>(BM, p.hidden - m0);
     const int cols = (int)min<int64_t>(BN, p.n - n0);
@@ -28,68 +28,21 @@ __device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t
 
 // A wave's 128x128 quarter of the tile, held as 4 (N blocks j) x 4 (M blocks i)
 // MFMA 32x32 accumulators of the transposed product: acc[j][i][4g + t] is
-// out[m][n] with m = mb + 32i + (lane & 31) and n = nb + 32j + 8g + 4*(lane >> 5) + t.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_wave_tile(const GroupedParams& p, int e, int64_t mb, int64_t nb,
-                                                int lane, const f32x16 (&acc)[4][4]) {
-    constexpr int ESIZE = OUT_BF16 ? 2 : 4;
-    const int64_t H = p.hidden, N = p.n;
-    const int l32 = lane & 31, lhi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = mb + 32 * i + l32;
-        if (m >= H) continue;
-        char* rowp = (char*)p.out + (((int64_t)e * H + m) * N) * ESIZE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t nn = nb + 32 * j + 8 * g + 4 * lhi;
-                if (nn >= N) continue;
-                float v0 = acc[j][i][4 * g + 0], v1 = acc[j][i][4 * g + 1];
-                float v2 = acc[j][i][4 * g + 2], v3 = acc[j][i][4 * g + 3];
-                if constexpr (OUT_BF16) {
-                    i32x2* dst = (i32x2*)(rowp + nn * 2);
-                    if (p.accumulate) {
-                        const i32x2 old = *dst;
-                        v0 += bf16_lo((uint32_t)old[0]);
-                        v1 += bf16_hi((uint32_t)old[0]);
-                        v2 += bf16_lo((uint32_t)old[1]);
-                        v3 += bf16_hi((uint32_t)old[1]);
-                    }
-                    const i32x2 w = {(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
-                    *dst = w;
-                } else {
-                    f32x4* dst = (f32x4*)(rowp + nn * 4);
-                    if (p.accumulate) {
-                        const f32x4 old = *dst;
-                        v0 += old[0];
-                        v1 += old[1];
-                        v2 += old[2];
-                        v3 += old[3];
-                    }
-                    const f32x4 w = {v0, v1, v2, v3};
-                    *dst = w;
-                }
-            }
-        }
-    }
-}
-
-// Same output as store_wave_tile, staged through `stage`, a 32 KiB LDS region
+// out[m][n] with m = mb + 32i + (lane & 31) and n = nb + 32j + 8g + 4*(lane >> 5) + t,
+// written (overwrite or accumulate, output kind OUT) through `stage`, a 32 KiB LDS region
 // private to the calling wave (16-byte aligned, free of other traffic).  The
 // MFMA layout gives each lane one row and four columns per register group, so
 // direct stores scatter 16 bytes over 32 rows per instruction; after a
 // transpose through LDS every store instruction writes whole row segments
-// (fp32: 2 rows x 512 B; bf16: 8 values per lane, 4 rows x 256 B), and
+// (fp32: 2 rows x 512 B; bf16/fp16: 8 values per lane, 4 rows x 256 B), and
 // accumulate mode reads the old values the same way.  The accumulators go
-// through LDS as fp32 in two passes of 64 rows (bf16 output is rounded once,
-// after the optional add).  The LDS image holds rows of 32 16-byte chunks with
+// through LDS as fp32 in two passes of 64 rows (16-bit outputs are rounded
+// once, after the optional add).  The LDS image holds rows of 32 16-byte chunks with
 // chunk c of row r at slot c ^ (r & 31), so both the scattered writes and the
 // row reads spread over all banks.  The caller must keep other waves' LDS
 // traffic out of `stage` until this returns (its LDS reads are complete once
 // its last store is issued).
-template <bool OUT_BF16>
+template <int OUT>
 __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, int e, int64_t mb, int64_t nb,
                                                        int lane, const f32x16 (&acc)[4][4], lds_char* stage) {
     const int64_t H = p.hidden, N = p.n;
@@ -112,7 +65,7 @@ __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, i
                     lds_store_16B(stage, (uint32_t)(r * 512 + ((c ^ (r & 31)) << 4)), __builtin_bit_cast(i32x4, w));
                 }
         }
-        if constexpr (OUT_BF16) {
+        if constexpr (OUT != kOutF32) {
             // each lane: 8 consecutive columns (two chunks) -> one 16-byte store;
             // an instruction writes four rows of 256 B
             const int c2 = lane & 15;
@@ -130,12 +83,12 @@ __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, i
                     const i32x4 old = *dst;
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        v[2 * h] += bf16_lo((uint32_t)old[h]);
-                        v[2 * h + 1] += bf16_hi((uint32_t)old[h]);
+                        v[2 * h] += half_lo<OUT>((uint32_t)old[h]);
+                        v[2 * h + 1] += half_hi<OUT>((uint32_t)old[h]);
                     }
                 }
-                const i32x4 w = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3]),
-                                 (int)pack_bf16x2(v[4], v[5]), (int)pack_bf16x2(v[6], v[7])};
+                const i32x4 w = {(int)pack_half2<OUT>(v[0], v[1]), (int)pack_half2<OUT>(v[2], v[3]),
+                                 (int)pack_half2<OUT>(v[4], v[5]), (int)pack_half2<OUT>(v[6], v[7])};
                 *dst = w;
             }
         } else {

@@ -61,10 +61,14 @@ typedef enum {
                                     kernel launch failed                                   */
 } kgw_status_t;
 
-/* Output element type of the dense (num_experts, hidden, n) result. */
+/* Output element type of the dense (num_experts, hidden, n) result.  The fp32
+ * accumulators are rounded once, to nearest even, into a 16-bit type (fp16
+ * overflows to infinity); the cuDNN page, "BF16 contract" table, lists fp32,
+ * bf16 and fp16 outputs. */
 typedef enum {
     KGW_OUT_FP32 = 0,
-    KGW_OUT_BF16 = 1
+    KGW_OUT_BF16 = 1,
+    KGW_OUT_FP16 = 2
 } kgw_out_dtype_t;
 
 /* Token-count alignment each entry point requires (cuDNN page, section "BF16

@@ -257,6 +257,21 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(f), np.nan, out)
 
 
+def round_to_fp16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to IEEE binary16 (numpy's cast: nearest, ties to even; overflow to
+    infinity), returned as float64.  Goes through float32 first, exact for the exactness pins'
+    values (integers below 2^24)."""
+    with np.errstate(over="ignore"):                 # overflow to infinity is the defined result
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
+
+
+def fp16_ulp(x: np.ndarray) -> np.ndarray:
+    """Unit in the last place of binary16 at |x| (2^(e-10) for normal x, 2^-24 below 2^-14)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
     """Spacing of bf16 numbers at |x| (8 significant bits): 2^(floor(log2|x|) - 7)."""
     ax = np.abs(np.asarray(x, dtype=np.float64))

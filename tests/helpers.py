@@ -7,6 +7,10 @@ Tolerances (floating point):
   * bf16 output: every element within 2 bf16 ulps of the exact value, the ulp
     taken at max(|exact|, 2^-8 * rms of that expert's exact result) so that
     near-cancelled elements are judged on the expert's scale.
+  * fp16 output: the same with fp16 ulps, floor also 2^-8 * rms: near zero the
+    fp32 accumulation the contract fixes errs by ~1e-6 of the rms over long
+    token ranges, which a finer floor would count against fp16's resolution
+    (2 fp16 ulps at 2^-8 * rms is ~8e-6 of the rms, in line with fp32's 1e-5).
 Integer-valued inputs make every partial sum exact in fp32, so those cases
 are compared bit for bit.
 """
@@ -20,6 +24,7 @@ import oracle
 FP32_REL_FROB = 1e-5
 BF16_ULPS = 2.0
 BF16_FLOOR = 2.0 ** -8
+FP16_FLOOR = 2.0 ** -8
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -50,6 +55,15 @@ def assert_fp32_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
 
 def assert_bf16_close(got: np.ndarray, ref: np.ndarray, what: str = "", rms: np.ndarray = None):
     """Element-wise 2-ulp check; `rms` gives each expert's rms (defaults to ref's own)."""
+    _assert_ulps(got, ref, what, rms, BF16_FLOOR, oracle.bf16_ulp, "bf16")
+
+
+def assert_fp16_close(got: np.ndarray, ref: np.ndarray, what: str = "", rms: np.ndarray = None):
+    """Element-wise 2-ulp check in fp16 units (floor 2^-8 * rms)."""
+    _assert_ulps(got, ref, what, rms, FP16_FLOOR, oracle.fp16_ulp, "fp16")
+
+
+def _assert_ulps(got, ref, what, rms, floor, ulp_fn, name):
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     for e in range(ref.shape[0]):
@@ -58,13 +72,13 @@ def assert_bf16_close(got: np.ndarray, ref: np.ndarray, what: str = "", rms: np.
         if s == 0.0:
             assert not np.any(got[e]), f"{what}: expert {e} should be exactly zero"
             continue
-        scale = np.maximum(np.abs(r), BF16_FLOOR * s)
-        tol = BF16_ULPS * oracle.bf16_ulp(scale)
+        scale = np.maximum(np.abs(r), floor * s)
+        tol = BF16_ULPS * ulp_fn(scale)
         bad = np.abs(got[e] - r) > tol
         nbad = int(bad.sum())
         if nbad:
             idx = np.argwhere(bad)[0]
-            raise AssertionError(f"{what}: expert {e}: {nbad} elements beyond 2 bf16 ulps, first at "
+            raise AssertionError(f"{what}: expert {e}: {nbad} elements beyond 2 {name} ulps, first at "
                                  f"{tuple(idx)} got {got[e][tuple(idx)]!r} want {r[tuple(idx)]!r}")
 
 

@@ -391,3 +391,15 @@ def test_quantizer_special_blocks():
     assert s[1, 0] != 255 and s[0, 3] != 255
     with pytest.raises(ValueError):
         oracle.quantize_fp8_tokens(x[:200], 0)
+
+
+def test_round_to_fp16_ties_overflow_and_ulp():
+    # binary16: 10 fraction bits; ties to even; the largest finite is 65504
+    assert oracle.round_to_fp16(np.array([1 + 2.0 ** -11]))[0] == 1.0
+    assert oracle.round_to_fp16(np.array([1 + 3 * 2.0 ** -11]))[0] == 1 + 2.0 ** -9
+    assert oracle.round_to_fp16(np.array([65504.0]))[0] == 65504.0
+    assert np.isinf(oracle.round_to_fp16(np.array([65520.0]))[0])
+    assert oracle.round_to_fp16(np.array([2.0 ** -25]))[0] == 0.0          # half the smallest subnormal
+    assert oracle.fp16_ulp(np.array([1.0]))[0] == 2.0 ** -10
+    assert oracle.fp16_ulp(np.array([3000.0]))[0] == 2.0
+    assert oracle.fp16_ulp(np.array([2.0 ** -20]))[0] == 2.0 ** -24

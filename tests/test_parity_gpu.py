@@ -13,7 +13,7 @@ import torch
 import grouped_gemm_expert_offsets_amd as kgw
 import oracle
 import workloads
-from helpers import assert_bf16_close, assert_fp32_close, rel_frob, sample_rows, to_f64, FP32_REL_FROB
+from helpers import assert_bf16_close, assert_fp16_close, assert_fp32_close, rel_frob, sample_rows, to_f64, FP32_REL_FROB
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -192,6 +192,48 @@ def test_more_experts_than_4096(kind):
         else:
             ref = oracle.wgrad_rows_fp8(wl.A.cpu(), wl.sfa.cpu(), wl.B.cpu(), wl.sfb.cpu(), off, e, rows)
         assert np.array_equal(to_f64(out[e]), ref), f"expert {e}"
+
+
+# ----------------------------------------------------------------------------
+# fp16 output (the cuDNN contract's third output type)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_fp16_output_integer_bit_exact(kind, accumulate):
+    counts = [256, 0, 512, 256]
+    wl = workloads.make_operands(counts, 320, 272, kind, torch.float16, accumulate, seed=81, device=DEV,
+                                 integer_range=4)
+    out = wl.C0.clone() if accumulate else nan_filled((4, 320, 272), torch.float16)
+    if kind == "bf16":
+        run_bf16(wl, out=out)
+    else:
+        run_fp8(wl, out=out)
+    W = oracle_dense(wl)
+    ref = oracle.round_to_fp16(oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None))
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}"
+    if accumulate:
+        assert torch.equal(out[1].view(torch.int16), wl.C0[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("split_k", [False, True])
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_fp16_output_random(kind, split_k):
+    counts = [4096, 0, 8192, 256] if split_k else [512, 0, 768, 256]
+    wl = workloads.make_operands(counts, 320, 384, kind, torch.float16, False, seed=82, device=DEV)
+    if split_k:
+        assert kgw.kgw_workspace_bytes(4, 320, 384, sum(counts), fp8=kind == "fp8") > 0
+    out = nan_filled((4, 320, 384), torch.float16)
+    if kind == "bf16":
+        kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, split_k=split_k)
+    else:
+        kgw.kgw_wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, split_k=split_k)
+    torch.cuda.synchronize()
+    ref = oracle_dense(wl)
+    got = to_f64(out)
+    assert np.all(got[1] == 0.0) and not np.any(np.signbit(got[1]))
+    assert_fp16_close(got, ref, f"{kind} fp16 split_k={split_k}")
 
 
 # ----------------------------------------------------------------------------
