@@ -61,17 +61,17 @@ def _load():
     lib.oracle_wgrad_rows_bf16.restype = ctypes.c_int
     lib.oracle_wgrad_rows_bf16.argtypes = [p, p, i64, i64, i64, i64, p, i64, p]
     lib.oracle_wgrad_rows_fp8.restype = ctypes.c_int
-    lib.oracle_wgrad_rows_fp8.argtypes = [p, p, i64, p, p, i64, i64, i64, i64, p, i64, p]
+    lib.oracle_wgrad_rows_fp8.argtypes = [p, p, i64, p, p, i64, i64, i64, i64, p, i64, p, i64]
     lib.oracle_wgrad_bf16.restype = ctypes.c_int
     lib.oracle_wgrad_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p]
     lib.oracle_wgrad_fp8.restype = ctypes.c_int
-    lib.oracle_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
+    lib.oracle_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i64]
     lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
     lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_double]
     lib.oracle_e8m0_for_amax.restype = ctypes.c_uint8
     lib.oracle_e8m0_for_amax.argtypes = [ctypes.c_double]
     lib.oracle_quantize_fp8_tokens.restype = ctypes.c_int
-    lib.oracle_quantize_fp8_tokens.argtypes = [p, i64, i64, ctypes.c_int, p, p]
+    lib.oracle_quantize_fp8_tokens.argtypes = [p, i64, i64, ctypes.c_int, p, p, i64]
     _lib = lib
     return lib
 
@@ -155,8 +155,8 @@ def wgrad_rows_bf16(A, B, offsets, e: int, rows: Sequence[int]) -> np.ndarray:
     return out
 
 
-def wgrad_rows_fp8(A, sfa, B, sfb, offsets, e: int, rows: Sequence[int]) -> np.ndarray:
-    """Rows `rows` of Wgrad[e] in float64 (e4m3 operands, UE8M0 per 128 tokens)."""
+def wgrad_rows_fp8(A, sfa, B, sfb, offsets, e: int, rows: Sequence[int], block: int = 128) -> np.ndarray:
+    """Rows `rows` of Wgrad[e] in float64 (e4m3 operands, one UE8M0 byte per `block` tokens)."""
     a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
     hidden, T = a.shape
     n = b.shape[1]
@@ -164,8 +164,9 @@ def wgrad_rows_fp8(A, sfa, B, sfb, offsets, e: int, rows: Sequence[int]) -> np.n
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     assert r.size == 0 or (r.min() >= 0 and r.max() < hidden)
     out = np.empty((r.size, n), dtype=np.float64)
+    assert sa.shape == (T // block, hidden) and sb.shape == (T // block, n), "scale shape"
     rc = _load().oracle_wgrad_rows_fp8(_ptr(a), _ptr(sa), hidden, _ptr(b), _ptr(sb), T, n, begin, end,
-                                       _ptr(r), r.size, _ptr(out))
+                                       _ptr(r), r.size, _ptr(out), int(block))
     if rc != 0:
         raise ValueError(f"oracle: bad token range [{begin}, {end}) for tokens_sum {T}")
     return out
@@ -184,15 +185,17 @@ def wgrad_bf16(A, B, offsets) -> np.ndarray:
     return out
 
 
-def wgrad_fp8(A, sfa, B, sfb, offsets) -> np.ndarray:
-    """Dense Wgrad (E, hidden, n) in float64 for e4m3 operands with UE8M0 block scales."""
+def wgrad_fp8(A, sfa, B, sfb, offsets, block: int = 128) -> np.ndarray:
+    """Dense Wgrad (E, hidden, n) in float64 for e4m3 operands with one UE8M0 byte per `block`
+    tokens: sfa (tokens_sum/block, hidden), sfb (tokens_sum/block, n)."""
     a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
     off = np.ascontiguousarray(_as_numpy(offsets).astype(np.int32))
     hidden, T = a.shape
     n = b.shape[1]
     out = np.empty((off.size, hidden, n), dtype=np.float64)
+    assert sa.shape == (T // block, hidden) and sb.shape == (T // block, n), "scale shape"
     rc = _load().oracle_wgrad_fp8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(off), off.size, hidden, n, T,
-                                  _ptr(out))
+                                  _ptr(out), int(block))
     if rc != 0:
         raise ValueError("oracle: malformed offsets")
     return out
@@ -209,11 +212,11 @@ def e8m0_for_amax(amax: float) -> int:
     return int(_load().oracle_e8m0_for_amax(float(amax)))
 
 
-def quantize_fp8_tokens(x, token_axis: int):
-    """Quantise bf16 x (rows, cols) to e4m3fn with one UE8M0 scale per 128 tokens.
+def quantize_fp8_tokens(x, token_axis: int, block: int = 128):
+    """Quantise bf16 x (rows, cols) to e4m3fn with one UE8M0 scale per `block` tokens.
 
-    token_axis 1: tokens along the columns (A (hidden, tokens)), scales (cols/128, rows);
-    token_axis 0: tokens along the rows (B (tokens, n)), scales (rows/128, cols).
+    token_axis 1: tokens along the columns (A (hidden, tokens)), scales (cols/block, rows);
+    token_axis 0: tokens along the rows (B (tokens, n)), scales (rows/block, cols).
     Returns (q uint8 in x's layout, s uint8).
     """
     xb = _u16(x)
@@ -221,11 +224,45 @@ def quantize_fp8_tokens(x, token_axis: int):
     tokens = cols if token_axis else rows
     other = rows if token_axis else cols
     q = np.empty((rows, cols), dtype=np.uint8)
-    s = np.empty((tokens // 128, other), dtype=np.uint8)
-    rc = _load().oracle_quantize_fp8_tokens(_ptr(xb), rows, cols, int(token_axis), _ptr(q), _ptr(s))
+    s = np.empty((tokens // block, other), dtype=np.uint8)
+    rc = _load().oracle_quantize_fp8_tokens(_ptr(xb), rows, cols, int(token_axis), _ptr(q), _ptr(s), int(block))
     if rc != 0:
-        raise ValueError("the token length must be a multiple of 128")
+        raise ValueError(f"the token length must be a multiple of {block}")
     return q, s
+
+
+# ----------------------------------------------------------------------------
+# packed UE8M0 scale layout
+# ----------------------------------------------------------------------------
+# The pages name a packed UE8M0 scale tensor (the DeepGEMM k-grouped page's
+# use_packed_ue8m0 flag; the llm-infra-atlas page, section 3, mn-major scales
+# whose 8-bit exponents are packed) without printing its layout.  Reading used
+# here: four consecutive blocks along the token axis share one little-endian
+# 32-bit word, mn-major -- word (w, m) holds the scale byte of block 4w + j for
+# mn index m in its byte j (bits 8j .. 8j+7); bytes of blocks past the last one
+# are zero.
+def pack_scales(s) -> np.ndarray:
+    """(nblocks, mn) uint8 scale bytes -> (ceil(nblocks/4), mn) int32 packed words."""
+    s = _u8(s)
+    nb, mn = s.shape
+    nw = (nb + 3) // 4
+    padded = np.zeros((4 * nw, mn), dtype=np.uint32)
+    padded[:nb] = s
+    words = np.zeros((nw, mn), dtype=np.uint32)
+    for j in range(4):
+        words |= padded[j::4] << np.uint32(8 * j)
+    return words.view(np.int32)
+
+
+def unpack_scales(words, nblocks: int) -> np.ndarray:
+    """Inverse of pack_scales: (ceil(nblocks/4), mn) int32 words -> (nblocks, mn) uint8 bytes."""
+    w = np.ascontiguousarray(_as_numpy(words)).view(np.uint32)
+    nw, mn = w.shape
+    assert nw == (nblocks + 3) // 4, "word count"
+    out = np.zeros((4 * nw, mn), dtype=np.uint8)
+    for j in range(4):
+        out[j::4] = ((w >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
+    return out[:nblocks]
 
 
 def apply_output_mode(W: np.ndarray, accumulate: bool, C0: Optional[np.ndarray] = None) -> np.ndarray:

@@ -19,9 +19,12 @@
  *
  * For the fp8 path (llm-infra-atlas "05 Grouped GEMM", section 3, FP8 data
  * layout: one power-of-two scale per 1x128 block, here along the token axis
- * as the k-grouped weight gradient needs) each operand element is first
- * decoded to its real value e4m3(q) * 2^(scale_byte - 127) and the same sum
- * is taken over those values.
+ * as the k-grouped weight gradient needs; the DeepGEMM k-grouped page's
+ * casting step also quantises with gran_k = 32, one scale per 32 elements)
+ * each operand element is first decoded to its real value
+ * e4m3(q) * 2^(scale_byte - 127), the scale byte being that of the element's
+ * block of `block` tokens (128 or 32), and the same sum is taken over those
+ * values.
  *
  * Format decoders are written from the format definitions:
  *   bf16      : the upper 16 bits of an IEEE-754 binary32 word;
@@ -101,21 +104,22 @@ int oracle_wgrad_rows_bf16(const uint16_t* A, const uint16_t* B, int64_t tokens_
 }
 
 /*
- * Same for fp8 operands with one UE8M0 scale per 128 tokens:
- * A: e4m3 bytes (hidden, tokens_sum); sfa: bytes (tokens_sum/128, hidden);
- * B: e4m3 bytes (tokens_sum, n);      sfb: bytes (tokens_sum/128, n).
+ * Same for fp8 operands with one UE8M0 scale per `block` tokens:
+ * A: e4m3 bytes (hidden, tokens_sum); sfa: bytes (tokens_sum/block, hidden);
+ * B: e4m3 bytes (tokens_sum, n);      sfb: bytes (tokens_sum/block, n).
  */
 int oracle_wgrad_rows_fp8(const uint8_t* A, const uint8_t* sfa, int64_t hidden, const uint8_t* B,
                           const uint8_t* sfb, int64_t tokens_sum, int64_t n, int64_t begin,
-                          int64_t end, const int64_t* rows, int64_t nrows, double* out) {
+                          int64_t end, const int64_t* rows, int64_t nrows, double* out, int64_t block) {
     if (begin < 0 || end < begin || end > tokens_sum) return -1;
+    if (block < 1 || tokens_sum % block != 0) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t m = rows[r];
         double* w = out + r * n;
         for (int64_t j = 0; j < n; ++j) w[j] = 0.0;
         for (int64_t k = begin; k < end; ++k) {
-            const int64_t blk = k / 128;
+            const int64_t blk = k / block;
             const double a = oracle_e4m3fn_value(A[m * tokens_sum + k]) *
                              oracle_e8m0_value(sfa[blk * hidden + m]);
             const uint8_t* brow = B + k * n;
@@ -148,7 +152,7 @@ int oracle_wgrad_bf16(const uint16_t* A, const uint16_t* B, const int32_t* offse
 /* Dense Wgrad (num_experts, hidden, n) for every expert, fp8 block-scaled operands. */
 int oracle_wgrad_fp8(const uint8_t* A, const uint8_t* sfa, const uint8_t* B, const uint8_t* sfb,
                      const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
-                     int64_t tokens_sum, double* out) {
+                     int64_t tokens_sum, double* out, int64_t block) {
     int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(hidden > 0 ? hidden : 1));
     if (!rows) return -2;
     for (int64_t m = 0; m < hidden; ++m) rows[m] = m;
@@ -157,7 +161,7 @@ int oracle_wgrad_fp8(const uint8_t* A, const uint8_t* sfa, const uint8_t* B, con
         int64_t begin, end;
         oracle_expert_range(offsets, e, &begin, &end);
         rc = oracle_wgrad_rows_fp8(A, sfa, hidden, B, sfb, tokens_sum, n, begin, end, rows, hidden,
-                                   out + (int64_t)e * hidden * n);
+                                   out + (int64_t)e * hidden * n, block);
     }
     free(rows);
     return rc;
@@ -166,7 +170,8 @@ int oracle_wgrad_fp8(const uint8_t* A, const uint8_t* sfa, const uint8_t* B, con
 /*
  * Token-axis fp8 quantiser (llm-infra-atlas "05 Grouped GEMM", section 3: one
  * power-of-two UE8M0 scale per 1x128 block; for the k-grouped weight gradient
- * the blocks run along the token axis, section 5.2).  The pages leave the
+ * the blocks run along the token axis, section 5.2; the DeepGEMM k-grouped
+ * page's casting step uses blocks of gran_k = 32 elements instead).  The pages leave the
  * choice of the scale open; the reading used here takes, per block, the
  * smallest power of two 2^k with amax <= 448 * 2^k (448 = largest e4m3fn),
  * stores the biased exponent k + 127 clamped to [1, 254] (127 for an all-zero
@@ -218,21 +223,21 @@ uint8_t oracle_e8m0_for_amax(double amax) {
 
 /* x: bf16 bits, (rows, cols) row-major.  token_axis 1: tokens run along the
  * columns (A of the weight gradient, (hidden, tokens)), scales s are
- * (cols/128, rows); token_axis 0: tokens run along the rows (B, (tokens, n)),
- * scales (rows/128, cols).  q: e4m3fn bytes in x's layout.  Returns 0, or -1
- * when the token length is not a multiple of 128. */
+ * (cols/block, rows); token_axis 0: tokens run along the rows (B, (tokens, n)),
+ * scales (rows/block, cols).  q: e4m3fn bytes in x's layout.  Returns 0, or -1
+ * when the token length is not a multiple of the block (block >= 1). */
 int oracle_quantize_fp8_tokens(const uint16_t* x, int64_t rows, int64_t cols, int token_axis, uint8_t* q,
-                               uint8_t* s) {
+                               uint8_t* s, int64_t block) {
     const int64_t tokens = token_axis ? cols : rows;
     const int64_t other = token_axis ? rows : cols;
-    if (tokens % 128 != 0) return -1;
-    const int64_t nblocks = tokens / 128;
+    if (block < 1 || tokens % block != 0) return -1;
+    const int64_t nblocks = tokens / block;
 #pragma omp parallel for schedule(static)
     for (int64_t o = 0; o < other; ++o) {
         for (int64_t b = 0; b < nblocks; ++b) {
             double amax = 0.0;
             int bad = 0;
-            for (int64_t t = 128 * b; t < 128 * b + 128; ++t) {
+            for (int64_t t = block * b; t < block * b + block; ++t) {
                 const int64_t idx = token_axis ? o * cols + t : t * cols + o;
                 const double v = oracle_bf16_value(x[idx]);
                 if (isnan(v) || isinf(v)) bad = 1;
@@ -240,7 +245,7 @@ int oracle_quantize_fp8_tokens(const uint16_t* x, int64_t rows, int64_t cols, in
             }
             const uint8_t e = bad ? 0xFF : oracle_e8m0_for_amax(amax);
             s[b * other + o] = e;
-            for (int64_t t = 128 * b; t < 128 * b + 128; ++t) {
+            for (int64_t t = block * b; t < block * b + block; ++t) {
                 const int64_t idx = token_axis ? o * cols + t : t * cols + o;
                 q[idx] = bad ? 0x7F : oracle_e4m3fn_encode(ldexp(oracle_bf16_value(x[idx]), 127 - (int)e));
             }

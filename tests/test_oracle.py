@@ -214,39 +214,93 @@ def test_tiny_config_against_brute_force(oracle_lib):
 # ----------------------------------------------------------------------------
 # fp8 block-scaled product
 # ----------------------------------------------------------------------------
-def dequant(q: torch.Tensor, s: torch.Tensor, token_axis: int) -> np.ndarray:
-    """Library-side dequantisation: torch float8 decode times 2^(s-127) per 128-token block."""
+def dequant(q: torch.Tensor, s: torch.Tensor, token_axis: int, block: int = 128) -> np.ndarray:
+    """Library-side dequantisation: torch float8 decode times 2^(s-127) per `block` tokens."""
     v = q.view(torch.float8_e4m3fn).double()
-    sc = torch.exp2(s.double() - 127.0).repeat_interleave(128, dim=0)    # (T, other)
+    sc = torch.exp2(s.double() - 127.0).repeat_interleave(block, dim=0)  # (T, other)
     if token_axis == 1:
         sc = sc.t()
     return (v * sc).numpy()
 
 
-def test_fp8_matches_dequantised_brute_force(oracle_lib):
+@pytest.mark.parametrize("block", [128, 32])
+def test_fp8_matches_dequantised_brute_force(oracle_lib, block):
     counts = [128, 0, 256, 384]
-    wl = workloads.make_operands(counts, 24, 40, "fp8", torch.bfloat16, False, seed=5)
-    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets)
-    ref = brute_force(dequant(wl.A, wl.sfa, 1), dequant(wl.B, wl.sfb, 0), counts)
+    wl = workloads.make_operands(counts, 24, 40, "fp8", torch.bfloat16, False, seed=5, scale_block=block)
+    assert wl.sfa.shape == (768 // block, 24)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, block=block)
+    ref = brute_force(dequant(wl.A, wl.sfa, 1, block), dequant(wl.B, wl.sfb, 0, block), counts)
     np.testing.assert_allclose(W, ref, rtol=1e-12, atol=1e-12)
 
 
-def test_fp8_block_scale_byte_doubles_its_block(oracle_lib):
+@pytest.mark.parametrize("block", [128, 32])
+def test_fp8_block_scale_byte_doubles_its_block(oracle_lib, block):
     counts = [256, 128]
-    wl = workloads.make_operands(counts, 8, 16, "fp8", torch.bfloat16, False, seed=6)
-    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets)
-    # contribution of token block 1 (tokens 128..255, inside expert 0) to row 3
+    wl = workloads.make_operands(counts, 8, 16, "fp8", torch.bfloat16, False, seed=6, scale_block=block)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, block=block)
+    # contribution of token block 1 (tokens block..2*block-1, inside expert 0) to row 3
     A1 = wl.A.clone()
-    A1[:, :128] = 0  # zero e4m3 byte is +0
-    A1[:, 256:] = 0
-    part = oracle.wgrad_fp8(A1, wl.sfa, wl.B, wl.sfb, wl.offsets)
+    A1[:, :block] = 0  # zero e4m3 byte is +0
+    A1[:, 2 * block:] = 0
+    part = oracle.wgrad_fp8(A1, wl.sfa, wl.B, wl.sfb, wl.offsets, block=block)
     sfa2 = wl.sfa.clone()
     sfa2[1, 3] += 1
-    W2 = oracle.wgrad_fp8(wl.A, sfa2, wl.B, wl.sfb, wl.offsets)
+    W2 = oracle.wgrad_fp8(wl.A, sfa2, wl.B, wl.sfb, wl.offsets, block=block)
     np.testing.assert_allclose(W2[0, 3] - W[0, 3], part[0, 3], rtol=1e-12, atol=1e-12)
     mask = np.ones_like(W, dtype=bool)
     mask[0, 3] = False
     assert np.array_equal(W2[mask], W[mask])
+    # the same through B: doubling block 1's scale of column 5 adds its contribution once more
+    B1 = wl.B.clone()
+    B1[:block] = 0
+    B1[2 * block:] = 0
+    partb = oracle.wgrad_fp8(wl.A, wl.sfa, B1, wl.sfb, wl.offsets, block=block)
+    sfb2 = wl.sfb.clone()
+    sfb2[1, 5] += 1
+    W3 = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, sfb2, wl.offsets, block=block)
+    np.testing.assert_allclose(W3[0, :, 5] - W[0, :, 5], partb[0, :, 5], rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_block_size_matters(oracle_lib):
+    # reading 32-token scales as 128-token ones (or the reverse) must change the result
+    counts = [256]
+    wl = workloads.make_operands(counts, 8, 16, "fp8", torch.bfloat16, False, seed=9, scale_block=32)
+    W = oracle.wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, block=32)
+    ref = brute_force(dequant(wl.A, wl.sfa, 1, 32), dequant(wl.B, wl.sfb, 0, 32), counts)
+    np.testing.assert_allclose(W, ref, rtol=1e-12, atol=1e-12)
+    wrong = brute_force(dequant(wl.A, wl.sfa[::4].contiguous(), 1, 128),
+                        dequant(wl.B, wl.sfb[::4].contiguous(), 0, 128), counts)
+    assert not np.allclose(W, wrong, rtol=1e-3)
+
+
+# ----------------------------------------------------------------------------
+# packed scale words (reading: four consecutive blocks per little-endian int32,
+# block 4w + j in byte j of word (w, m), zero bytes past the last block)
+# ----------------------------------------------------------------------------
+def test_pack_scales_hand_example(oracle_lib):
+    # five blocks of two columns: column 0 holds 1, 3, 5, 7, 9 and column 1 holds 2, 4, ..., 10
+    s = np.arange(1, 11, dtype=np.uint8).reshape(5, 2)
+    w = oracle.pack_scales(s).view(np.uint32)
+    assert w.shape == (2, 2)
+    assert w.tolist() == [[0x07050301, 0x08060402], [0x00000009, 0x0000000A]]
+    assert np.array_equal(oracle.unpack_scales(w.view(np.int32), 5), s)
+    # the same words read as bytes in memory order: byte j of a word is its bits 8j..8j+7
+    assert w.view(np.uint8)[0].tolist() == [1, 3, 5, 7, 2, 4, 6, 8]
+
+
+@pytest.mark.parametrize("nblocks", [1, 4, 6, 13])
+def test_pack_scales_round_trip_and_generator(oracle_lib, nblocks):
+    g = torch.Generator().manual_seed(nblocks)
+    s = torch.randint(0, 256, (nblocks, 7), generator=g, dtype=torch.int32).to(torch.uint8)
+    w = oracle.pack_scales(s.numpy())
+    assert w.shape == ((nblocks + 3) // 4, 7) and w.dtype == np.int32
+    assert np.array_equal(oracle.unpack_scales(w, nblocks), s.numpy())
+    assert np.array_equal(workloads.pack_scale_words(s).numpy(), w)
+    # padding bytes past the last block are zero
+    pad = 4 * w.shape[0] - nblocks
+    if pad:
+        last = w[-1].view(np.uint32)
+        assert np.all(last >> np.uint32(8 * (4 - pad)) == 0)
 
 
 def test_fp8_integer_inputs_are_exact(oracle_lib):
@@ -343,29 +397,32 @@ def test_e8m0_for_amax_is_the_smallest_sufficient_power_of_two():
     assert oracle.e8m0_for_amax(float("nan")) == 255
 
 
+@pytest.mark.parametrize("block", [128, 32])
 @pytest.mark.parametrize("token_axis", [0, 1])
-def test_quantizer_matches_the_independent_generator_implementation(token_axis):
+def test_quantizer_matches_the_independent_generator_implementation(token_axis, block):
     # workloads.quantize_token_blocks (torch float8 cast, float64 log2) is written separately
     g = torch.Generator().manual_seed(7)
     shape = (200, 384) if token_axis else (384, 200)
     x = (torch.randn(shape, generator=g) * torch.exp2(torch.randint(-20, 20, (1, shape[1]), generator=g).float())
          ).to(torch.bfloat16)
-    q_ref, s_ref = workloads.quantize_token_blocks(x, token_axis=token_axis)
-    q, s = oracle.quantize_fp8_tokens(x, token_axis)
+    q_ref, s_ref = workloads.quantize_token_blocks(x, token_axis=token_axis, block=block)
+    q, s = oracle.quantize_fp8_tokens(x, token_axis, block=block)
+    assert s.shape == (384 // block, 200)
     assert np.array_equal(s, s_ref.numpy())
     assert np.array_equal(q, q_ref.numpy())
 
 
+@pytest.mark.parametrize("block", [128, 32])
 @pytest.mark.parametrize("token_axis", [0, 1])
-def test_quantizer_dequantised_values_are_within_half_an_e4m3_step(token_axis):
+def test_quantizer_dequantised_values_are_within_half_an_e4m3_step(token_axis, block):
     g = torch.Generator().manual_seed(8)
     shape = (64, 256) if token_axis else (256, 64)
     x = torch.randn(shape, generator=g).to(torch.bfloat16)
-    q, s = oracle.quantize_fp8_tokens(x, token_axis)
+    q, s = oracle.quantize_fp8_tokens(x, token_axis, block=block)
     xs = x.float().numpy().astype(np.float64)
     deq = np.vectorize(oracle.e4m3fn_value)(q)
     scale = np.exp2(s.astype(np.float64) - 127)
-    scale_full = np.repeat(scale, 128, axis=0)            # (tokens, other)
+    scale_full = np.repeat(scale, block, axis=0)          # (tokens, other)
     if token_axis:
         scale_full = scale_full.T
     v = deq * scale_full
@@ -375,7 +432,7 @@ def test_quantizer_dequantised_values_are_within_half_an_e4m3_step(token_axis):
     assert np.all(np.abs(v - xs) <= step / 2 + 1e-300)
     # every block's largest element, scaled, lies in (224, 448], so after rounding in [224, 448]
     tok_major = deq if not token_axis else deq.T                    # (tokens, other)
-    bmax = np.abs(tok_major).reshape(-1, 128, tok_major.shape[1]).max(axis=1)
+    bmax = np.abs(tok_major).reshape(-1, block, tok_major.shape[1]).max(axis=1)
     assert np.all(bmax >= 224) and np.all(bmax <= 448)
 
 
@@ -391,6 +448,14 @@ def test_quantizer_special_blocks():
     assert s[1, 0] != 255 and s[0, 3] != 255
     with pytest.raises(ValueError):
         oracle.quantize_fp8_tokens(x[:200], 0)
+    # 32-token blocks: the NaN at token 130 poisons only block 4 of column 1
+    q32, s32 = oracle.quantize_fp8_tokens(x, 0, block=32)
+    assert s32[4, 1] == 255 and np.all(q32[128:160, 1] == 0x7F)
+    assert np.all(s32[[0, 1, 2, 3, 5, 6, 7], 1] != 255) and np.all(q32[160:, 1] != 0x7F)
+    assert s32[0, 2] == 255 and s32[1, 2] != 255
+    assert np.all(s32[:4, 0] == 127)
+    with pytest.raises(ValueError):
+        oracle.quantize_fp8_tokens(x[:240], 0, block=32)
 
 
 def test_round_to_fp16_ties_overflow_and_ulp():

@@ -132,27 +132,37 @@ def e8m0_exponent_for_block(amax: torch.Tensor) -> torch.Tensor:
     return e.clamp_(1, 254).to(torch.uint8)
 
 
-def quantize_token_blocks(x: torch.Tensor, token_axis: int):
-    """Quantise a bf16/fp32 matrix to OCP e4m3fn with one UE8M0 scale per 128 tokens.
+def quantize_token_blocks(x: torch.Tensor, token_axis: int, block: int = SCALE_BLOCK):
+    """Quantise a bf16/fp32 matrix to OCP e4m3fn with one UE8M0 scale per `block` tokens.
 
     token_axis = 1 for A (hidden, tokens) and 0 for B (tokens, N).  Returns
     (q, s): q holds e4m3fn bytes (uint8) in x's layout; s holds the biased
-    exponents (uint8) laid out (tokens/128, other_dim), i.e. mn-major.
+    exponents (uint8) laid out (tokens/block, other_dim), i.e. mn-major.
     Rounding: round-to-nearest-even in the float8 conversion.
     """
     xf = x.to(torch.float32)
     if token_axis == 1:
         xf = xf.t()                      # (tokens, other)
     t, o = xf.shape
-    assert t % SCALE_BLOCK == 0, "token count must be a multiple of the scale block"
-    blocks = xf.reshape(t // SCALE_BLOCK, SCALE_BLOCK, o)
-    amax = blocks.abs().amax(dim=1)      # (t/128, o)
-    s = e8m0_exponent_for_block(amax)    # (t/128, o) uint8
+    assert t % block == 0, "token count must be a multiple of the scale block"
+    blocks = xf.reshape(t // block, block, o)
+    amax = blocks.abs().amax(dim=1)      # (t/block, o)
+    s = e8m0_exponent_for_block(amax)    # (t/block, o) uint8
     scale = torch.exp2(s.to(torch.float32) - E8M0_BIAS)
     q = (blocks / scale[:, None, :]).reshape(t, o).to(torch.float8_e4m3fn).view(torch.uint8)
     if token_axis == 1:
         q = q.t()
     return q.contiguous(), s.contiguous()
+
+
+def pack_scale_words(s: torch.Tensor) -> torch.Tensor:
+    """(nblocks, mn) uint8 scale bytes -> (ceil(nblocks/4), mn) int32 words, four consecutive
+    blocks per little-endian word (block 4w + j in byte j), zero bytes past the last block."""
+    nb, mn = s.shape
+    nw = (nb + 3) // 4
+    padded = torch.zeros((4 * nw, mn), dtype=torch.uint8, device=s.device)
+    padded[:nb] = s
+    return padded.reshape(nw, 4, mn).permute(0, 2, 1).contiguous().view(torch.int32).reshape(nw, mn)
 
 
 # ----------------------------------------------------------------------------
@@ -169,10 +179,11 @@ class Workload:
     accumulate: bool
     A: torch.Tensor = None        # bf16 (hidden, T) or uint8 e4m3 bytes
     B: torch.Tensor = None        # bf16 (T, n) or uint8 e4m3 bytes
-    sfa: Optional[torch.Tensor] = None   # uint8 (T/128, hidden)
-    sfb: Optional[torch.Tensor] = None   # uint8 (T/128, n)
+    sfa: Optional[torch.Tensor] = None   # uint8 (T/scale_block, hidden)
+    sfb: Optional[torch.Tensor] = None   # uint8 (T/scale_block, n)
     C0: Optional[torch.Tensor] = None    # initial output for accumulate mode
     offsets: torch.Tensor = None         # int32 (E,)
+    scale_block: int = SCALE_BLOCK       # tokens per fp8 scale (128, or 32 for MX-style blocks)
     meta: Dict = field(default_factory=dict)
 
     @property
@@ -219,18 +230,20 @@ def config_spec(name: str, seed: int = 1) -> Dict:
 
 def make_operands(counts: List[int], hidden: int, n: int, kind: str, out_dtype: torch.dtype,
                   accumulate: bool, seed: int, device="cpu", std: float = 1.0,
-                  integer_range: Optional[int] = None, name: str = "custom") -> Workload:
+                  integer_range: Optional[int] = None, name: str = "custom",
+                  scale_block: int = SCALE_BLOCK) -> Workload:
     """Build a Workload with tensors on `device`.
 
     Draw order from one generator seeded with `seed`: A, then B, then the
     initial output C0 (accumulate mode only).  With `integer_range=r` the
     operands hold integers in [-r, r] instead of normals (for fp8 the integers
-    are stored exactly as e4m3 values with unit scales).
+    are stored exactly as e4m3 values with unit scales).  fp8 operands get one
+    scale per `scale_block` tokens.
     """
     T = int(sum(counts))
     g = _gen(seed, device)
     wl = Workload(name=name, counts=list(map(int, counts)), hidden=hidden, n=n, kind=kind,
-                  out_dtype=out_dtype, accumulate=accumulate)
+                  out_dtype=out_dtype, accumulate=accumulate, scale_block=scale_block)
     if integer_range is None:
         A = randn_bf16((hidden, T), std, g, device)
         B = randn_bf16((T, n), std, g, device)
@@ -241,13 +254,13 @@ def make_operands(counts: List[int], hidden: int, n: int, kind: str, out_dtype: 
         wl.A, wl.B = A, B
     elif kind == "fp8":
         if integer_range is None:
-            wl.A, wl.sfa = quantize_token_blocks(A, token_axis=1)
-            wl.B, wl.sfb = quantize_token_blocks(B, token_axis=0)
+            wl.A, wl.sfa = quantize_token_blocks(A, token_axis=1, block=scale_block)
+            wl.B, wl.sfb = quantize_token_blocks(B, token_axis=0, block=scale_block)
         else:
             wl.A = A.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
             wl.B = B.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
-            wl.sfa = torch.full((T // SCALE_BLOCK, hidden), E8M0_BIAS, dtype=torch.uint8, device=device)
-            wl.sfb = torch.full((T // SCALE_BLOCK, n), E8M0_BIAS, dtype=torch.uint8, device=device)
+            wl.sfa = torch.full((T // scale_block, hidden), E8M0_BIAS, dtype=torch.uint8, device=device)
+            wl.sfb = torch.full((T // scale_block, n), E8M0_BIAS, dtype=torch.uint8, device=device)
         del A, B
     else:
         raise ValueError(kind)
