@@ -18,7 +18,14 @@ and is null when the kernel sources changed after those counters were taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `secondary` reports the other workloads (the 32-expert skewed-accumulate,
 fp8 and many-small-expert configs, and the tiny one) with the same timing,
-and the on-device fp8 quantiser on the fp8 workload's operand shapes.
+the fp8 workload with 32-token (MX-style) packed scales, and the on-device
+fp8 quantiser on the fp8 workload's operand shapes.
+
+Warm-up: from idle the GPU needs about 100 ms of continuous load before its
+clocks settle (the first launches of the headline run ~15% slower than the
+steady state), so the default warm-up is 400 steps (about 0.2 s) and the
+secondary workloads warm up for at least 0.2 s each.  The numbers are
+steady-state throughput, as in a training loop.
 """
 from __future__ import annotations
 
@@ -87,16 +94,27 @@ def make_call(wl, out, native=False):
     import grouped_gemm_expert_offsets_amd as kgw
     if wl.kind == "bf16":
         return lambda: kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=wl.accumulate)
+    if wl.scale_block == 32:
+        import workloads
+        sfa, sfb = workloads.pack_scale_words(wl.sfa), workloads.pack_scale_words(wl.sfb)
+        return lambda: kgw.kgw_wgrad_fp8_ex(wl.A, sfa, wl.B, sfb, wl.offsets, scale_format=kgw.KGW_SCALES_PACKED_32,
+                                            native=native, out=out, accumulate=wl.accumulate)
     fn = kgw.kgw_wgrad_fp8_native if native else kgw.kgw_wgrad_fp8
     return lambda: fn(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, accumulate=wl.accumulate)
 
 
-def time_call(call, steps: int, warmup: int):
-    """Wall time of `steps` back-to-back calls plus HIP-event time of each launch."""
+def time_call(call, steps: int, warmup: int, min_warm_s: float = 0.0):
+    """Wall time of `steps` back-to-back calls plus HIP-event time of each launch, after
+    `warmup` untimed calls (continued until `min_warm_s` seconds have passed, if given)."""
     import torch
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -111,17 +129,23 @@ def time_call(call, steps: int, warmup: int):
     return wall_ms / steps, launch_ms
 
 
-def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1):
+def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1, min_warm_s: float = 0.0,
+                 scale_block: int = 128):
     import torch
     import workloads
-    wl = workloads.make_workload(name, seed=seed, device="cuda")
+    if scale_block == 128:
+        wl = workloads.make_workload(name, seed=seed, device="cuda")
+    else:
+        spec = workloads.config_spec(name, seed)
+        std = spec.pop("std")
+        wl = workloads.make_operands(seed=seed, device="cuda", std=std, name=name, scale_block=scale_block, **spec)
     out = wl.C0 if wl.accumulate else torch.empty((wl.num_experts, wl.hidden, wl.n), dtype=wl.out_dtype,
                                                   device="cuda")
-    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup)
+    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup, min_warm_s)
     launch_ms.sort()
     mean_launch = sum(launch_ms) / len(launch_ms)
     res = {
-        "workload": name + ("_native" if native else ""),
+        "workload": name + ("_mx32" if scale_block == 32 else "") + ("_native" if native else ""),
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "launch_ms_median": launch_ms[len(launch_ms) // 2],
@@ -140,7 +164,7 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
     return res
 
 
-def run_quantize(token_axis: int, steps: int, warmup: int):
+def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0.0):
     """kgw_quantize_fp8 on the fp8 workload's bf16 operand shape (A: (hidden, tokens_sum),
     token_axis 1; B: (tokens_sum, n), token_axis 0).  HBM-bound: 2 bytes read and 1 written per
     element plus one scale byte per 128."""
@@ -152,7 +176,7 @@ def run_quantize(token_axis: int, steps: int, warmup: int):
     shape = (H, T) if token_axis else (T, N)
     g = torch.Generator(device="cuda").manual_seed(1)
     x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
-    ms_step, launch_ms = time_call(lambda: kgw.kgw_quantize_fp8(x, token_axis), steps, warmup)
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_quantize_fp8(x, token_axis), steps, warmup, min_warm_s)
     mean_launch = sum(launch_ms) / len(launch_ms)
     nbytes = 3.0 * x.numel() + x.numel() / 128
     res = {
@@ -229,8 +253,9 @@ def copy_calibration(gib: float = 1.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--secondary-warm-seconds", type=float, default=0.2)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--native-fp8", action="store_true", help="time kgw_wgrad_fp8_native for fp8 workloads")
     ap.add_argument("--no-secondary", action="store_true")
@@ -308,14 +333,17 @@ def main():
     }
     if not args.no_secondary:
         sec = []
-        for name, native in (("tiny", False), ("skewed", False), ("fp8", False), ("fp8", True),
-                             ("many_small", False)):
+        sec_steps, sec_warm = max(5, args.steps // 10), 2
+        for name, native, block in (("tiny", False, 128), ("skewed", False, 128), ("fp8", False, 128),
+                                    ("fp8", True, 128), ("fp8", False, 32), ("fp8", True, 32),
+                                    ("many_small", False, 128)):
             if name == args.workload:
                 continue
-            r = run_workload(name, max(5, args.steps // 2), max(2, args.warmup // 2), native=native)
+            r = run_workload(name, sec_steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
+                             scale_block=block)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         for axis in (1, 0):
-            r = run_quantize(axis, max(5, args.steps // 2), max(2, args.warmup // 2))
+            r = run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         line["secondary"] = sec
     if not args.no_cpu_baseline:

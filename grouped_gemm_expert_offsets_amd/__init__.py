@@ -25,11 +25,13 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_quantize_fp8", "kgw_workspace_bytes",
+    "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
+    "kgw_quantize_fp8", "kgw_workspace_bytes",
     "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
     "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16", "KGW_OUT_FP16",
+    "KGW_SCALES_U8", "KGW_SCALES_PACKED", "KGW_SCALES_PACKED_32", "scale_shape",
     "BF16_TOKEN_ALIGN", "FP8_TOKEN_ALIGN", "library_path", "load_library",
 ]
 
@@ -42,6 +44,9 @@ KGW_ERROR_DEVICE = 5
 KGW_OUT_FP32 = 0
 KGW_OUT_BF16 = 1
 KGW_OUT_FP16 = 2
+KGW_SCALES_U8 = 0          # uint8 (tokens/128, mn)
+KGW_SCALES_PACKED = 1      # int32 (ceil(tokens/512), mn): four 128-token blocks per word
+KGW_SCALES_PACKED_32 = 2   # int32 (tokens/128, mn): four 32-token blocks per word
 BF16_TOKEN_ALIGN = 256
 FP8_TOKEN_ALIGN = 128
 
@@ -50,8 +55,8 @@ library_path = os.path.join(_HERE, "libkgw.so")
 _lib = None
 
 # Every symbol include/kgw.h declares.
-EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_quantize_fp8",
-                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
+EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
+                    "kgw_wgrad_fp8_ex", "kgw_quantize_fp8", "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
                     "kgw_device_info")
 
 
@@ -71,8 +76,12 @@ def load_library():
     lib.kgw_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_native.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_native.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_bf16_ex.restype = ctypes.c_int
+    lib.kgw_wgrad_bf16_ex.argtypes = [p, p, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_fp8_ex.restype = ctypes.c_int
+    lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
-    lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, p, p, p]
+    lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, i32, p, p, p]
     lib.kgw_workspace_bytes.restype = sz
     lib.kgw_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.kgw_validate_offsets_host.restype = ctypes.c_int
@@ -144,6 +153,24 @@ def _prepare_out(out, E, hidden, n, out_dtype, accumulate, device):
     return out
 
 
+def _prepare_outs(outs, E, hidden, n, out_dtype, device, stream):
+    """Per-expert outputs -> (list, device int64 array of their addresses, 0 for None)."""
+    outs = list(outs)
+    if len(outs) != E:
+        raise ValueError(f"need one output (or None) per expert: {E}, got {len(outs)}")
+    for t in outs:
+        if t is None:
+            continue
+        if tuple(t.shape) != (hidden, n) or t.dtype != out_dtype or t.device != device or not t.is_contiguous():
+            raise ValueError(f"each output must be a contiguous {(hidden, n)} {out_dtype} tensor on {device}")
+    addrs = torch.tensor([0 if t is None else int(t.data_ptr()) for t in outs], dtype=torch.int64)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    with torch.cuda.stream(s):
+        ptrs = addrs.to(device)
+    ptrs.record_stream(s)
+    return outs, ptrs
+
+
 def _check_offsets(offsets: torch.Tensor, device):
     if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
         raise ValueError("offsets must be a contiguous 1-D int32 tensor")
@@ -188,6 +215,53 @@ def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out:
     return out
 
 
+def kgw_wgrad_bf16_ex(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                      outs=None, out_dtype: torch.dtype = torch.float32, accumulate: bool = False,
+                      validate: bool = False, stream=None, split_k: bool = True):
+    """kgw_wgrad_bf16 with discrete outputs: `outs` is a list of num_experts (hidden, n) tensors
+    (None skips that expert) whose addresses go to the device as the pointer array; returns
+    `outs`.  With `out` instead it behaves like kgw_wgrad_bf16."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("kgw_wgrad_bf16_ex takes bfloat16 A and B")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (A token-contiguous, B row-major)")
+    device = A.device
+    if B.device != device:
+        raise ValueError("A and B must be on the same device")
+    _check_offsets(offsets, device)
+    hidden, T = A.shape
+    n = B.shape[1]
+    E = offsets.numel()
+    out, outs, ptrs, code = _outputs(out, outs, E, hidden, n, out_dtype, accumulate, device, stream)
+    if validate:
+        kgw_validate_offsets(offsets, T, BF16_TOKEN_ALIGN, stream=stream)
+    ws, ws_bytes = _workspace(E, hidden, n, T, False, device, stream, split_k)
+    st = load_library().kgw_wgrad_bf16_ex(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), _ptr(ptrs),
+                                          code, int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
+    _check(st, "kgw_wgrad_bf16_ex")
+    return out if outs is None else outs
+
+
+def _outputs(out, outs, E, hidden, n, out_dtype, accumulate, device, stream):
+    """Resolve the dense / discrete output forms: (out, outs, pointer array, dtype code)."""
+    if out is not None and outs is not None:
+        raise ValueError("pass either out or outs, not both")
+    if outs is not None:
+        outs = list(outs)
+        given = [t for t in outs if t is not None]
+        if given:
+            out_dtype = given[0].dtype
+        code = _out_code(out_dtype)
+        outs, ptrs = _prepare_outs(outs, E, hidden, n, out_dtype, device, stream)
+        return None, outs, ptrs, code
+    if out is not None:
+        out_dtype = out.dtype
+    code = _out_code(out_dtype)
+    return _prepare_out(out, E, hidden, n, out_dtype, accumulate, device), None, None, code
+
+
 def kgw_wgrad_fp8(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
                   out: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.bfloat16,
                   accumulate: bool = False, validate: bool = False, stream=None, split_k: bool = True) -> torch.Tensor:
@@ -205,20 +279,44 @@ def kgw_wgrad_fp8_native(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sf
                      stream, split_k)
 
 
-def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream, split_k):
+def kgw_wgrad_fp8_ex(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor,
+                     offsets: torch.Tensor, *, scale_format: int = KGW_SCALES_U8, native: bool = False,
+                     out: Optional[torch.Tensor] = None, outs=None, out_dtype: torch.dtype = torch.bfloat16,
+                     accumulate: bool = False, validate: bool = False, stream=None, split_k: bool = True):
+    """fp8 product with a scale layout (KGW_SCALES_*: uint8 per 128 tokens, packed int32 words of
+    four 128-token blocks, or packed words of four 32-token blocks) and a dense `out` or discrete
+    `outs` (see kgw_wgrad_bf16_ex); native=True uses the scaled fp8 MFMA."""
+    return _fp8_call("kgw_wgrad_fp8_ex", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream,
+                     split_k, scale_format=scale_format, native=native, outs=outs)
+
+
+def scale_shape(tokens: int, mn: int, scale_format: int) -> Tuple[Tuple[int, int], torch.dtype]:
+    """Shape and dtype of the scale tensor of an operand with `tokens` tokens and mn other extent."""
+    if scale_format == KGW_SCALES_U8:
+        return (tokens // FP8_TOKEN_ALIGN, mn), torch.uint8
+    if scale_format == KGW_SCALES_PACKED:
+        return ((tokens // FP8_TOKEN_ALIGN + 3) // 4, mn), torch.int32
+    if scale_format == KGW_SCALES_PACKED_32:
+        return (tokens // FP8_TOKEN_ALIGN, mn), torch.int32
+    raise ValueError(f"unknown scale_format {scale_format}")
+
+
+def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream, split_k,
+              scale_format=KGW_SCALES_U8, native=None, outs=None):
     fp8_types = (torch.uint8, torch.float8_e4m3fn)
     if A.dtype not in fp8_types or B.dtype not in fp8_types:
         raise ValueError(f"{name} takes e4m3fn (or raw uint8) A and B")
     if sfa is None or sfb is None:
         raise ValueError(f"{name} needs both scale tensors sfa and sfb")
-    if sfa.dtype != torch.uint8 or sfb.dtype != torch.uint8:
-        raise ValueError("sfa and sfb hold UE8M0 exponent bytes (uint8)")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
     hidden, T = A.shape
     n = B.shape[1]
-    if tuple(sfa.shape) != (T // FP8_TOKEN_ALIGN, hidden) or tuple(sfb.shape) != (T // FP8_TOKEN_ALIGN, n):
-        raise ValueError(f"scale shapes must be {(T // FP8_TOKEN_ALIGN, hidden)} and {(T // FP8_TOKEN_ALIGN, n)}")
+    (sa_shape, sdtype), (sb_shape, _) = scale_shape(T, hidden, scale_format), scale_shape(T, n, scale_format)
+    if sfa.dtype != sdtype or sfb.dtype != sdtype:
+        raise ValueError(f"this scale format takes {sdtype} scale tensors")
+    if tuple(sfa.shape) != sa_shape or tuple(sfb.shape) != sb_shape:
+        raise ValueError(f"scale shapes must be {sa_shape} and {sb_shape}")
     for t in (A, B, sfa, sfb):
         if not t.is_contiguous():
             raise ValueError("fp8 operands and scales must be contiguous")
@@ -227,25 +325,29 @@ def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validat
         raise ValueError("operands and scales must be on the same device")
     _check_offsets(offsets, device)
     E = offsets.numel()
-    if out is not None:
-        out_dtype = out.dtype
-    code = _out_code(out_dtype)
-    out = _prepare_out(out, E, hidden, n, out_dtype, accumulate, device)
+    out, outs, ptrs, code = _outputs(out, outs, E, hidden, n, out_dtype, accumulate, device, stream)
     if validate:
         kgw_validate_offsets(offsets, T, FP8_TOKEN_ALIGN, stream=stream)
     fn = getattr(load_library(), name)
     ws, ws_bytes = _workspace(E, hidden, n, T, True, device, stream, split_k)
-    st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
-            int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
+    if native is None:
+        st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
+                int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
+    else:
+        st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), int(scale_format), int(bool(native)), _ptr(offsets), E,
+                hidden, n, T, _ptr(out), _ptr(ptrs), code, int(bool(accumulate)), _ptr(ws), ws_bytes,
+                _stream_ptr(stream))
     _check(st, name)
-    return out
+    return out if outs is None else outs
 
 
-def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """bf16 x (rows, cols) -> (e4m3fn bytes as uint8 (rows, cols), UE8M0 scale bytes).
+def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None,
+                     scale_format: int = KGW_SCALES_U8) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 x (rows, cols) -> (e4m3fn bytes as uint8 (rows, cols), UE8M0 scales in `scale_format`).
 
-    token_axis 1: tokens along the columns (A (hidden, tokens)), scales (cols/128, rows);
-    token_axis 0: tokens along the rows (B (tokens, n)), scales (rows/128, cols).
+    token_axis 1: tokens along the columns (A (hidden, tokens)), scales with mn = rows;
+    token_axis 0: tokens along the rows (B (tokens, n)), scales with mn = cols.  See
+    scale_shape for the scale tensor of each format.
     """
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("kgw_quantize_fp8 takes a contiguous 2-D bfloat16 tensor")
@@ -255,9 +357,10 @@ def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None) -> Tuple[tor
     tokens, other = (cols, rows) if token_axis else (rows, cols)
     if tokens % FP8_TOKEN_ALIGN != 0:
         raise ValueError(f"the token length ({tokens}) must be a multiple of {FP8_TOKEN_ALIGN}")
+    shape, sdtype = scale_shape(tokens, other, scale_format)
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    s = torch.empty((tokens // FP8_TOKEN_ALIGN, other), dtype=torch.uint8, device=x.device)
-    st = load_library().kgw_quantize_fp8(_ptr(x), rows, cols, int(token_axis), _ptr(q), _ptr(s),
+    s = torch.empty(shape, dtype=sdtype, device=x.device)
+    st = load_library().kgw_quantize_fp8(_ptr(x), rows, cols, int(token_axis), int(scale_format), _ptr(q), _ptr(s),
                                          _stream_ptr(stream))
     _check(st, "kgw_quantize_fp8")
     return q, s

@@ -114,6 +114,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         const int e = ec / p.split;
         const int c = ec - e * p.split;
         const int eo = c * p.num_experts + e;
+        if (p.out_ptrs && !p.out_ptrs[eo]) continue;     // the caller wants no output for this expert
         int tm, tn;
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;

@@ -60,6 +60,18 @@ __device__ __forceinline__ void dma_16B(i32x4 rsrc, uint32_t voff, uint32_t lds_
                  :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
 }
 
+// Narrow direct loads to LDS: every lane fetches the byte (dma_1B, zero-extended)
+// or the dword (dma_4B) at `voff` of the buffer, and lane L's value lands as the
+// dword at `lds_dst` + 4 * L.  Same ordering rules as dma_16B.
+__device__ __forceinline__ void dma_1B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
+}
+__device__ __forceinline__ void dma_4B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
+}
+
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left unconstrained); gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -90,6 +102,9 @@ __device__ __forceinline__ i32x4 lds_load_16B(const lds_char* base, uint32_t off
 }
 __device__ __forceinline__ i32x2 lds_load_8B(const lds_char* base, uint32_t off) {
     return *reinterpret_cast<const __attribute__((address_space(3))) i32x2*>(base + off);
+}
+__device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
 }
 
 // Transposing LDS reads (gfx950).  Within each group of 16 lanes, lane 4b+c

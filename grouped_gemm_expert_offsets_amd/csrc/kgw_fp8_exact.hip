@@ -1,11 +1,13 @@
 // Persistent K-grouped weight-gradient kernel, OCP e4m3 operands with one UE8M0
-// scale per 128 tokens, fp32 accumulation on the bf16 MFMA (gfx950).  This is
-// the kernel behind kgw_wgrad_fp8.
+// scale per 128 tokens (or per 32 tokens, MX), fp32 accumulation on the bf16
+// MFMA (gfx950).  This is the kernel behind kgw_wgrad_fp8.
 //
 // Same operation and work decomposition as the bf16 kernel (cuDNN "Grouped GEMM
 // + WGrad (Unified)", section "Operation"); the operands are fp8 with per-block
 // 1x128 power-of-two scales (llm-infra-atlas "05 Grouped GEMM", section 3),
-// the blocks running along the contracted token axis.
+// the blocks running along the contracted token axis.  The MX instantiation
+// takes one scale per 32 tokens instead (the DeepGEMM k-grouped page's
+// gran_k = 32), packed four to a word: one word per row per 128-token stage.
 //
 // The fp8 bytes travel from HBM to LDS as fp8 (half the bytes of bf16).  Each
 // MFMA operand fragment -- eight tokens of one output row m (from A) or one
@@ -19,7 +21,8 @@
 // Loads and LDS layout are those of the native fp8 kernel (both kernels move
 // the same bytes): A in 128-token stages (256 rows x 128 B, one scale block)
 // in a 3-slot ring, B in 64-token stages (64 rows x 256 B) in a 3-slot ring,
-// the block's scale bytes by byte-wide direct loads into a 3-slot scale ring,
+// the block's scale bytes by byte-wide direct loads (the MX scale words by
+// dword-wide ones) into a 3-slot scale ring,
 // ten direct loads per wave per 64-token step spread over its MFMAs, one
 // barrier per step.  Inside a step the wave runs four 16-token groups of 16
 // bf16 MFMAs (32x32x16; 4 waves, each 128x128 of the 256x256 tile):
@@ -58,19 +61,9 @@ static_assert(BM == 256 && BN == 256 && kFp8BK == 2 * KS, "index math below assu
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
 static_assert(2 * 128 * 512 <= SC_RING, "output staging must fit below the scale ring");
 
-// Direct byte load to LDS: every lane fetches the byte at `voff` of the buffer;
-// lane L's byte lands zero-extended in the dword at `lds_dst` + 4 * L.
-__device__ __forceinline__ void dma_1B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
-}
-
-__device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
-}
-
-template <int OUT>
+template <int OUT, int FMT>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
+    constexpr bool MX = FMT == kScalesPacked32;           // one scale per 32 tokens
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
     const uint32_t tiles_addr = lds_addr(smem);
@@ -118,6 +111,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         const int e = ec / p.split;
         const int c = ec - e * p.split;
         const int eo = c * p.num_experts + e;
+        if (p.out_ptrs && !p.out_ptrs[eo]) continue;     // the caller wants no output for this expert
         int tm, tn;
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
@@ -144,8 +138,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * T + begin;
         const uint8_t* Bbase = (const uint8_t*)p.B + (int64_t)begin * N + n0;
-        const uint8_t* SAbase = p.sfa + (int64_t)(begin / (2 * KS)) * H;
-        const uint8_t* SBbase = p.sfb + (int64_t)(begin / (2 * KS)) * N;
+        const int64_t gb0 = begin / (2 * KS);          // global index of the item's first 128-token block
         // Rows of A past hidden and columns of B past n belong to outputs that are
         // never stored; the buffer ranges end at the last valid A row and at the
         // end of B, so such lanes read zeros or bytes of B's next row, never
@@ -154,11 +147,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         const int64_t b_bytes = (T - begin) * N - n0;
         const uint32_t a_voff0 = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)T;
         const uint32_t b_voff0 = (uint32_t)(16 * wave + (lane >> 4)) * (uint32_t)N;
-        // Scale bytes: sa for rows m0 + wm*128 + 64h + lane, sb for columns
-        // n0 + wn*128 + 64h + lane (h = 0, 1); bytes past hidden / n read as 0
-        // through the buffer range and belong to rows / columns never stored.
-        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane);
-        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane);
+        // Scales: sa for rows m0 + wm*128 + 64h + lane, sb for columns
+        // n0 + wn*128 + 64h + lane (h = 0, 1), one byte (or, packed, one byte or
+        // word at a 4-byte stride) each; values past hidden / n read as 0 through
+        // the buffer range and belong to rows / columns never stored.
+        constexpr uint32_t sstride = FMT == kScalesU8 ? 1u : 4u;
+        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane) * sstride;
+        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane) * sstride;
 
         // Direct loads, as in the native fp8 kernel: A stage a (steps 2a, 2a+1;
         // scale block a) to A slot a % NA, B step s to B slot s % NB; stages past
@@ -180,9 +175,11 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         auto dma_s = [&](int a, bool b_side, int h) {
             const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((a % NA) * SC_STAGE) +
                                  (b_side ? 512u : 0u) + (uint32_t)h * 256u;
-            const uint8_t* base = b_side ? SBbase + (int64_t)a * N : SAbase + (int64_t)a * H;
-            const uint32_t limit = a < nblocks ? (uint32_t)(b_side ? N : H) : 0u;
-            dma_1B(rsrc_words(base, limit), (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u, dst);
+            const ScaleSource src = scale_source<FMT>(b_side ? p.sfb : p.sfa, b_side ? N : H, gb0 + a);
+            const i32x4 r = rsrc_words(src.base, a < nblocks ? src.limit : 0u);
+            const uint32_t voff = (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u * sstride;
+            if constexpr (MX) dma_4B(r, voff, dst);
+            else dma_1B(r, voff, dst);
         };
         // The loads of step s (also for the prologue's virtual steps s < 0), in
         // issue order: B step s+3, then half of an A stage and two scale loads
@@ -240,11 +237,18 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
                 f.b[m - 4][g] = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * (m - 4))) + (uint32_t)g * 4096u);
             }
         };
-        auto scales_to_float = [&](Raw& f) {
+        // Scales of the 32-token block `sub` (0..3) of the stage (MX), or of the
+        // stage's single block, as fp32 conversion factors.
+        auto scales_to_float = [&](Raw& f, int sub) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                f.fa[x] = e8m0_to_f32((uint32_t)f.sa[x]);
-                f.fb[x] = e8m0_to_f32((uint32_t)f.sb[x]);
+                if constexpr (MX) {
+                    f.fa[x] = e8m0_to_f32(((uint32_t)f.sa[x] >> (8 * sub)) & 0xFFu);
+                    f.fb[x] = e8m0_to_f32(((uint32_t)f.sb[x] >> (8 * sub)) & 0xFFu);
+                } else {
+                    f.fa[x] = e8m0_to_f32((uint32_t)f.sa[x]);
+                    f.fb[x] = e8m0_to_f32((uint32_t)f.sb[x]);
+                }
             }
         };
         // Conversion number c (0..7) of group g: A block c, then B block c-4.
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 #pragma unroll
             for (int m = 0; m < 16; ++m) read_one(0, g, m, r0);
         wait_lgkmcnt0();
-        scales_to_float(r0);
+        scales_to_float(r0, 0);
 #pragma unroll
         for (int c = 0; c < 8; ++c) convert_one(r0, 0, c, c0);
 
@@ -289,7 +293,10 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         // when k%6 == 2, read (g, m) of step s+1 (group g's raw fragments, and
         // the scales in group 0), and every other MFMA one conversion for the
         // next group (group 0 of step s+1 during group 3, once its reads and
-        // scales are in).  sched_barrier(0) pins the interleaving.
+        // scales are in).  With 32-token scales (MX) groups 2g and 2g+1 share
+        // block 2*(s&1) + g of the stage: the factors of `cur` are switched to the
+        // second block before group 1 (whose conversions are group 2's).
+        // sched_barrier(0) pins the interleaving.
         auto body = [&](int s, Raw& cur, Raw& nxt) {
             wait_lgkmcnt0();
             wait_vmcnt<16>();
@@ -299,9 +306,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
             for (int g = 0; g < 4; ++g) {
                 Conv& cv = (g & 1) ? c1 : c0;
                 Conv& cn = (g & 1) ? c0 : c1;
+                if (MX && g == 1) {
+                    scales_to_float(cur, 2 * (s & 1) + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (g == 3) {
                     wait_lgkmcnt0();
-                    scales_to_float(nxt);
+                    scales_to_float(nxt, MX ? 2 * ((s + 1) & 1) : 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
@@ -337,13 +348,20 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 
 }  // namespace
 
-hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+template <int FMT>
+static void launch_exact(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
     if (out_kind == kOutBf16)
-        hipLaunchKernelGGL(wgrad_fp8_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_kernel<kOutBf16, FMT>), dim3(grid), dim3(NT), 0, stream, p);
     else if (out_kind == kOutF16)
-        hipLaunchKernelGGL(wgrad_fp8_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_kernel<kOutF16, FMT>), dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(wgrad_fp8_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_kernel<kOutF32, FMT>), dim3(grid), dim3(NT), 0, stream, p);
+}
+
+hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+    if (p.scale_format == kScalesPacked32) launch_exact<kScalesPacked32>(p, out_kind, grid, stream);
+    else if (p.scale_format == kScalesPacked) launch_exact<kScalesPacked>(p, out_kind, grid, stream);
+    else launch_exact<kScalesU8>(p, out_kind, grid, stream);
     return hipGetLastError();
 }
 

@@ -21,6 +21,14 @@
 // single byte sfb[block][n]: the products are qa*qb*2^(ea-127)*2^(eb-127) with
 // no dequantisation pass.
 //
+// The instruction's K order: lane l of an operand holds K 16*(l>>5) + 0..15 in
+// bytes 0..15 and K 32 + 16*(l>>5) + 0..15 in bytes 16..31, and it applies the
+// scale of lanes 0..31 to K 0..31 and that of lanes 32..63 to K 32..63 (one
+// scale per row / column per 32 K).  The fragment reads below follow that
+// order, so each 32-token half of a step is one hardware scale block: with
+// 32-token scales (the MX instantiation, the DeepGEMM k-grouped page's
+// gran_k = 32, packed four to a word) each lane passes the byte of its half.
+//
 // Pipeline (the bf16 kernel's, in bytes): K step of 64 tokens = 16 MFMAs of
 // 32x32x64 per wave (4 waves, each 128x128 of the 256x256 tile).  Direct
 // global->LDS loads, no register staging:
@@ -65,19 +73,9 @@ static_assert(BM == 256 && BN == 256 && kFp8BK == 2 * KS, "index math below assu
 static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
 static_assert(2 * 128 * 512 <= SC_RING, "output staging must fit below the scale ring");
 
-// Direct byte load to LDS: every lane fetches the byte at `voff` of the buffer;
-// lane L's byte lands zero-extended in the dword at `lds_dst` + 4 * L.
-__device__ __forceinline__ void dma_1B(i32x4 rsrc, uint32_t voff, uint32_t lds_dst) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds_dst) : "memory");
-}
-
-__device__ __forceinline__ int lds_load_4B(const lds_char* base, uint32_t off) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(base + off);
-}
-
-template <int OUT>
+template <int OUT, int FMT>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p) {
+    constexpr bool MX = FMT == kScalesPacked32;           // one scale per 32 tokens
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
     const uint32_t tiles_addr = lds_addr(smem);
@@ -99,16 +97,18 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
     const int b_q0 = (lane & 15) ^ (2 * ((lane >> 4) & 7));
     const int b_q1 = (lane & 15) ^ (2 * ((4 + (lane >> 4)) & 7));
 
-    // Fragment read offsets (fixed per lane).  A: row wm*128 + 32i + l32, the
-    // 32 tokens 32*lhi.. of the step's 64-token half of the stage.  B: lane l
-    // gets column 32j + l32 of the wave's half, tokens 32*lhi + 0..31, from four
-    // 8x16 transposed blocks; block j's offset is block 0's with the 16-byte
-    // chunk index XOR 2j (the unswizzled chunk 8wn + (g16&1) + 2j has no carry).
+    // Fragment read offsets (fixed per lane), in the instruction's K order:
+    // tokens 16*lhi + 0..15 and 32 + 16*lhi + 0..15 of the step.  A: row
+    // wm*128 + 32i + l32, two 16-byte reads (chunks 4*(s&1) + lhi and + 2 of the
+    // stage row).  B: lane l gets column 32j + l32 of the wave's half from four
+    // 8x16 transposed blocks at k-rows 16*lhi + {0, 8, 32, 40}; block j's offset
+    // is block 0's with the 16-byte chunk index XOR 2j (the unswizzled chunk
+    // 8wn + (g16&1) + 2j has no carry).
     const int l32 = lane & 31, lhi = lane >> 5;
     const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u;
     const int a_sw = (l32 >> 1) & 7;
     const int g16 = lane >> 4, i16 = lane & 15;
-    const uint32_t b_frag0 = (uint32_t)(32 * (g16 >> 1) + (i16 >> 1)) * 256u +
+    const uint32_t b_frag0 = (uint32_t)(16 * (g16 >> 1) + (i16 >> 1)) * 256u +
                              (uint32_t)((8 * wn + (g16 & 1)) ^ (2 * (i16 >> 1))) * 16u + (uint32_t)(i16 & 1) * 8u;
     // Scale dwords of this wave: sa row r at 4r, sb column c at 512 + 4c.
     const uint32_t sc_wave = (uint32_t)(SC_RING + wave * SC_WAVE);
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         const int e = ec / p.split;
         const int c = ec - e * p.split;
         const int eo = c * p.num_experts + e;
+        if (p.out_ptrs && !p.out_ptrs[eo]) continue;     // the caller wants no output for this expert
         int tm, tn;
         tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
@@ -152,8 +153,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
 
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * T + begin;
         const uint8_t* Bbase = (const uint8_t*)p.B + (int64_t)begin * N + n0;
-        const uint8_t* SAbase = p.sfa + (int64_t)(begin / (2 * KS)) * H;
-        const uint8_t* SBbase = p.sfb + (int64_t)(begin / (2 * KS)) * N;
+        const int64_t gb0 = begin / (2 * KS);          // global index of the item's first 128-token block
         // Rows of A past hidden and columns of B past n belong to outputs that are
         // never stored; the buffer ranges below end at the last valid A row and at
         // the end of B, so such lanes read zeros or bytes of B's next row, never
@@ -162,11 +162,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         const int64_t b_bytes = (T - begin) * N - n0;
         const uint32_t a_voff0 = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)T;
         const uint32_t b_voff0 = (uint32_t)(16 * wave + (lane >> 4)) * (uint32_t)N;
-        // Scale bytes: sa for rows m0 + wm*128 + 64h + lane, sb for columns
-        // n0 + wn*128 + 64h + lane (h = 0, 1); bytes past hidden / n read as 0
-        // through the buffer range and belong to rows / columns never stored.
-        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane);
-        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane);
+        // Scales: sa for rows m0 + wm*128 + 64h + lane, sb for columns
+        // n0 + wn*128 + 64h + lane (h = 0, 1), one byte (or, packed, one byte or
+        // word at a 4-byte stride) each; values past hidden / n read as 0 through
+        // the buffer range and belong to rows / columns never stored.
+        constexpr uint32_t sstride = FMT == kScalesU8 ? 1u : 4u;
+        const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane) * sstride;
+        const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane) * sstride;
 
         // Direct loads.  A stage a (steps 2a, 2a+1; scale block a) goes to A slot
         // a % NA, B step s to B slot s % NB.  Stages past the expert's range use
@@ -191,9 +193,11 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
         auto dma_s = [&](int a, bool b_side, int h) {
             const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((a % NA) * SC_STAGE) +
                                  (b_side ? 512u : 0u) + (uint32_t)h * 256u;
-            const uint8_t* base = b_side ? SBbase + (int64_t)a * N : SAbase + (int64_t)a * H;
-            const uint32_t limit = a < nblocks ? (uint32_t)(b_side ? N : H) : 0u;
-            dma_1B(rsrc_words(base, limit), (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u, dst);
+            const ScaleSource src = scale_source<FMT>(b_side ? p.sfb : p.sfa, b_side ? N : H, gb0 + a);
+            const i32x4 r = rsrc_words(src.base, a < nblocks ? src.limit : 0u);
+            const uint32_t voff = (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u * sstride;
+            if constexpr (MX) dma_4B(r, voff, dst);
+            else dma_1B(r, voff, dst);
         };
         // The loads of step s (also for the prologue's virtual steps s < 0), in
         // issue order: B step s+3, then half of an A stage and two scale loads
@@ -228,26 +232,31 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
             int sa[4], sb[4];
         };
         // Fragment read number r (0..31) of step s: A halves (8), B pieces (16),
-        // then the block's scale dwords (8).
+        // then the block's scale dwords (8); an MX word is shifted so that byte 0
+        // is the scale of the lane's 32-token half, block 2*(s&1) + lhi of the stage.
         auto read_one = [&](int s, int r, Frags& f) {
             if (r < 8) {
                 const int i = r >> 1, h = r & 1;
                 const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
-                const uint32_t chunk = (uint32_t)(((4 * (s & 1) + 2 * lhi + h) ^ a_sw) << 4);
+                const uint32_t chunk = (uint32_t)(((4 * (s & 1) + lhi + 2 * h) ^ a_sw) << 4);
                 const i32x4 v = lds_load_16B(As, a_frag_row + i * 4096u + chunk);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) f.a[i][4 * h + x] = v[x];
             } else if (r < 24) {
                 const int j = (r - 8) >> 2, q = (r - 8) & 3;
                 const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
-                const i32x2 v = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * j)) + q * 2048u);
+                const i32x2 v = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * j)) + q * 2048u + (q >> 1) * 4096u);
                 f.b[j][2 * q] = v[0];
                 f.b[j][2 * q + 1] = v[1];
             } else {
                 const lds_char* Sc = tiles + sc_wave + ((s >> 1) % NA) * SC_STAGE;
                 const int q = r - 24;
-                if (q < 4) f.sa[q] = lds_load_4B(Sc, (uint32_t)(4 * (32 * q + l32)));
-                else f.sb[q - 4] = lds_load_4B(Sc, (uint32_t)(512 + 4 * (32 * (q - 4) + l32)));
+                int w;
+                if (q < 4) w = lds_load_4B(Sc, (uint32_t)(4 * (32 * q + l32)));
+                else w = lds_load_4B(Sc, (uint32_t)(512 + 4 * (32 * (q - 4) + l32)));
+                if constexpr (MX) w = (int)((uint32_t)w >> (8 * (2 * (s & 1) + lhi)));
+                if (q < 4) f.sa[q] = w;
+                else f.sb[q - 4] = w;
             }
         };
         auto read_all = [&](int s, Frags& f) {
@@ -321,13 +330,20 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_native_kernel(GroupedParams p
 
 }  // namespace
 
-hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+template <int FMT>
+static void launch_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
     if (out_kind == kOutBf16)
-        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_native_kernel<kOutBf16, FMT>), dim3(grid), dim3(NT), 0, stream, p);
     else if (out_kind == kOutF16)
-        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_native_kernel<kOutF16, FMT>), dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(wgrad_fp8_native_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((wgrad_fp8_native_kernel<kOutF32, FMT>), dim3(grid), dim3(NT), 0, stream, p);
+}
+
+hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+    if (p.scale_format == kScalesPacked32) launch_native<kScalesPacked32>(p, out_kind, grid, stream);
+    else if (p.scale_format == kScalesPacked) launch_native<kScalesPacked>(p, out_kind, grid, stream);
+    else launch_native<kScalesU8>(p, out_kind, grid, stream);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Checks shared by both entry points; everything here is pure host logic.
 kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
-                          int64_t hidden, int64_t n, int64_t tokens_sum, const void* out,
+                          int64_t hidden, int64_t n, int64_t tokens_sum, const void* out, void* const* out_ptrs,
                           int32_t out_dtype, int32_t accumulate, int64_t token_align, int64_t n_align,
                           int64_t bm, int64_t bn) {
     if (num_experts < 1 || hidden < 0 || n < 0 || tokens_sum < 0) return KGW_ERROR_INVALID_VALUE;
@@ -55,13 +55,16 @@ kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, 
     if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
     if (!offsets) return KGW_ERROR_INVALID_VALUE;
     const bool has_output = hidden > 0 && n > 0;
-    if (has_output && !out) return KGW_ERROR_INVALID_VALUE;
+    if (out && out_ptrs) return KGW_ERROR_INVALID_VALUE;              // one output form or the other
+    if (has_output && !out && !out_ptrs) return KGW_ERROR_INVALID_VALUE;
     if (tokens_sum > 0 && has_output && (!A || !B)) return KGW_ERROR_INVALID_VALUE;
     if (num_experts > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
     if (tokens_sum > INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    if (hidden >= ((int64_t)1 << 28) || n >= ((int64_t)1 << 28)) return KGW_ERROR_UNSUPPORTED;
     if (tokens_sum % token_align != 0) return KGW_ERROR_BAD_OFFSETS;
     if (n % n_align != 0) return KGW_ERROR_MISALIGNED;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || ((uintptr_t)offsets & 3u))
+    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || ((uintptr_t)offsets & 3u) ||
+        ((uintptr_t)out_ptrs & 7u))
         return KGW_ERROR_MISALIGNED;
     // The kernels address one tile's rows with 32-bit byte offsets.
     if (bm * tokens_sum * 2 >= (int64_t)1 << 32 || 64 * n * 2 >= (int64_t)1 << 31) return KGW_ERROR_UNSUPPORTED;
@@ -105,10 +108,10 @@ SplitPlan split_plan(int32_t num_experts, int64_t hidden, int64_t n, int64_t tok
     return plan;
 }
 
-kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
-                 const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
-                 int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, const void* sfb,
+                 int32_t scale_format, const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                 int64_t tokens_sum, void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
+                 void* workspace, size_t workspace_bytes, void* stream) {
     const bool fp8 = kernel != Kernel::kBf16;
     const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
     const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
@@ -116,10 +119,18 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     const int64_t nalign = fp8 ? 16 : 8;
     static_assert(KGW_OUT_FP32 == kgw::kOutF32 && KGW_OUT_BF16 == kgw::kOutBf16 && KGW_OUT_FP16 == kgw::kOutF16,
                   "output kind codes");
-    kgw_status_t st = check_common(A, B, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
+    static_assert(KGW_SCALES_U8 == kgw::kScalesU8 && KGW_SCALES_PACKED == kgw::kScalesPacked &&
+                      KGW_SCALES_PACKED_32 == kgw::kScalesPacked32,
+                  "scale format codes");
+    kgw_status_t st = check_common(A, B, offsets, num_experts, hidden, n, tokens_sum, out, out_ptrs, out_dtype,
                                    accumulate, talign, nalign, bm, bn);
     if (st != KGW_SUCCESS) return st;
+    if (fp8 && scale_format != KGW_SCALES_U8 && scale_format != KGW_SCALES_PACKED &&
+        scale_format != KGW_SCALES_PACKED_32)
+        return KGW_ERROR_INVALID_VALUE;
     if (fp8 && tokens_sum > 0 && hidden > 0 && n > 0 && (!sfa || !sfb)) return KGW_ERROR_INVALID_VALUE;
+    if (fp8 && scale_format == KGW_SCALES_PACKED_32 && (((uintptr_t)sfa | (uintptr_t)sfb) & 3u))
+        return KGW_ERROR_MISALIGNED;
     if (hidden == 0 || n == 0) return KGW_SUCCESS;                 // no output elements
     if (accumulate && tokens_sum == 0) return KGW_SUCCESS;         // adds nothing
 
@@ -131,10 +142,12 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     kgw::GroupedParams p;
     p.A = A;
     p.B = B;
-    p.sfa = sfa;
-    p.sfb = sfb;
+    p.sfa = (const uint8_t*)sfa;
+    p.sfb = (const uint8_t*)sfb;
+    p.scale_format = fp8 ? scale_format : kgw::kScalesU8;
     p.offsets = offsets;
     p.out = out;
+    p.out_ptrs = out_ptrs;
     p.hidden = hidden;
     p.n = n;
     p.tokens_sum = tokens_sum;
@@ -155,6 +168,7 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
         p.split = plan.split;
         p.num_items *= plan.split;
         p.out = workspace;
+        p.out_ptrs = nullptr;
         p.accumulate = 0;
         out_kind = kgw::kOutF32;
     }
@@ -167,7 +181,7 @@ kgw_status_t run(Kernel kernel, const void* A, const uint8_t* sfa, const void* B
     }
     if (err == hipSuccess && split)
         err = kgw::launch_splitk_reduce((const float*)workspace, offsets, num_experts, hidden, n, tokens_sum,
-                                        plan.split, out, out_dtype, accumulate, d.num_cus,
+                                        plan.split, out, out_ptrs, out_dtype, accumulate, d.num_cus,
                                         (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
@@ -179,42 +193,62 @@ extern "C" {
 kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
                             int64_t hidden, int64_t n, int64_t tokens_sum, void* out, int32_t out_dtype,
                             int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
-    return run(Kernel::kBf16, A, nullptr, B, nullptr, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, workspace, workspace_bytes, stream);
+    return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
+               out, nullptr, out_dtype, accumulate, workspace, workspace_bytes, stream);
+}
+
+kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
+                               int64_t hidden, int64_t n, int64_t tokens_sum, void* out, void* const* out_ptrs,
+                               int32_t out_dtype, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
+               out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
 }
 
 kgw_status_t kgw_wgrad_fp8(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
                            const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                            int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    return run(Kernel::kFp8, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, workspace, workspace_bytes, stream);
+    return run(Kernel::kFp8, A, sfa, B, sfb, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum, out,
+               nullptr, out_dtype, accumulate, workspace, workspace_bytes, stream);
 }
 
 kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,
                                   const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                                   int64_t tokens_sum, void* out, int32_t out_dtype, int32_t accumulate,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-    return run(Kernel::kFp8Native, A, sfa, B, sfb, offsets, num_experts, hidden, n, tokens_sum, out, out_dtype,
-               accumulate, workspace, workspace_bytes, stream);
+    return run(Kernel::kFp8Native, A, sfa, B, sfb, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
+               out, nullptr, out_dtype, accumulate, workspace, workspace_bytes, stream);
 }
 
-kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
-                              uint8_t* scales, void* stream) {
+kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, const void* sfb, int32_t scale_format,
+                              int32_t native, const int32_t* offsets, int32_t num_experts, int64_t hidden,
+                              int64_t n, int64_t tokens_sum, void* out, void* const* out_ptrs, int32_t out_dtype,
+                              int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+    if (native != 0 && native != 1) return KGW_ERROR_INVALID_VALUE;
+    return run(native ? Kernel::kFp8Native : Kernel::kFp8, A, sfa, B, sfb, scale_format, offsets, num_experts,
+               hidden, n, tokens_sum, out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
+}
+
+kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                              void* q, void* scales, void* stream) {
     if (token_axis != 0 && token_axis != 1) return KGW_ERROR_INVALID_VALUE;
+    if (scale_format != KGW_SCALES_U8 && scale_format != KGW_SCALES_PACKED && scale_format != KGW_SCALES_PACKED_32)
+        return KGW_ERROR_INVALID_VALUE;
     if (rows < 0 || cols < 0) return KGW_ERROR_INVALID_VALUE;
     const int64_t tokens = token_axis ? cols : rows;
     if (tokens % 128 != 0) return KGW_ERROR_INVALID_VALUE;
     if (rows == 0 || cols == 0) return KGW_SUCCESS;
     if (!x || !q || !scales) return KGW_ERROR_INVALID_VALUE;
     if (cols % 8 != 0 || !aligned16(x) || !aligned16(q)) return KGW_ERROR_MISALIGNED;
-    if (!token_axis && ((uintptr_t)scales & 7u)) return KGW_ERROR_MISALIGNED;
+    if (scale_format == KGW_SCALES_U8 && !token_axis && ((uintptr_t)scales & 7u)) return KGW_ERROR_MISALIGNED;
+    if (scale_format == KGW_SCALES_PACKED_32 && !aligned16(scales)) return KGW_ERROR_MISALIGNED;
     if (rows * cols >= ((int64_t)1 << 40)) return KGW_ERROR_UNSUPPORTED;
     DeviceProps d;
     kgw_status_t st = current_props(&d);
     if (st != KGW_SUCCESS) return st;
     if (!d.is_gfx950) return KGW_ERROR_DEVICE;
-    const hipError_t err = kgw::launch_quantize_fp8(x, rows, cols, token_axis, q, scales, d.num_cus,
+    const hipError_t err = kgw::launch_quantize_fp8(x, rows, cols, token_axis, scale_format, q, scales, d.num_cus,
                                                     (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }

@@ -10,13 +10,22 @@ namespace kgw {
 // token range with scalar loads of the offsets; nothing is sized by it).
 constexpr int kMaxExperts = 65536;
 
+// Scale layouts of the fp8 operands (the values of kgw_scale_format_t).
+//   kScalesU8:       one byte per 128 tokens, (tokens_sum/128, mn) bytes;
+//   kScalesPacked:   128-token blocks, four consecutive blocks per int32 word,
+//                    (ceil(tokens_sum/512), mn) words, block b in byte b%4 of word b/4;
+//   kScalesPacked32: 32-token blocks packed the same way: one word per 128 tokens,
+//                    (tokens_sum/128, mn) words.
+constexpr int kScalesU8 = 0, kScalesPacked = 1, kScalesPacked32 = 2;
+
 struct GroupedParams {
     const void* A;          // (hidden, tokens_sum), token axis contiguous
     const void* B;          // (tokens_sum, n), row-major
-    const uint8_t* sfa;     // fp8 only: (tokens_sum/128, hidden) UE8M0 bytes
-    const uint8_t* sfb;     // fp8 only: (tokens_sum/128, n) UE8M0 bytes
+    const uint8_t* sfa;     // fp8 only: UE8M0 scales of A, layout scale_format, mn = hidden
+    const uint8_t* sfb;     // fp8 only: UE8M0 scales of B, layout scale_format, mn = n
     const int32_t* offsets; // (num_experts,) inclusive cumulative token counts
-    void* out;              // (num_experts, hidden, n) fp32, bf16 or fp16
+    void* out;              // (num_experts, hidden, n) fp32, bf16 or fp16 (when out_ptrs is NULL)
+    void* const* out_ptrs;  // or: per-expert (hidden, n) outputs; a NULL entry skips its expert
     int64_t hidden;
     int64_t n;
     int64_t tokens_sum;
@@ -27,7 +36,24 @@ struct GroupedParams {
     int32_t accumulate;     // 1: out += W, 0: out = W
     int32_t num_xcds;       // XCD count used to remap workgroup ids
     int32_t split;          // K chunks per expert: 1, or > 1 for split-K partials
+    int32_t scale_format;   // fp8 only: kScalesU8, kScalesPacked or kScalesPacked32
 };
+
+// Scales of the global 128-token block gb in layout FMT: the value for mn
+// index i is the byte (kScalesU8, kScalesPacked) or the word of four 32-token
+// scales (kScalesPacked32) at base + i * stride, stride 1 or 4 bytes; the first
+// `limit` bytes from base are valid, so a buffer range of that size reads zero
+// for i >= mn.
+struct ScaleSource {
+    const uint8_t* base;
+    uint32_t limit;
+};
+template <int FMT>
+__device__ __forceinline__ ScaleSource scale_source(const uint8_t* sf, int64_t mn, int64_t gb) {
+    if constexpr (FMT == kScalesU8) return {sf + gb * mn, (uint32_t)mn};
+    else if constexpr (FMT == kScalesPacked) return {sf + (gb >> 2) * 4 * mn + (gb & 3), (uint32_t)(4 * mn - (gb & 3))};
+    else return {sf + gb * 4 * mn, (uint32_t)(4 * mn)};
+}
 
 // Split-K chunks start on multiples of this many tokens (a multiple of both
 // token alignments, so no chunk splits a 128-token fp8 scale block).
@@ -41,11 +67,11 @@ hipError_t launch_wgrad_bf16(const GroupedParams& p, int out_kind, int grid, hip
 // Split-K second pass: out[e] (=|+=) the sum over c = 0..split-1, in order, of the fp32
 // partial slabs ws[c*E + e]; in accumulate mode an expert without tokens is left as is.
 hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t num_experts, int64_t hidden,
-                                int64_t n, int64_t tokens_sum, int32_t split, void* out, int out_kind,
-                                int32_t accumulate, int num_cus, hipStream_t stream);
+                                int64_t n, int64_t tokens_sum, int32_t split, void* out, void* const* out_ptrs,
+                                int out_kind, int32_t accumulate, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
-hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
-                               uint8_t* s, int num_cus, hipStream_t stream);
+hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                               void* q, void* s, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

@@ -2,7 +2,10 @@
 // scale byte per 128 tokens, the operand format the fp8 weight-gradient
 // kernels consume (llm-infra-atlas "05 Grouped GEMM", section 3: 1x128
 // blocks, power-of-two UE8M0 scales; for the k-grouped weight gradient the
-// blocks run along the contracted token axis, section 5.2).
+// blocks run along the contracted token axis, section 5.2).  The scales come
+// out as bytes (mn-major), packed four consecutive blocks to a little-endian
+// word, or -- with one scale per 32 tokens, the DeepGEMM k-grouped page's
+// gran_k = 32 -- as one packed word per 128 tokens.
 //
 // Per block: amax = the largest |x|; the scale is the smallest power of two
 // 2^k with amax <= 448 * 2^k (448 = largest e4m3fn), stored as the biased
@@ -18,8 +21,9 @@
 //     block maximum is reduced across the 8 lanes; 16-byte stores;
 //   - tokens along the rows (B, (tokens, n)): a wave holds a 128-row x 64-column
 //     block in registers (lane: 8 columns of 16 rows, each load 8 rows x 128
-//     bytes), reduces each column over its 16 rows and then across the 8 lanes
-//     that share the column, and stores from registers.
+//     bytes), reduces each column over its 16 rows (four 32-row sub-blocks
+//     of 4 rows each for 32-token scales) and then across the 8 lanes that
+//     share the column, and stores from registers.
 #include "kgw_device.h"
 #include "kgw_internal.h"
 
@@ -58,20 +62,41 @@ __device__ __forceinline__ int cvt4(float a, float b, float c, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
 }
 
-// tokens along the columns: x (rows, cols), q same layout, s (cols/128, rows).
-// Lane l: tokens 16l .. 16l+15 of the wave's 1024 (two 16-byte loads, one
-// 16-byte store); 8 lanes make one 128-token block.
+// Store the scale of 128-token block b (of nb) for mn index o (of mn) in layout FMT
+// (kScalesU8 or kScalesPacked); the lane that stores a packed word's last block
+// also zeroes the word's unused bytes.
+template <int FMT>
+__device__ __forceinline__ void store_scale_byte(uint8_t* s, int64_t b, int64_t nb, int64_t o, int64_t mn,
+                                                 uint32_t e) {
+    if constexpr (FMT == kScalesU8) {
+        s[b * mn + o] = (uint8_t)e;
+    } else {
+        uint8_t* w = s + (b >> 2) * 4 * mn + 4 * o;
+        w[b & 3] = (uint8_t)e;
+        if (b == nb - 1)
+            for (int64_t j = (b & 3) + 1; j < 4; ++j) w[j] = 0;
+    }
+}
+
+// tokens along the columns: x (rows, cols), q same layout, scales in layout FMT
+// with mn = rows.  Lane l: tokens 16l .. 16l+15 of the wave's 1024 (two 16-byte
+// loads, one 16-byte store); 8 lanes make one 128-token block, 2 lanes one
+// 32-token block (kScalesPacked32, whose word for a 128-token group is
+// assembled from the four pairs and stored by the group's first lane).
+template <int FMT>
 __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* x, int64_t rows, int64_t cols,
                                                           uint8_t* q, uint8_t* s) {
+    constexpr int RED = FMT == kScalesPacked32 ? 2 : 8;   // lanes per scale block
     const int lane = threadIdx.x & 63;
     const int64_t chunks = (cols + 1023) / 1024;         // 1024 tokens (eight blocks) per wave step
     const int64_t units = rows * chunks;
+    const int64_t nb = cols / 128;
     const int64_t wave0 = (int64_t)blockIdx.x * NWAVE + (threadIdx.x >> 6);
     for (int64_t u = wave0; u < units; u += (int64_t)gridDim.x * NWAVE) {
         const int64_t r = u / chunks;
         const int64_t c = u - r * chunks;
         const int64_t t0 = c * 1024 + 16 * lane;        // this lane's first token
-        const bool active = t0 < cols;                   // cols is a multiple of 128
+        const bool active = t0 < cols;                   // cols is a multiple of 128: whole 8-lane groups
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = 0.0f;
@@ -93,14 +118,20 @@ __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* x, in
             amax = fmaxf(amax, fabsf(v[i]));
             bad |= not_finite(v[i]) ? 1 : 0;
         }
-        // reduce over the 8 lanes of the block (xor 1, 2, 4 stays in the group)
+        // reduce over the lanes of the block (xor 1, 2, 4 stays in the 8-lane group)
 #pragma unroll
-        for (int m = 1; m < 8; m <<= 1) {
+        for (int m = 1; m < RED; m <<= 1) {
             amax = fmaxf(amax, __shfl_xor(amax, m, 64));
             bad |= __shfl_xor(bad, m, 64);
         }
-        if (!active) continue;
         const uint32_t e = bad ? 255u : e8m0_for_amax(amax);
+        uint32_t word = 0;
+        if constexpr (FMT == kScalesPacked32) {
+            const int g0 = lane & ~7;                     // the 128-token group's first lane
+#pragma unroll
+            for (int j = 0; j < 4; ++j) word |= (uint32_t)__shfl((int)e, g0 + 2 * j, 64) << (8 * j);
+        }
+        if (!active) continue;
         i32x4 out;
         if (bad) {
             out = i32x4{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
@@ -110,17 +141,25 @@ __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* x, in
             for (int h = 0; h < 4; ++h) out[h] = cvt4(v[4 * h] * f, v[4 * h + 1] * f, v[4 * h + 2] * f, v[4 * h + 3] * f);
         }
         *(i32x4*)(q + r * cols + t0) = out;
-        if ((lane & 7) == 0) s[(t0 / 128) * rows + r] = (uint8_t)e;
+        if ((lane & 7) == 0) {
+            if constexpr (FMT == kScalesPacked32) ((uint32_t*)s)[(t0 / 128) * rows + r] = word;
+            else store_scale_byte<FMT>(s, t0 / 128, nb, r, rows, e);
+        }
     }
 }
 
-// tokens along the rows: x (rows, cols), q same layout, s (rows/128, cols).
-// Lane l: columns 8*(l & 7) .. +7 of the wave's 64, rows (l >> 3) + 8*i, i < 16.
+// tokens along the rows: x (rows, cols), q same layout, scales in layout FMT
+// with mn = cols.  Lane l: columns 8*(l & 7) .. +7 of the wave's 64, rows
+// (l >> 3) + 8*i, i < 16, of one 128-row block; with 32-token blocks
+// (kScalesPacked32) rows i = 4k .. 4k+3 of every lane form sub-block k.
+template <int FMT>
 __global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* x, int64_t rows, int64_t cols,
                                                           uint8_t* q, uint8_t* s) {
+    constexpr int NSUB = FMT == kScalesPacked32 ? 4 : 1;  // scale blocks per 128 rows
     const int lane = threadIdx.x & 63;
     const int64_t cchunks = (cols + 63) / 64;
-    const int64_t units = (rows / 128) * cchunks;
+    const int64_t nb = rows / 128;
+    const int64_t units = nb * cchunks;
     const int64_t wave0 = (int64_t)blockIdx.x * NWAVE + (threadIdx.x >> 6);
     const int rsub = lane >> 3;
     for (int64_t u = wave0; u < units; u += (int64_t)gridDim.x * NWAVE) {
@@ -134,54 +173,76 @@ __global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* x, in
             if (active) v[i] = *(const i32x4*)(x + row * cols + n0);
             else v[i] = i32x4{0, 0, 0, 0};
         }
-        // per column (8 per lane): max over this lane's 16 rows, then over the
-        // 8 lanes with the same column group (xor 8, 16, 32)
-        float amax[8];
+        // per column (8 per lane) and sub-block: max over this lane's rows of
+        // the sub-block, then over the 8 lanes with the same column group (xor
+        // 8, 16, 32); bit 8k + j of `bad` flags column j of sub-block k
+        float amax[NSUB][8];
         int bad = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax[j] = 0.0f;
+        for (int k = 0; k < NSUB; ++k)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 8; ++j) amax[k][j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = i / (16 / NSUB);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const float a = bf16_lo((uint32_t)v[i][h]), c = bf16_hi((uint32_t)v[i][h]);
-                amax[2 * h] = fmaxf(amax[2 * h], fabsf(a));
-                amax[2 * h + 1] = fmaxf(amax[2 * h + 1], fabsf(c));
-                bad |= (not_finite(a) ? 1 : 0) << (2 * h);
-                bad |= (not_finite(c) ? 1 : 0) << (2 * h + 1);
+                amax[k][2 * h] = fmaxf(amax[k][2 * h], fabsf(a));
+                amax[k][2 * h + 1] = fmaxf(amax[k][2 * h + 1], fabsf(c));
+                bad |= (not_finite(a) ? 1 : 0) << (8 * k + 2 * h);
+                bad |= (not_finite(c) ? 1 : 0) << (8 * k + 2 * h + 1);
             }
+        }
 #pragma unroll
         for (int m = 8; m < 64; m <<= 1) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], m, 64));
+            for (int k = 0; k < NSUB; ++k)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax[k][j] = fmaxf(amax[k][j], __shfl_xor(amax[k][j], m, 64));
             bad |= __shfl_xor(bad, m, 64);
         }
         if (!active) continue;
-        uint32_t e[8];
-        float f[8];
+        uint32_t e[NSUB][8];
+        float f[NSUB][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            e[j] = ((bad >> j) & 1) ? 255u : e8m0_for_amax(amax[j]);
-            f[j] = inv_scale(e[j] == 255u ? 127u : e[j]);
-        }
+        for (int k = 0; k < NSUB; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                e[k][j] = ((bad >> (8 * k + j)) & 1) ? 255u : e8m0_for_amax(amax[k][j]);
+                f[k][j] = inv_scale(e[k][j] == 255u ? 127u : e[k][j]);
+            }
         if (rsub == 0) {
-            const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
-                              (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
-            *(i32x2*)(s + b * cols + n0) = sw;
+            if constexpr (FMT == kScalesU8) {
+                const i32x2 sw = {(int)(e[0][0] | (e[0][1] << 8) | (e[0][2] << 16) | (e[0][3] << 24)),
+                                  (int)(e[0][4] | (e[0][5] << 8) | (e[0][6] << 16) | (e[0][7] << 24))};
+                *(i32x2*)(s + b * cols + n0) = sw;
+            } else if constexpr (FMT == kScalesPacked) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) store_scale_byte<FMT>(s, b, nb, n0 + j, cols, e[0][j]);
+            } else {
+                uint32_t w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) w[j] = e[0][j] | (e[1][j] << 8) | (e[2][j] << 16) | (e[3][j] << 24);
+                i32x4* dst = (i32x4*)(s + (b * cols + n0) * 4);
+                dst[0] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+                dst[1] = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+            const int k = i / (16 / NSUB);
             float val[8];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                val[2 * h] = bf16_lo((uint32_t)v[i][h]) * f[2 * h];
-                val[2 * h + 1] = bf16_hi((uint32_t)v[i][h]) * f[2 * h + 1];
+                val[2 * h] = bf16_lo((uint32_t)v[i][h]) * f[k][2 * h];
+                val[2 * h + 1] = bf16_hi((uint32_t)v[i][h]) * f[k][2 * h + 1];
             }
             i32x2 out = {cvt4(val[0], val[1], val[2], val[3]), cvt4(val[4], val[5], val[6], val[7])};
-            // NaN/infinity columns: every byte of the block is NaN
+            // NaN/infinity columns of the sub-block: every byte of the block is NaN
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if ((bad >> j) & 1) out[j >> 2] = (out[j >> 2] & ~(0xFF << (8 * (j & 3)))) | (0x7F << (8 * (j & 3)));
+                if ((bad >> (8 * k + j)) & 1) out[j >> 2] = (out[j >> 2] & ~(0xFF << (8 * (j & 3)))) | (0x7F << (8 * (j & 3)));
             const int64_t row = 128 * b + rsub + 8 * i;
             *(i32x2*)(q + row * cols + n0) = out;
         }
@@ -190,19 +251,27 @@ __global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* x, in
 
 }  // namespace
 
-hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
-                               uint8_t* s, int num_cus, hipStream_t stream) {
+template <int FMT>
+static void launch_fmt(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q, void* s,
+                       int64_t blocks, hipStream_t stream) {
+    if (token_axis)
+        hipLaunchKernelGGL(quantize_tokens_cols<FMT>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                           (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+    else
+        hipLaunchKernelGGL(quantize_tokens_rows<FMT>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                           (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+}
+
+hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                               void* q, void* s, int num_cus, hipStream_t stream) {
     const int64_t units = token_axis ? rows * ((cols + 1023) / 1024) : (rows / 128) * ((cols + 63) / 64);
     int64_t blocks = (units + NWAVE - 1) / NWAVE;
     const int64_t cap = (int64_t)num_cus * 16;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    if (token_axis)
-        hipLaunchKernelGGL(quantize_tokens_cols, dim3((unsigned)blocks), dim3(NT), 0, stream, (const uint16_t*)x,
-                           rows, cols, (uint8_t*)q, s);
-    else
-        hipLaunchKernelGGL(quantize_tokens_rows, dim3((unsigned)blocks), dim3(NT), 0, stream, (const uint16_t*)x,
-                           rows, cols, (uint8_t*)q, s);
+    if (scale_format == kScalesPacked32) launch_fmt<kScalesPacked32>(x, rows, cols, token_axis, q, s, blocks, stream);
+    else if (scale_format == kScalesPacked) launch_fmt<kScalesPacked>(x, rows, cols, token_axis, q, s, blocks, stream);
+    else launch_fmt<kScalesU8>(x, rows, cols, token_axis, q, s, blocks, stream);
     return hipGetLastError();
 }
 

@@ -7,6 +7,15 @@
 
 namespace kgw {
 
+// First byte of output matrix e (hidden x n, row-major): slab e of the dense
+// output, or the caller's pointer for expert e (NULL: the expert is skipped).
+template <int OUT>
+__device__ __forceinline__ char* expert_output(const GroupedParams& p, int e) {
+    constexpr int ESIZE = OUT == kOutF32 ? 4 : 2;
+    if (p.out_ptrs) return (char*)p.out_ptrs[e];
+    return (char*)p.out + (int64_t)e * p.hidden * p.n * ESIZE;
+}
+
 // Overwrite-mode output of an expert without tokens: +0.0 over the tile
 // [m0, m0+BM) x [n0, n0+BN) of out[e], clipped to (hidden, n).
 template <int OUT, int BM, int BN, int NT>
@@ -17,7 +26,7 @@ __device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t
     const int cols = (int)min<int64_t>(BN, p.n - n0);
     const int cpr = cols / PER_CHUNK;  // n is a multiple of 8: whole 16-byte chunks
     const int total = rows * cpr;
-    char* base = (char*)p.out + (((int64_t)e * p.hidden + m0) * p.n + n0) * ESIZE;
+    char* base = expert_output<OUT>(p, e) + (m0 * p.n + n0) * ESIZE;
     const i32x4 z = {0, 0, 0, 0};
     for (int c = tid; c < total; c += NT) {
         const int r = c / cpr;
@@ -26,7 +35,7 @@ __device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t
     }
 }
 
-// A wave's 128x128 quarter of the tile, held as 4 (N blocks j) x 4 (M blocks i)
+// A wave's 128x128 quarter of output matrix e's tile, held as 4 (N blocks j) x 4 (M blocks i)
 // MFMA 32x32 accumulators of the transposed product: acc[j][i][4g + t] is
 // out[m][n] with m = mb + 32i + (lane & 31) and n = nb + 32j + 8g + 4*(lane >> 5) + t,
 // written (overwrite or accumulate, output kind OUT) through `stage`, a 32 KiB LDS region
@@ -46,6 +55,7 @@ template <int OUT>
 __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, int e, int64_t mb, int64_t nb,
                                                        int lane, const f32x16 (&acc)[4][4], lds_char* stage) {
     const int64_t H = p.hidden, N = p.n;
+    char* const obase = expert_output<OUT>(p, e);
     const int l32 = lane & 31, lhi = lane >> 5;
     const int c_read = lane & 31;
     const int64_t nn = nb + 4 * c_read;
@@ -78,7 +88,7 @@ __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, i
                 const int64_t m = mb + 64 * pass + r;
                 if (m >= H || nn8 >= N) continue;
                 float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                i32x4* dst = (i32x4*)((char*)p.out + (((int64_t)e * H + m) * N + nn8) * 2);
+                i32x4* dst = (i32x4*)(obase + (m * N + nn8) * 2);
                 if (p.accumulate) {
                     const i32x4 old = *dst;
 #pragma unroll
@@ -98,7 +108,7 @@ __device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, i
                 f32x4 v = __builtin_bit_cast(f32x4, lds_load_16B(stage, (uint32_t)(r * 512 + ((c_read ^ (r & 31)) << 4))));
                 const int64_t m = mb + 64 * pass + r;
                 if (m >= H || nn >= N) continue;
-                f32x4* dst = (f32x4*)((char*)p.out + (((int64_t)e * H + m) * N + nn) * 4);
+                f32x4* dst = (f32x4*)(obase + (m * N + nn) * 4);
                 if (p.accumulate) v += *dst;
                 *dst = v;
             }

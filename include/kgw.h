@@ -71,6 +71,26 @@ typedef enum {
     KGW_OUT_FP16 = 2
 } kgw_out_dtype_t;
 
+/* Layout of the UE8M0 scales of an fp8 operand (mn = hidden for sfa, n for sfb).
+ * The llm-infra-atlas page, section 3, keeps the scales mn-major with packed
+ * 8-bit exponents, and the DeepGEMM k-grouped page casts with gran_k = 32 and
+ * use_packed_ue8m0; neither prints the packed layout.  Reading taken here: four
+ * consecutive token blocks share one little-endian 32-bit word, block 4w + j in
+ * byte j of word (w, m); bytes past the last block are zero (written so by
+ * kgw_quantize_fp8, ignored by the GEMMs).
+ *   KGW_SCALES_U8         one byte per 128 tokens: uint8 (tokens_sum/128, mn).
+ *   KGW_SCALES_PACKED     one byte per 128 tokens, packed: int32
+ *                         (ceil(tokens_sum/512), mn).
+ *   KGW_SCALES_PACKED_32  one byte per 32 tokens (MX-style blocks), packed: int32
+ *                         (tokens_sum/128, mn) -- word (w, m) holds the scales of
+ *                         tokens 128w + 32j .. 128w + 32j + 31 in byte j; 4-byte
+ *                         aligned (16-byte for kgw_quantize_fp8's output). */
+typedef enum {
+    KGW_SCALES_U8 = 0,
+    KGW_SCALES_PACKED = 1,
+    KGW_SCALES_PACKED_32 = 2
+} kgw_scale_format_t;
+
 /* Token-count alignment each entry point requires (cuDNN page, section "BF16
  * contract": every count a multiple of 256 for BF16; for fp8 one UE8M0 scale
  * block, llm-infra-atlas section 3, is 128 tokens). */
@@ -102,7 +122,7 @@ typedef enum {
  *            applying the output mode once: the result differs from the
  *            one-pass result only by the order of the fp32 additions.
  *
- * Sizes: 1 <= num_experts <= 65536; hidden, n >= 0; tokens_sum >= 0 and a
+ * Sizes: 1 <= num_experts <= 65536; 0 <= hidden, n < 2^28; tokens_sum >= 0 and a
  * multiple of 256; n a multiple of 8; tokens_sum < 2^31 (int32 offsets).
  * tokens_sum == 0 (or hidden == 0, or n == 0) is valid: overwrite writes zeros,
  * accumulate does nothing; A and B may then be NULL.  A, B and out must be
@@ -112,6 +132,25 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
                             int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                             void* out, int32_t out_dtype, int32_t accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kgw_wgrad_bf16_ex -- kgw_wgrad_bf16 with a choice of output form (cuDNN page,
+ * section "Output modes": one dense tensor, or discrete per-expert outputs
+ * through an array of pointers, wgrad_ptrs).  Exactly one of `out` and
+ * `out_ptrs` is non-NULL:
+ *   out       the dense (num_experts, hidden, n) output, as for kgw_wgrad_bf16;
+ *   out_ptrs  DEVICE array of num_experts pointers, 8-byte aligned; entry e
+ *             points to expert e's own (hidden, n) row-major matrix of
+ *             out_dtype, 16-byte aligned, not overlapping another entry's (the
+ *             pointers are read on the device only; like the offsets, they are
+ *             the caller's to get right).  A NULL entry skips its expert:
+ *             nothing is computed or written for it.
+ * Everything else (modes, workspace, sizes, errors) as for kgw_wgrad_bf16.
+ */
+kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, const int32_t* offsets,
+                               int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
+                               void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kgw_wgrad_fp8 -- OCP e4m3 ("fn") operands with one power-of-two (UE8M0) scale per
@@ -158,6 +197,26 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kgw_wgrad_fp8_ex -- the fp8 product with a choice of scale layout and output
+ * form.  scale_format is a kgw_scale_format_t: with KGW_SCALES_PACKED_32 every
+ * operand element is scaled by the UE8M0 byte of its own 32-token block (the
+ * DeepGEMM k-grouped page's gran_k = 32); otherwise by that of its 128-token
+ * block.  native 0 computes as kgw_wgrad_fp8 (exact bf16 conversion, bf16
+ * MFMA), 1 as kgw_wgrad_fp8_native (the scaled fp8 MFMA, whose hardware scale
+ * blocks are exactly 32 tokens: each lane hands the instruction the byte of
+ * its half of the 64-token step).  out / out_ptrs as for kgw_wgrad_bf16_ex.
+ * Counts stay multiples of 128 for every format.  Everything else as for
+ * kgw_wgrad_fp8; an unknown scale_format or native value is
+ * KGW_ERROR_INVALID_VALUE, a misaligned KGW_SCALES_PACKED_32 pointer
+ * KGW_ERROR_MISALIGNED.
+ */
+kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, const void* sfb,
+                              int32_t scale_format, int32_t native, const int32_t* offsets,
+                              int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
+                              void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kgw_quantize_fp8 -- produce the fp8 operands of kgw_wgrad_fp8 from bf16 on the
  * device: OCP e4m3fn bytes plus one UE8M0 scale byte per 128 tokens, the
  * blocks running along the token axis (llm-infra-atlas "05 Grouped GEMM",
@@ -168,25 +227,29 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
  * block, 448 = largest e4m3fn), its byte k + 127 clamped to [1, 254] (127 for
  * an all-zero block), and every element is e4m3fn(x / 2^k) rounded to
  * nearest, ties to even.  A block holding a NaN or an infinity gets scale byte
- * 0xFF (NaN) and NaN elements (0x7F).
+ * 0xFF (NaN) and NaN elements (0x7F).  With scale_format KGW_SCALES_PACKED_32
+ * the blocks are 32 tokens long (the DeepGEMM k-grouped page's gran_k = 32).
  *
  *   x       bf16 (rows, cols), row-major, device, 16-byte aligned.
  *   token_axis  1: tokens along the columns -- A of the weight gradient,
- *           (hidden, tokens_sum); scales (cols/128, rows).
- *           0: tokens along the rows -- B, (tokens_sum, n); scales
- *           (rows/128, cols).
+ *           (hidden, tokens_sum); scales with mn = rows.
+ *           0: tokens along the rows -- B, (tokens_sum, n); scales with
+ *           mn = cols.
+ *   scale_format  a kgw_scale_format_t: the layout of `scales`, the one the
+ *           GEMM entry points take with the same code.
  *   q       uint8 (rows, cols), same layout as x, device, 16-byte aligned.
- *   scales  uint8 as above (mn-major, the layout kgw_wgrad_fp8 takes), device;
- *           8-byte aligned when token_axis == 0.
+ *   scales  device; KGW_SCALES_U8 8-byte aligned when token_axis == 0,
+ *           KGW_SCALES_PACKED_32 16-byte aligned.
  *   stream  hipStream_t (NULL = default stream); asynchronous.
  *
  * The token length (cols for token_axis 1, rows for 0) must be a multiple of
- * 128 (else KGW_ERROR_INVALID_VALUE) and cols a multiple of 8
- * (KGW_ERROR_MISALIGNED).  rows or cols == 0 does nothing.  Every output byte
+ * 128 for every format (else KGW_ERROR_INVALID_VALUE) and cols a multiple of 8
+ * (KGW_ERROR_MISALIGNED); an unknown token_axis or scale_format is
+ * KGW_ERROR_INVALID_VALUE.  rows or cols == 0 does nothing.  Every output byte
  * is a function of x alone: results are bit-for-bit reproducible.
  */
-kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, void* q,
-                              uint8_t* scales, void* stream);
+kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis,
+                              int32_t scale_format, void* q, void* scales, void* stream);
 
 /*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape

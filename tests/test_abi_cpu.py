@@ -155,3 +155,46 @@ def test_python_binding_rejects_bad_tensors():
         kgw.kgw_wgrad_fp8(A.view(torch.uint8)[:, :256], None, B.view(torch.uint8), None, off)  # no scales
     with pytest.raises(ValueError):
         kgw.kgw_wgrad_bf16(A, B, off, accumulate=True)                         # accumulate needs out
+
+
+def call_bf16_ex(lib, out=FAKE, ptrs=None, H=256, N=512, E=4, T=1024):
+    return lib.kgw_wgrad_bf16_ex(FAKE, FAKE, FAKE, E, H, N, T, out, ptrs, 0, 0, None, 0, None)
+
+
+def call_fp8_ex(lib, sa=FAKE, sb=FAKE, fmt=0, native=0, out=FAKE, ptrs=None, H=256, N=512, T=1024):
+    return lib.kgw_wgrad_fp8_ex(FAKE, sa, FAKE, sb, fmt, native, FAKE, 4, H, N, T, out, ptrs, 1, 0, None, 0, None)
+
+
+def test_extended_entry_point_errors(lib):
+    # exactly one output form
+    assert call_bf16_ex(lib, out=FAKE, ptrs=FAKE) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16_ex(lib, out=None, ptrs=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16_ex(lib, out=None, ptrs=FAKE + 4) == kgw.KGW_ERROR_MISALIGNED   # pointer array alignment
+    assert call_bf16_ex(lib, out=None, ptrs=None, H=0) == kgw.KGW_SUCCESS         # nothing to write
+    assert call_bf16_ex(lib, H=1 << 28) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, fmt=3) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, fmt=-1) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, native=2) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, sa=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED_32, sa=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED
+    assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED, sa=FAKE + 2, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
+    assert call_fp8_ex(lib, out=FAKE, ptrs=FAKE) == kgw.KGW_ERROR_INVALID_VALUE
+
+
+def test_quantizer_argument_errors(lib):
+    q = lib.kgw_quantize_fp8
+    assert q(FAKE, 256, 256, 1, 3, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # unknown format
+    assert q(FAKE, 256, 256, 2, 0, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # unknown axis
+    assert q(FAKE, 256, 200, 1, 2, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # tokens % 128
+    assert q(FAKE, 256, 256, 0, 2, FAKE, FAKE + 4, None) == kgw.KGW_ERROR_MISALIGNED     # packed-32 needs 16 B
+    assert q(FAKE, 256, 256, 0, 0, FAKE, FAKE + 4, None) == kgw.KGW_ERROR_MISALIGNED     # bytes, rows: 8 B
+    assert q(FAKE, 0, 256, 1, 1, None, None, None) == kgw.KGW_SUCCESS                    # empty
+
+
+def test_scale_shapes():
+    import torch
+    assert kgw.scale_shape(1280, 7, kgw.KGW_SCALES_U8) == ((10, 7), torch.uint8)
+    assert kgw.scale_shape(1280, 7, kgw.KGW_SCALES_PACKED) == ((3, 7), torch.int32)
+    assert kgw.scale_shape(1280, 7, kgw.KGW_SCALES_PACKED_32) == ((10, 7), torch.int32)
+    with pytest.raises(ValueError):
+        kgw.scale_shape(1280, 7, 5)
