@@ -70,6 +70,8 @@ def _load():
     lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_double]
     lib.oracle_e8m0_for_amax.restype = ctypes.c_uint8
     lib.oracle_e8m0_for_amax.argtypes = [ctypes.c_double]
+    lib.oracle_mgrouped_bf16.restype = ctypes.c_int
+    lib.oracle_mgrouped_bf16.argtypes = [p, p, p, i64, i64, i64, i32, ctypes.c_int, p]
     lib.oracle_quantize_fp8_tokens.restype = ctypes.c_int
     lib.oracle_quantize_fp8_tokens.argtypes = [p, i64, i64, ctypes.c_int, p, p, i64]
     _lib = lib
@@ -263,6 +265,45 @@ def unpack_scales(words, nblocks: int) -> np.ndarray:
     for j in range(4):
         out[j::4] = ((w >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
     return out[:nblocks]
+
+
+# ----------------------------------------------------------------------------
+# m-grouped GEMM (forward / dgrad of the same experts)
+# ----------------------------------------------------------------------------
+def row_groups_from_offsets(offsets, M: int) -> np.ndarray:
+    """Group of every row of an M-row contiguous layout: row m is in group e when
+    offsets[e-1] <= m < offsets[e] (offsets[-1] read as 0); rows at or past the last offset
+    belong to no group (-1)."""
+    off = np.asarray(_as_numpy(offsets), dtype=np.int64)
+    g = np.searchsorted(off, np.arange(M), side="right").astype(np.int32)
+    g[g >= off.size] = -1
+    return g
+
+
+def mgrouped_bf16(A, W, *, offsets=None, m_indices=None, layout: str = "nt") -> np.ndarray:
+    """(M, N) float64 result of the m-grouped product; rows of no group are NaN.
+
+    A bf16 (M, K); W bf16 (E, N, K) for layout "nt" (forward, out = A_g @ W_g^T) or
+    (E, K, N) for "nn" (dgrad, out = A_g @ W_g).  Groups from inclusive cumulative
+    `offsets` (E,) or from per-row `m_indices` (M,) (negative = no group).
+    """
+    a, w = _u16(A), _u16(W)
+    M, K = a.shape
+    E = w.shape[0]
+    nt = layout == "nt"
+    assert layout in ("nt", "nn")
+    N = w.shape[1] if nt else w.shape[2]
+    assert (w.shape[2] if nt else w.shape[1]) == K, "W does not match A's K"
+    if m_indices is not None:
+        grp = np.ascontiguousarray(np.asarray(_as_numpy(m_indices), dtype=np.int32))
+    else:
+        grp = row_groups_from_offsets(offsets, M)
+    assert grp.shape == (M,)
+    out = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_mgrouped_bf16(_ptr(a), _ptr(w), _ptr(grp), M, K, N, E, int(nt), _ptr(out))
+    if rc != 0:
+        raise ValueError("group id out of range")
+    return out
 
 
 def apply_output_mode(W: np.ndarray, accumulate: bool, C0: Optional[np.ndarray] = None) -> np.ndarray:

@@ -253,3 +253,44 @@ int oracle_quantize_fp8_tokens(const uint16_t* x, int64_t rows, int64_t cols, in
     }
     return 0;
 }
+
+/*
+ * M-grouped GEMM (llm-infra-atlas "05 Grouped GEMM", section 1 "grouping only
+ * along M" and section 2.1 "contiguous layout"; section 5.1 for the dgrad
+ * form).  The rows of A (M, K) are the concatenated tokens of the experts;
+ * row m belongs to group g(m) and
+ *
+ *     forward ("nt"): out[m, :] = A[m, :] @ W[g(m)]^T    W (E, N, K)
+ *     dgrad   ("nn"): out[m, :] = A[m, :] @ W[g(m)]      W (E, K, N)
+ *
+ * bf16 operands, each output element one fp64 sum over k in increasing order.
+ * group[m] < 0 marks a row that belongs to no group: it is not computed
+ * (out row left as NaN for the caller to recognise).  Returns 0, or -1 on a
+ * group id >= num_groups.
+ */
+int oracle_mgrouped_bf16(const uint16_t* A, const uint16_t* W, const int32_t* group, int64_t M, int64_t K,
+                         int64_t N, int32_t num_groups, int nt, double* out) {
+    for (int64_t m = 0; m < M; ++m)
+        if (group[m] >= num_groups) return -1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t m = 0; m < M; ++m) {
+        double* o = out + m * N;
+        const int32_t g = group[m];
+        if (g < 0) {
+            for (int64_t j = 0; j < N; ++j) o[j] = NAN;
+            continue;
+        }
+        const uint16_t* Wg = W + (int64_t)g * K * N;
+        for (int64_t j = 0; j < N; ++j) o[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = oracle_bf16_value(A[m * K + k]);
+            if (nt) {
+                for (int64_t j = 0; j < N; ++j) o[j] += a * oracle_bf16_value(Wg[j * K + k]);
+            } else {
+                const uint16_t* wrow = Wg + k * N;
+                for (int64_t j = 0; j < N; ++j) o[j] += a * oracle_bf16_value(wrow[j]);
+            }
+        }
+    }
+    return 0;
+}

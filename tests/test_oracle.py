@@ -468,3 +468,90 @@ def test_round_to_fp16_ties_overflow_and_ulp():
     assert oracle.fp16_ulp(np.array([1.0]))[0] == 2.0 ** -10
     assert oracle.fp16_ulp(np.array([3000.0]))[0] == 2.0
     assert oracle.fp16_ulp(np.array([2.0 ** -20]))[0] == 2.0 ** -24
+
+
+# ----------------------------------------------------------------------------
+# m-grouped product (forward "nt" and dgrad "nn" of the same experts)
+# ----------------------------------------------------------------------------
+def test_mgrouped_hand_worked_example(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "mgrouped_example.json")))
+    A = bf16_bits(np.array(g["A"], dtype=np.float64))
+    W = bf16_bits(np.array(g["W"], dtype=np.float64))
+    off = np.array(g["offsets"], dtype=np.int32)
+    assert np.array_equal(oracle.mgrouped_bf16(A, W, offsets=off, layout="nn"), np.array(g["nn_out"], dtype=np.float64))
+    assert np.array_equal(oracle.mgrouped_bf16(A, W, offsets=off, layout="nt"), np.array(g["nt_out"], dtype=np.float64))
+
+
+def _mgrouped_case(counts, K, N, seed, pad_rows=0):
+    rng = np.random.default_rng(seed)
+    M = sum(counts) + pad_rows
+    A = bf16_bits(rng.standard_normal((M, K)))
+    W = bf16_bits(rng.standard_normal((len(counts), N, K)))
+    return A, W, np.cumsum(counts).astype(np.int32), M
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn"])
+def test_mgrouped_matches_numpy_brute_force(oracle_lib, layout):
+    counts = [3, 0, 5, 2]
+    A, W, off, M = _mgrouped_case(counts, 7, 6, seed=31, pad_rows=2)
+    if layout == "nn":
+        W = np.ascontiguousarray(W.transpose(0, 2, 1))       # (E, K, N)
+    got = oracle.mgrouped_bf16(A, W, offsets=off, layout=layout)
+    A64, W64 = bf16_to_f64(A), bf16_to_f64(W)
+    start = 0
+    for e, c in enumerate(counts):
+        Wg = W64[e].T if layout == "nt" else W64[e]
+        np.testing.assert_allclose(got[start:start + c], A64[start:start + c] @ Wg, rtol=1e-12, atol=1e-12)
+        start += c
+    assert np.all(np.isnan(got[start:]))                       # rows past the last offset: no group
+
+
+def test_mgrouped_nt_equals_nn_on_transposed_weights(oracle_lib):
+    A, W, off, M = _mgrouped_case([4, 4, 8], 5, 9, seed=32)
+    Wt = np.ascontiguousarray(W.transpose(0, 2, 1))
+    assert np.array_equal(oracle.mgrouped_bf16(A, W, offsets=off, layout="nt"),
+                          oracle.mgrouped_bf16(A, Wt, offsets=off, layout="nn"))
+
+
+def test_mgrouped_m_indices_match_offsets_and_mark_padding(oracle_lib):
+    counts = [2, 0, 3, 1]
+    A, W, off, M = _mgrouped_case(counts, 4, 3, seed=33, pad_rows=2)
+    idx = np.concatenate([np.repeat(np.arange(4), counts), [-1, -1]]).astype(np.int32)
+    a = oracle.mgrouped_bf16(A, W, offsets=off)
+    b = oracle.mgrouped_bf16(A, W, m_indices=idx)
+    assert np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[:6], b[:6])
+    # one row moved to another group changes exactly that row
+    idx2 = idx.copy()
+    idx2[0] = 3
+    c = oracle.mgrouped_bf16(A, W, m_indices=idx2)
+    assert not np.allclose(c[0], b[0]) and np.array_equal(c[1:6], b[1:6])
+    with pytest.raises(ValueError):
+        oracle.mgrouped_bf16(A, W, m_indices=np.full(M, 4, dtype=np.int32))
+
+
+def test_mgrouped_single_group_is_plain_gemm_and_integers_exact(oracle_lib):
+    rng = np.random.default_rng(34)
+    A = rng.integers(-4, 5, (9, 11)).astype(np.float64)
+    W = rng.integers(-4, 5, (1, 6, 11)).astype(np.float64)
+    got = oracle.mgrouped_bf16(bf16_bits(A), bf16_bits(W), offsets=np.array([9], dtype=np.int32))
+    assert np.array_equal(got, A @ W[0].T)
+
+
+def test_mgrouped_forward_dgrad_wgrad_trace_identity(oracle_lib):
+    # With Y = X W^T per expert (forward), dX = dY W (dgrad) and dW = dY^T X (wgrad, the
+    # k-grouped oracle): <Y, dY> = <dX, X> = sum_e <W_e, dW_e>.
+    counts = [256, 0, 512, 256]
+    T, K, N = sum(counts), 24, 40
+    rng = np.random.default_rng(35)
+    X = bf16_bits(rng.standard_normal((T, K)))
+    dY = bf16_bits(rng.standard_normal((T, N)))
+    W = bf16_bits(rng.standard_normal((4, N, K)))
+    off = np.cumsum(counts).astype(np.int32)
+    Y = oracle.mgrouped_bf16(X, W, offsets=off, layout="nt")                 # (T, N)
+    dX = oracle.mgrouped_bf16(dY, W, offsets=off, layout="nn")               # W_e read as (N, K): (T, K)
+    dW = oracle.wgrad_bf16(np.ascontiguousarray(dY.T), X, off)               # (E, N, K)
+    X64, dY64, W64 = bf16_to_f64(X), bf16_to_f64(dY), bf16_to_f64(W)
+    a = float(np.sum(Y * dY64))
+    b = float(np.sum(dX * X64))
+    c = float(np.sum(W64 * dW))
+    assert abs(a - b) <= 1e-9 * max(1.0, abs(a)) and abs(a - c) <= 1e-9 * max(1.0, abs(a))

@@ -72,3 +72,15 @@ def test_integer_operands_exact():
     wl = workloads.make_operands([256, 256], 8, 16, "bf16", torch.float32, True, seed=1, integer_range=4)
     assert torch.equal(wl.A.float(), wl.A.float().round()) and wl.A.float().abs().max() <= 4
     assert wl.C0.shape == (2, 8, 16)
+
+
+def test_mgrouped_inputs():
+    wl = workloads.make_mgrouped([256, 0, 128], 64, 32, "nt", seed=2, pad_rows=128)
+    assert wl.A.shape == (512, 64) and wl.W.shape == (3, 32, 64) and wl.A.dtype == torch.bfloat16
+    assert wl.offsets.tolist() == [256, 256, 384]
+    idx = wl.m_indices.tolist()
+    assert idx[:256] == [0] * 256 and idx[256:384] == [2] * 128 and idx[384:] == [-1] * 128
+    nn = workloads.make_mgrouped([128], 16, 8, "nn", seed=2)
+    assert nn.W.shape == (1, 16, 8)
+    again = workloads.make_mgrouped([256, 0, 128], 64, 32, "nt", seed=2, pad_rows=128)
+    assert torch.equal(again.A, wl.A) and torch.equal(again.W, wl.W)

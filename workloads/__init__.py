@@ -284,3 +284,46 @@ def make_workload(name: str, seed: int = 1, device="cpu") -> Workload:
 
 
 CONFIG_NAMES = ["tiny", "balanced", "skewed", "fp8", "many_small"]
+
+
+# ----------------------------------------------------------------------------
+# m-grouped (forward / dgrad) inputs
+# ----------------------------------------------------------------------------
+@dataclass
+class MGroupedWorkload:
+    counts: List[int]              # rows per group (multiples of 128; zero allowed)
+    K: int
+    N: int
+    layout: str                    # "nt": W (E, N, K) (forward); "nn": W (E, K, N) (dgrad)
+    A: torch.Tensor = None         # bf16 (M, K), rows grouped contiguously
+    W: torch.Tensor = None         # bf16, see layout
+    offsets: torch.Tensor = None   # int32 (E,), inclusive cumulative row counts
+    m_indices: torch.Tensor = None  # int32 (M,), group id per row (-1 for pad rows)
+
+    @property
+    def M(self) -> int:
+        return int(self.A.shape[0])
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * sum(self.counts) * self.K * self.N
+
+
+def make_mgrouped(counts: List[int], K: int, N: int, layout: str, seed: int, device="cpu", pad_rows: int = 0,
+                  std: float = 1.0, integer_range: Optional[int] = None) -> MGroupedWorkload:
+    """Seeded operands of the m-grouped GEMM: A then W from one generator; `pad_rows` extra rows
+    after the last group (group id -1 in m_indices, beyond the last offset)."""
+    g = _gen(seed, device)
+    M = int(sum(counts)) + pad_rows
+    E = len(counts)
+    wshape = (E, N, K) if layout == "nt" else (E, K, N)
+    if integer_range is None:
+        A = randn_bf16((M, K), std, g, device)
+        W = randn_bf16(wshape, std, g, device)
+    else:
+        A = randint_values((M, K), -integer_range, integer_range, g, device, torch.bfloat16)
+        W = randint_values(wshape, -integer_range, integer_range, g, device, torch.bfloat16)
+    idx = np.concatenate([np.repeat(np.arange(E), counts), -np.ones(pad_rows, dtype=np.int64)]).astype(np.int32)
+    return MGroupedWorkload(counts=list(map(int, counts)), K=K, N=N, layout=layout, A=A, W=W,
+                            offsets=torch.from_numpy(offsets_from_counts(counts)).to(device),
+                            m_indices=torch.from_numpy(idx).to(device))
