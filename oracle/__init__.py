@@ -285,7 +285,7 @@ def mgrouped_bf16(A, W, *, offsets=None, m_indices=None, layout: str = "nt") -> 
 
     A bf16 (M, K); W bf16 (E, N, K) for layout "nt" (forward, out = A_g @ W_g^T) or
     (E, K, N) for "nn" (dgrad, out = A_g @ W_g).  Groups from inclusive cumulative
-    `offsets` (E,) or from per-row `m_indices` (M,) (negative = no group).
+    `offsets` (E,) or from per-row `m_indices` (M,) (an id outside [0, E) = no group).
     """
     a, w = _u16(A), _u16(W)
     M, K = a.shape
@@ -300,9 +300,7 @@ def mgrouped_bf16(A, W, *, offsets=None, m_indices=None, layout: str = "nt") -> 
         grp = row_groups_from_offsets(offsets, M)
     assert grp.shape == (M,)
     out = np.empty((M, N), dtype=np.float64)
-    rc = _load().oracle_mgrouped_bf16(_ptr(a), _ptr(w), _ptr(grp), M, K, N, E, int(nt), _ptr(out))
-    if rc != 0:
-        raise ValueError("group id out of range")
+    _load().oracle_mgrouped_bf16(_ptr(a), _ptr(w), _ptr(grp), M, K, N, E, int(nt), _ptr(out))
     return out
 
 

@@ -264,19 +264,17 @@ int oracle_quantize_fp8_tokens(const uint16_t* x, int64_t rows, int64_t cols, in
  *     dgrad   ("nn"): out[m, :] = A[m, :] @ W[g(m)]      W (E, K, N)
  *
  * bf16 operands, each output element one fp64 sum over k in increasing order.
- * group[m] < 0 marks a row that belongs to no group: it is not computed
- * (out row left as NaN for the caller to recognise).  Returns 0, or -1 on a
- * group id >= num_groups.
+ * A group id outside [0, num_groups) marks a row that belongs to no group (the
+ * pages use -1 for padding rows; larger ids are read the same way): it is not
+ * computed (out row left as NaN for the caller to recognise).  Returns 0.
  */
 int oracle_mgrouped_bf16(const uint16_t* A, const uint16_t* W, const int32_t* group, int64_t M, int64_t K,
                          int64_t N, int32_t num_groups, int nt, double* out) {
-    for (int64_t m = 0; m < M; ++m)
-        if (group[m] >= num_groups) return -1;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t m = 0; m < M; ++m) {
         double* o = out + m * N;
         const int32_t g = group[m];
-        if (g < 0) {
+        if (g < 0 || g >= num_groups) {
             for (int64_t j = 0; j < N; ++j) o[j] = NAN;
             continue;
         }

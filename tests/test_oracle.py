@@ -525,8 +525,9 @@ def test_mgrouped_m_indices_match_offsets_and_mark_padding(oracle_lib):
     idx2[0] = 3
     c = oracle.mgrouped_bf16(A, W, m_indices=idx2)
     assert not np.allclose(c[0], b[0]) and np.array_equal(c[1:6], b[1:6])
-    with pytest.raises(ValueError):
-        oracle.mgrouped_bf16(A, W, m_indices=np.full(M, 4, dtype=np.int32))
+    # ids outside [0, E) -- negative or too large -- mark rows of no group
+    d = oracle.mgrouped_bf16(A, W, m_indices=np.where(idx == 2, 4, idx).astype(np.int32))
+    assert np.all(np.isnan(d[2:5])) and np.array_equal(d[:2], b[:2]) and np.array_equal(d[5:6], b[5:6])
 
 
 def test_mgrouped_single_group_is_plain_gemm_and_integers_exact(oracle_lib):
