@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
-    "kgw_quantize_fp8", "kgw_workspace_bytes",
+    "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT", "KGW_LAYOUT_NN",
     "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
@@ -44,6 +44,8 @@ KGW_ERROR_DEVICE = 5
 KGW_OUT_FP32 = 0
 KGW_OUT_BF16 = 1
 KGW_OUT_FP16 = 2
+KGW_LAYOUT_NT = 0          # m-grouped forward: W (E, N, K)
+KGW_LAYOUT_NN = 1          # m-grouped dgrad:   W (E, K, N)
 KGW_SCALES_U8 = 0          # uint8 (tokens/128, mn)
 KGW_SCALES_PACKED = 1      # int32 (ceil(tokens/512), mn): four 128-token blocks per word
 KGW_SCALES_PACKED_32 = 2   # int32 (tokens/128, mn): four 32-token blocks per word
@@ -56,7 +58,7 @@ _lib = None
 
 # Every symbol include/kgw.h declares.
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
-                    "kgw_wgrad_fp8_ex", "kgw_quantize_fp8", "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
+                    "kgw_wgrad_fp8_ex", "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
                     "kgw_device_info")
 
 
@@ -80,6 +82,8 @@ def load_library():
     lib.kgw_wgrad_bf16_ex.argtypes = [p, p, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_ex.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
+    lib.kgw_mgrouped_bf16.restype = ctypes.c_int
+    lib.kgw_mgrouped_bf16.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
     lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, i32, p, p, p]
     lib.kgw_workspace_bytes.restype = sz
@@ -364,6 +368,52 @@ def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None,
                                          _stream_ptr(stream))
     _check(st, "kgw_quantize_fp8")
     return q, s
+
+
+def kgw_mgrouped_bf16(A: torch.Tensor, W: torch.Tensor, *, offsets: Optional[torch.Tensor] = None,
+                      m_indices: Optional[torch.Tensor] = None, layout: str = "nt",
+                      out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                      accumulate: bool = False, stream=None) -> torch.Tensor:
+    """m-grouped product: out[r] = A[r] @ W[g(r)]^T ("nt", W (E, N, K), the forward) or
+    A[r] @ W[g(r)] ("nn", W (E, K, N), dgrad); groups from `offsets` (inclusive cumulative
+    rows) or per-row `m_indices`; rows of no group are left untouched."""
+    if A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("kgw_mgrouped_bf16 takes bfloat16 A and W")
+    if A.dim() != 2 or W.dim() != 3 or not A.is_contiguous() or not W.is_contiguous():
+        raise ValueError("A must be a contiguous (M, K) and W a contiguous (E, ., .) tensor")
+    if layout not in ("nt", "nn"):
+        raise ValueError("layout is 'nt' (forward) or 'nn' (dgrad)")
+    M, K = A.shape
+    E = W.shape[0]
+    N = W.shape[1] if layout == "nt" else W.shape[2]
+    if (W.shape[2] if layout == "nt" else W.shape[1]) != K:
+        raise ValueError(f"W {tuple(W.shape)} does not match A's K = {K} for layout {layout}")
+    device = A.device
+    if W.device != device:
+        raise ValueError("A and W must be on the same device")
+    if (offsets is None) == (m_indices is None):
+        raise ValueError("pass exactly one of offsets and m_indices")
+    idx = offsets if offsets is not None else m_indices
+    if idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous() or idx.device != device:
+        raise ValueError("offsets / m_indices must be a contiguous 1-D int32 tensor on the operands' device")
+    if offsets is not None and offsets.numel() != E:
+        raise ValueError(f"offsets must have one entry per group ({E})")
+    if m_indices is not None and m_indices.numel() != M:
+        raise ValueError(f"m_indices must have one entry per row ({M})")
+    if out is not None:
+        out_dtype = out.dtype
+    code = _out_code(out_dtype)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an initialised `out`")
+        out = torch.empty((M, N), dtype=out_dtype, device=device)
+    elif tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != device:
+        raise ValueError(f"out must be a contiguous {(M, N)} tensor on the operands' device")
+    st = load_library().kgw_mgrouped_bf16(_ptr(A), _ptr(W), KGW_LAYOUT_NT if layout == "nt" else KGW_LAYOUT_NN,
+                                          _ptr(offsets), _ptr(m_indices), E, M, K, N, _ptr(out), code,
+                                          int(bool(accumulate)), _stream_ptr(stream))
+    _check(st, "kgw_mgrouped_bf16")
+    return out
 
 
 def kgw_workspace_bytes(num_experts: int, hidden: int, n: int, tokens_sum: int, fp8: bool = False) -> int:

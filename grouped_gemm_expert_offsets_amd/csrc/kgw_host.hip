@@ -253,6 +253,49 @@ kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 
+kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, const int32_t* offsets,
+                               const int32_t* m_indices, int32_t num_groups, int64_t m, int64_t k, int64_t n,
+                               void* out, int32_t out_dtype, int32_t accumulate, void* stream) {
+    if (num_groups < 1 || m < 0 || k < 0 || n < 0) return KGW_ERROR_INVALID_VALUE;
+    if (layout != KGW_LAYOUT_NT && layout != KGW_LAYOUT_NN) return KGW_ERROR_INVALID_VALUE;
+    if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16 && out_dtype != KGW_OUT_FP16)
+        return KGW_ERROR_INVALID_VALUE;
+    if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
+    if ((offsets != nullptr) == (m_indices != nullptr)) return KGW_ERROR_INVALID_VALUE;
+    if (num_groups > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
+    if (m > INT32_MAX || k >= ((int64_t)1 << 22) || n >= ((int64_t)1 << 24)) return KGW_ERROR_UNSUPPORTED;
+    if (k % 64 != 0 || n % 8 != 0) return KGW_ERROR_MISALIGNED;
+    if (m == 0 || n == 0) return KGW_SUCCESS;
+    if (!out || (k > 0 && (!A || !W))) return KGW_ERROR_INVALID_VALUE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (((uintptr_t)offsets | (uintptr_t)m_indices) & 3u))
+        return KGW_ERROR_MISALIGNED;
+    if (accumulate && k == 0) return KGW_SUCCESS;
+    DeviceProps d;
+    kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    kgw::MGroupedParams p;
+    p.A = A;
+    p.W = W;
+    p.offsets = offsets;
+    p.m_indices = m_indices;
+    p.out = out;
+    p.out_ptrs = nullptr;
+    p.hidden = m;
+    p.n = n;
+    p.k = k;
+    p.num_groups = num_groups;
+    p.tiles_m = (int32_t)((m + 255) / 256);
+    p.tiles_n = (int32_t)((n + 255) / 256);
+    if ((int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    p.num_items = p.tiles_m * p.tiles_n;
+    p.accumulate = accumulate;
+    p.num_xcds = d.num_xcds;
+    const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
+    const hipError_t err = kgw::launch_mgrouped_bf16(p, layout == KGW_LAYOUT_NT, out_dtype, grid, (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int32_t fp8) {
     DeviceProps d;
     const int cus = current_props(&d) == KGW_SUCCESS ? d.num_cus : kDefaultCus;

@@ -55,6 +55,27 @@ __device__ __forceinline__ ScaleSource scale_source(const uint8_t* sf, int64_t m
     else return {sf + gb * 4 * mn, (uint32_t)(4 * mn)};
 }
 
+// M-grouped GEMM (forward / dgrad): rows of A grouped along M, each group with
+// its own weight.  Field names follow GroupedParams where the output helpers
+// share them (`hidden` = rows of the output = M).
+struct MGroupedParams {
+    const void* A;          // (M, K), K contiguous
+    const void* W;          // nt: (E, N, K); nn: (E, K, N)
+    const int32_t* offsets; // (E,) inclusive cumulative row counts, or NULL
+    const int32_t* m_indices; // (M,) group of every row, or NULL (then offsets)
+    void* out;              // (M, N), row-major
+    void* const* out_ptrs;  // always NULL (one output matrix)
+    int64_t hidden;         // M
+    int64_t n;              // N
+    int64_t k;              // K, a multiple of 64
+    int32_t num_groups;
+    int32_t tiles_m;
+    int32_t tiles_n;
+    int32_t num_items;
+    int32_t accumulate;
+    int32_t num_xcds;
+};
+
 // Split-K chunks start on multiples of this many tokens (a multiple of both
 // token alignments, so no chunk splits a 128-token fp8 scale block).
 constexpr int kSplitUnit = 256;
@@ -73,5 +94,6 @@ hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipS
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
                                void* q, void* s, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

@@ -7,10 +7,13 @@
 
 namespace kgw {
 
+// The output helpers take any parameter block with the fields `out`,
+// `out_ptrs`, `hidden` (rows of one output matrix), `n` and `accumulate`.
+//
 // First byte of output matrix e (hidden x n, row-major): slab e of the dense
 // output, or the caller's pointer for expert e (NULL: the expert is skipped).
-template <int OUT>
-__device__ __forceinline__ char* expert_output(const GroupedParams& p, int e) {
+template <int OUT, class P>
+__device__ __forceinline__ char* expert_output(const P& p, int e) {
     constexpr int ESIZE = OUT == kOutF32 ? 4 : 2;
     if (p.out_ptrs) return (char*)p.out_ptrs[e];
     return (char*)p.out + (int64_t)e * p.hidden * p.n * ESIZE;
@@ -18,8 +21,8 @@ __device__ __forceinline__ char* expert_output(const GroupedParams& p, int e) {
 
 // Overwrite-mode output of an expert without tokens: +0.0 over the tile
 // [m0, m0+BM) x [n0, n0+BN) of out[e], clipped to (hidden, n).
-template <int OUT, int BM, int BN, int NT>
-__device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t m0, int64_t n0, int tid) {
+template <int OUT, int BM, int BN, int NT, class P>
+__device__ __forceinline__ void zero_tile(const P& p, int e, int64_t m0, int64_t n0, int tid) {
     constexpr int ESIZE = OUT == kOutF32 ? 4 : 2;
     constexpr int PER_CHUNK = 16 / ESIZE;
     const int rows = (int)min<int64_t>(BM, p.hidden - m0);
@@ -51,8 +54,8 @@ __device__ __forceinline__ void zero_tile(const GroupedParams& p, int e, int64_t
 // row reads spread over all banks.  The caller must keep other waves' LDS
 // traffic out of `stage` until this returns (its LDS reads are complete once
 // its last store is issued).
-template <int OUT>
-__device__ __forceinline__ void store_wave_tile_staged(const GroupedParams& p, int e, int64_t mb, int64_t nb,
+template <int OUT, class P>
+__device__ __forceinline__ void store_wave_tile_staged(const P& p, int e, int64_t mb, int64_t nb,
                                                        int lane, const f32x16 (&acc)[4][4], lds_char* stage) {
     const int64_t H = p.hidden, N = p.n;
     char* const obase = expert_output<OUT>(p, e);

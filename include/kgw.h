@@ -251,6 +251,47 @@ kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, con
 kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis,
                               int32_t scale_format, void* q, void* scales, void* stream);
 
+/* Weight layout of the m-grouped product (DeepGEMM's "nt" / "nn" naming). */
+typedef enum {
+    KGW_LAYOUT_NT = 0,   /* forward: W (num_groups, n, k), k contiguous; out = A @ W[g]^T */
+    KGW_LAYOUT_NN = 1    /* dgrad:   W (num_groups, k, n), n contiguous; out = A @ W[g]   */
+} kgw_layout_t;
+
+/*
+ * kgw_mgrouped_bf16 -- the m-grouped GEMM of the same MoE layer: its forward and
+ * dgrad (llm-infra-atlas "05 Grouped GEMM": section 1, grouping along M only,
+ * N and K fixed; section 2.1, the contiguous layout; section 5.1, dgrad is
+ * m-grouped too).  Row r of A belongs to group g(r) and
+ *
+ *     layout KGW_LAYOUT_NT:  out[r, :] = A[r, :] @ W[g(r)]^T
+ *     layout KGW_LAYOUT_NN:  out[r, :] = A[r, :] @ W[g(r)]
+ *
+ * bf16 operands, fp32 accumulation, output rounded once to out_dtype.
+ *
+ *   A          bf16 (m, k), row-major (k contiguous), device.
+ *   W          bf16, (num_groups, n, k) for NT or (num_groups, k, n) for NN, device.
+ *   offsets    int32 (num_groups,) inclusive cumulative row counts: row r is in
+ *              group e when offsets[e-1] <= r < offsets[e]; rows at or past
+ *              offsets[num_groups-1] are in no group.  Or NULL, with:
+ *   m_indices  int32 (m,) group id of every row (any id outside
+ *              [0, num_groups) marks a row of no group).  Exactly one of
+ *              offsets / m_indices is given.
+ *              Contract (not checked on the host): every group starts on a
+ *              multiple of 128 rows and holds a multiple of 128 rows, i.e. every
+ *              aligned 128-row block lies in one group (or in none).
+ *   out        (m, n) row-major, out_dtype, device.  accumulate 0: out = product;
+ *              1: out += product.  Rows of no group are left untouched.
+ *   stream     hipStream_t (NULL = default stream); asynchronous, allocates nothing.
+ *
+ * Sizes: 1 <= num_groups <= 65536, 0 <= m < 2^31, 0 <= k < 2^22 and a multiple of
+ * 64, 0 <= n < 2^24 and a multiple of 8 (KGW_ERROR_MISALIGNED otherwise);
+ * A, W, out 16-byte aligned.  m == 0 or n == 0 does nothing; k == 0 writes zeros
+ * (overwrite) into the rows of a group.  Errors as for kgw_wgrad_bf16.
+ */
+kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, const int32_t* offsets,
+                               const int32_t* m_indices, int32_t num_groups, int64_t m, int64_t k, int64_t n,
+                               void* out, int32_t out_dtype, int32_t accumulate, void* stream);
+
 /*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape
  * on the current device (fp8 != 0 selects the fp8 entry points; 256 compute

@@ -198,3 +198,40 @@ def test_scale_shapes():
     assert kgw.scale_shape(1280, 7, kgw.KGW_SCALES_PACKED_32) == ((10, 7), torch.int32)
     with pytest.raises(ValueError):
         kgw.scale_shape(1280, 7, 5)
+
+
+def call_mg(lib, A=FAKE, W=FAKE, layout=0, off=FAKE, idx=None, E=4, M=1024, K=256, N=512, out=FAKE, dt=1, acc=0):
+    return lib.kgw_mgrouped_bf16(A, W, layout, off, idx, E, M, K, N, out, dt, acc, None)
+
+
+def test_mgrouped_argument_errors(lib):
+    assert call_mg(lib, layout=2) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg(lib, E=0) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg(lib, off=None, idx=None) == kgw.KGW_ERROR_INVALID_VALUE     # no grouping
+    assert call_mg(lib, off=FAKE, idx=FAKE) == kgw.KGW_ERROR_INVALID_VALUE     # both
+    assert call_mg(lib, dt=5) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg(lib, acc=3) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg(lib, K=96) == kgw.KGW_ERROR_MISALIGNED                      # K % 64
+    assert call_mg(lib, N=500) == kgw.KGW_ERROR_MISALIGNED                     # N % 8
+    assert call_mg(lib, A=FAKE + 8) == kgw.KGW_ERROR_MISALIGNED
+    assert call_mg(lib, off=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED
+    assert call_mg(lib, K=1 << 22) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_mg(lib, E=65537) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_mg(lib, out=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg(lib, M=0, out=None, A=None) == kgw.KGW_SUCCESS              # nothing to do
+    assert call_mg(lib, K=0, acc=1, A=None, W=None) == kgw.KGW_SUCCESS          # adds nothing
+
+
+def test_mgrouped_binding_rejects_bad_tensors():
+    import torch
+    A = torch.zeros(256, 64, dtype=torch.bfloat16)
+    W = torch.zeros(2, 32, 64, dtype=torch.bfloat16)
+    off = torch.tensor([128, 256], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_bf16(A, W)                                              # no grouping
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_bf16(A, W, offsets=off, layout="tt")
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_bf16(A, W, offsets=off, layout="nn")                    # K mismatch for nn
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_bf16(A, W, offsets=off[:1])
