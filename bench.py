@@ -18,8 +18,9 @@ and is null when the kernel sources changed after those counters were taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `secondary` reports the other workloads (the 32-expert skewed-accumulate,
 fp8 and many-small-expert configs, and the tiny one) with the same timing,
-the fp8 workload with 32-token (MX-style) packed scales, and the on-device
-fp8 quantiser on the fp8 workload's operand shapes.
+the fp8 workload with 32-token (MX-style) packed scales, the m-grouped
+forward and dgrad of the fp8 workload's layer, and the on-device fp8
+quantiser on the fp8 workload's operand shapes.
 
 Warm-up: from idle the GPU needs about 100 ms of continuous load before its
 clocks settle (the first launches of the headline run ~15% slower than the
@@ -192,6 +193,33 @@ def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0
     return res
 
 
+def run_mgrouped(layout: str, steps: int, warmup: int, min_warm_s: float = 0.0):
+    """kgw_mgrouped_bf16 on the fp8 workload's layer: 32 groups of roundup128(8192*U(0.7,1.3))
+    rows; forward ("nt") X (T, 7168) @ W^T with W (32, 4096, 7168); dgrad ("nn") dY (T, 4096) @ W
+    with W (32, 4096, 7168) read as (K=4096, N=7168); bf16 output."""
+    import torch
+    import grouped_gemm_expert_offsets_amd as kgw
+    import workloads
+    counts = workloads.counts_uniform(32, 8192, 128, 1)
+    K, N = (7168, 4096) if layout == "nt" else (4096, 7168)
+    wl = workloads.make_mgrouped(counts, K, N, layout, seed=1, device="cuda")
+    out = torch.empty((wl.M, N), dtype=torch.bfloat16, device="cuda")
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_mgrouped_bf16(wl.A, wl.W, offsets=wl.offsets, layout=layout,
+                                                                 out=out), steps, warmup, min_warm_s)
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    res = {
+        "workload": f"mgrouped_{layout} {'forward' if layout == 'nt' else 'dgrad'} M={wl.M} K={K} N={N} E=32 bf16",
+        "ms_per_step": ms_step,
+        "launch_ms_mean": mean_launch,
+        "tflops": wl.flops / (mean_launch * 1e-3) / 1e12,
+        "flops_per_launch": wl.flops,
+    }
+    res["frac_of_mfma_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    del wl, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_seconds: float):
     """Time the CPU oracle on a bounded sample of the headline workload.
 
@@ -341,6 +369,9 @@ def main():
                 continue
             r = run_workload(name, sec_steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
                              scale_block=block)
+            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+        for layout in ("nt", "nn"):
+            r = run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         for axis in (1, 0):
             r = run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds)
