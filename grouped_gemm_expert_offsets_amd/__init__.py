@@ -27,6 +27,7 @@ import torch
 __all__ = [
     "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
     "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT", "KGW_LAYOUT_NN",
+    "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
     "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
@@ -44,6 +45,9 @@ KGW_ERROR_DEVICE = 5
 KGW_OUT_FP32 = 0
 KGW_OUT_BF16 = 1
 KGW_OUT_FP16 = 2
+KGW_A_M_MAJOR = 1          # weight-gradient A stored (tokens_sum, hidden)
+KGW_B_K_MAJOR = 2          # weight-gradient B stored (n, tokens_sum)
+KGW_RAGGED = 4             # per-expert K-contiguous blocks back to back (with KGW_B_K_MAJOR)
 KGW_LAYOUT_NT = 0          # m-grouped forward: W (E, N, K)
 KGW_LAYOUT_NN = 1          # m-grouped dgrad:   W (E, K, N)
 KGW_SCALES_U8 = 0          # uint8 (tokens/128, mn)
@@ -79,7 +83,7 @@ def load_library():
     lib.kgw_wgrad_fp8_native.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_native.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_bf16_ex.restype = ctypes.c_int
-    lib.kgw_wgrad_bf16_ex.argtypes = [p, p, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_bf16_ex.argtypes = [p, p, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_ex.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_mgrouped_bf16.restype = ctypes.c_int
@@ -219,31 +223,55 @@ def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out:
     return out
 
 
-def kgw_wgrad_bf16_ex(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, *, out: Optional[torch.Tensor] = None,
-                      outs=None, out_dtype: torch.dtype = torch.float32, accumulate: bool = False,
-                      validate: bool = False, stream=None, split_k: bool = True):
-    """kgw_wgrad_bf16 with discrete outputs: `outs` is a list of num_experts (hidden, n) tensors
-    (None skips that expert) whose addresses go to the device as the pointer array; returns
-    `outs`.  With `out` instead it behaves like kgw_wgrad_bf16."""
+def kgw_wgrad_bf16_ex(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, *, a_major: str = "k",
+                      b_major: str = "n", ragged: bool = False, hidden: Optional[int] = None,
+                      n: Optional[int] = None, out: Optional[torch.Tensor] = None, outs=None,
+                      out_dtype: torch.dtype = torch.float32, accumulate: bool = False, validate: bool = False,
+                      stream=None, split_k: bool = True):
+    """kgw_wgrad_bf16 with a choice of operand layout and output form.
+
+    a_major "k": A is (hidden, tokens_sum) (the default); "m": A is stored (tokens_sum, hidden).
+    b_major "n": B is (tokens_sum, n) (the default); "k": B is stored (n, tokens_sum).
+    ragged=True (with a_major "k", b_major "k"): A and B hold per-expert blocks (hidden, n_e) and
+    (n, n_e) back to back; pass them as flat buffers with `hidden` and `n`.
+    `outs` is a list of num_experts (hidden, n) tensors (None skips that expert) whose addresses
+    go to the device as the pointer array (returned); otherwise `out` as for kgw_wgrad_bf16.
+    """
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise ValueError("kgw_wgrad_bf16_ex takes bfloat16 A and B")
-    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
-        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if a_major not in ("k", "m") or b_major not in ("n", "k"):
+        raise ValueError("a_major is 'k' or 'm', b_major is 'n' or 'k'")
     if not (A.is_contiguous() and B.is_contiguous()):
-        raise ValueError("A and B must be contiguous (A token-contiguous, B row-major)")
+        raise ValueError("A and B must be contiguous in their declared layout")
+    layout = (KGW_A_M_MAJOR if a_major == "m" else 0) | (KGW_B_K_MAJOR if b_major == "k" else 0)
+    if ragged:
+        if a_major != "k" or b_major != "k":
+            raise ValueError("ragged input needs K-major A and B (a_major='k', b_major='k')")
+        if hidden is None or n is None or hidden <= 0 or n <= 0 or A.numel() % hidden:
+            raise ValueError("ragged input needs hidden and n, and A.numel() a multiple of hidden")
+        layout |= KGW_RAGGED
+        T = A.numel() // hidden
+        if B.numel() != T * n:
+            raise ValueError(f"B must hold tokens_sum * n = {T * n} elements")
+    else:
+        if A.dim() != 2 or B.dim() != 2:
+            raise ValueError("A and B must be 2-D")
+        hidden, T = A.shape if a_major == "k" else (A.shape[1], A.shape[0])
+        Tb, n = B.shape if b_major == "n" else (B.shape[1], B.shape[0])
+        if Tb != T:
+            raise ValueError(f"shape mismatch: A {tuple(A.shape)} ({a_major}-major), B {tuple(B.shape)} ({b_major}-major)")
     device = A.device
     if B.device != device:
         raise ValueError("A and B must be on the same device")
     _check_offsets(offsets, device)
-    hidden, T = A.shape
-    n = B.shape[1]
     E = offsets.numel()
     out, outs, ptrs, code = _outputs(out, outs, E, hidden, n, out_dtype, accumulate, device, stream)
     if validate:
         kgw_validate_offsets(offsets, T, BF16_TOKEN_ALIGN, stream=stream)
     ws, ws_bytes = _workspace(E, hidden, n, T, False, device, stream, split_k)
-    st = load_library().kgw_wgrad_bf16_ex(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), _ptr(ptrs),
-                                          code, int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
+    st = load_library().kgw_wgrad_bf16_ex(_ptr(A), _ptr(B), layout, _ptr(offsets), E, hidden, n, T, _ptr(out),
+                                          _ptr(ptrs), code, int(bool(accumulate)), _ptr(ws), ws_bytes,
+                                          _stream_ptr(stream))
     _check(st, "kgw_wgrad_bf16_ex")
     return out if outs is None else outs
 

@@ -111,7 +111,7 @@ SplitPlan split_plan(int32_t num_experts, int64_t hidden, int64_t n, int64_t tok
 kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, const void* sfb,
                  int32_t scale_format, const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                  int64_t tokens_sum, void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream, int32_t layout = 0) {
     const bool fp8 = kernel != Kernel::kBf16;
     const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
     const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
@@ -131,6 +131,10 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     if (fp8 && tokens_sum > 0 && hidden > 0 && n > 0 && (!sfa || !sfb)) return KGW_ERROR_INVALID_VALUE;
     if (fp8 && scale_format == KGW_SCALES_PACKED_32 && (((uintptr_t)sfa | (uintptr_t)sfb) & 3u))
         return KGW_ERROR_MISALIGNED;
+    if (layout & ~(KGW_A_M_MAJOR | KGW_B_K_MAJOR | KGW_RAGGED)) return KGW_ERROR_INVALID_VALUE;
+    if ((layout & KGW_RAGGED) && (layout & (KGW_A_M_MAJOR | KGW_B_K_MAJOR)) != KGW_B_K_MAJOR)
+        return KGW_ERROR_INVALID_VALUE;      // ragged blocks are K-contiguous for both operands
+    if ((layout & KGW_A_M_MAJOR) && hidden % 8 != 0) return KGW_ERROR_MISALIGNED;
     if (hidden == 0 || n == 0) return KGW_SUCCESS;                 // no output elements
     if (accumulate && tokens_sum == 0) return KGW_SUCCESS;         // adds nothing
 
@@ -148,6 +152,7 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     p.offsets = offsets;
     p.out = out;
     p.out_ptrs = out_ptrs;
+    p.ragged = (layout & KGW_RAGGED) ? 1 : 0;
     p.hidden = hidden;
     p.n = n;
     p.tokens_sum = tokens_sum;
@@ -175,7 +180,12 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
     hipError_t err;
     switch (kernel) {
-        case Kernel::kBf16: err = kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream); break;
+        case Kernel::kBf16:
+            err = layout ? kgw::launch_wgrad_bf16_layout(p, (layout & KGW_A_M_MAJOR) != 0,
+                                                         (layout & KGW_B_K_MAJOR) != 0, out_kind, grid,
+                                                         (hipStream_t)stream)
+                         : kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream);
+            break;
         case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream); break;
         default: err = kgw::launch_wgrad_fp8_native(p, out_kind, grid, (hipStream_t)stream); break;
     }
@@ -197,12 +207,12 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
                out, nullptr, out_dtype, accumulate, workspace, workspace_bytes, stream);
 }
 
-kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
-                               int64_t hidden, int64_t n, int64_t tokens_sum, void* out, void* const* out_ptrs,
-                               int32_t out_dtype, int32_t accumulate, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, int32_t layout, const int32_t* offsets,
+                               int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, void* out,
+                               void* const* out_ptrs, int32_t out_dtype, int32_t accumulate, void* workspace,
+                               size_t workspace_bytes, void* stream) {
     return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
-               out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
+               out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream, layout);
 }
 
 kgw_status_t kgw_wgrad_fp8(const void* A, const uint8_t* sfa, const void* B, const uint8_t* sfb,

@@ -37,6 +37,7 @@ struct GroupedParams {
     int32_t num_xcds;       // XCD count used to remap workgroup ids
     int32_t split;          // K chunks per expert: 1, or > 1 for split-K partials
     int32_t scale_format;   // fp8 only: kScalesU8, kScalesPacked or kScalesPacked32
+    int32_t ragged;         // bf16 layouts: A and B are per-expert (., n_e) blocks back to back
 };
 
 // Scales of the global 128-token block gb in layout FMT: the value for mn
@@ -85,6 +86,9 @@ constexpr int kBf16BM = 256, kBf16BN = 256, kBf16BK = 32;
 constexpr int kFp8BM = 256, kFp8BN = 256, kFp8BK = 128;
 
 hipError_t launch_wgrad_bf16(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// The other operand majors (A M-major and / or B K-major; ragged blocks with both K-major).
+hipError_t launch_wgrad_bf16_layout(const GroupedParams& p, bool a_m_major, bool b_k_major, int out_kind, int grid,
+                                    hipStream_t stream);
 // Split-K second pass: out[e] (=|+=) the sum over c = 0..split-1, in order, of the fp32
 // partial slabs ws[c*E + e]; in accumulate mode an expert without tokens is left as is.
 hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t num_experts, int64_t hidden,

@@ -238,10 +238,11 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
             i16x4 bhi[2][4];
             i32x4 bt[2][4];
         };
-        constexpr int READS = BT ? 16 : 24;
+        // Block read r (0..15) of step s: per ks the four A blocks, then the four
+        // B blocks (nn: two transposed halves each).
+        constexpr int READS = 16;
         auto read_one = [&](int s, int r, Frags& f) __attribute__((always_inline)) {
-            const int per = READS / 2;
-            const int ks = r / per, q = r % per;
+            const int ks = r >> 3, q = r & 7;
             if (q < 4) {
                 const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
                 const uint32_t a_chunk = (uint32_t)(((4 * (s & 1) + 2 * ks + lhi) ^ a_sw) << 4);
@@ -252,10 +253,9 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
                 f.bt[ks][q - 4] = lds_load_16B(Bs, bt_frag_row + (q - 4) * 4096u + chunk);
             } else {
                 const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
-                const int j = (q - 4) >> 1, hi = (q - 4) & 1;
-                const i16x4 v = lds_read_tr16(Bs, b_frag[j] + ks * 8192u + hi * 2048u);
-                if (hi) f.bhi[ks][j] = v;
-                else f.blo[ks][j] = v;
+                const int j = q - 4;
+                f.blo[ks][j] = lds_read_tr16(Bs, b_frag[j] + ks * 8192u);
+                f.bhi[ks][j] = lds_read_tr16(Bs, b_frag[j] + ks * 8192u + 2048u);
             }
         };
         auto read_all = [&](int s, Frags& f) __attribute__((always_inline)) {
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
         read_all(0, f0);
 
         // Step s: a barrier publishes step s+1 once its loads have landed, then
-        // 32 MFMAs with the step's loads spread among them and the fragment reads
-        // of step s+1 after the 16th.  nn: as the k-grouped kernel (at most 16 /
+        // 32 MFMAs with the step's loads spread among them and the 16 block reads
+        // of step s+1 after MFMAs 16..31, one per MFMA.  nn: as the k-grouped kernel (at most 16 /
         // 20 later loads outstanding for odd / even s).  nt: step s+1 needs, for
         // odd s, B stage (s+1)/2 (issued first in step s-2): 8 later loads may
         // remain; for even s nothing newer than B stage s/2 (step s-3): 20.
@@ -334,19 +334,10 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
                     } else {
                         if (r8 == 0) dma_step(s, k >> 3);
                     }
-                    if (k >= 16) read_one(s + 1, k - 16, nxt);
                 } else {
                     if ((k & 3) == 0) dma_step(s, k >> 2);
-                    if (k >= 16) {
-                        const int q = k - 16;
-                        if (q < 8) {
-                            read_one(s + 1, 2 * q, nxt);
-                            read_one(s + 1, 2 * q + 1, nxt);
-                        } else {
-                            read_one(s + 1, 8 + q, nxt);
-                        }
-                    }
                 }
+                if (k >= 16) read_one(s + 1, k - 16, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };

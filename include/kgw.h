@@ -133,11 +133,30 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
                             void* out, int32_t out_dtype, int32_t accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Operand layouts of kgw_wgrad_bf16_ex (cuDNN page, "BF16 contract" table and
+ * its input_order), combined as bit flags; 0 is kgw_wgrad_bf16's layout
+ * (A K-major: (hidden, tokens_sum) row-major; B N-major: (tokens_sum, n)
+ * row-major).  Element (m, t) of A and (t, j) of B then live at:
+ *   KGW_A_M_MAJOR  A stored as (tokens_sum, hidden) row-major: A[t * hidden + m]
+ *                  (stride (1, hidden)); hidden must be a multiple of 8.
+ *   KGW_B_K_MAJOR  B stored as (n, tokens_sum) row-major: B[j * tokens_sum + t]
+ *                  (stride (1, tokens_sum)).
+ *   KGW_RAGGED     with KGW_B_K_MAJOR and without KGW_A_M_MAJOR only ("tensor_ragged":
+ *                  per-expert K-contiguous blocks back to back): expert e's A block
+ *                  is (hidden, n_e) row-major from element begin*hidden, its B block
+ *                  (n, n_e) row-major from element begin*n, where n_e = end - begin:
+ *                  A[begin*hidden + m*n_e + (t - begin)], B[begin*n + j*n_e + (t - begin)]. */
+#define KGW_A_M_MAJOR 1
+#define KGW_B_K_MAJOR 2
+#define KGW_RAGGED 4
+
 /*
- * kgw_wgrad_bf16_ex -- kgw_wgrad_bf16 with a choice of output form (cuDNN page,
- * section "Output modes": one dense tensor, or discrete per-expert outputs
- * through an array of pointers, wgrad_ptrs).  Exactly one of `out` and
- * `out_ptrs` is non-NULL:
+ * kgw_wgrad_bf16_ex -- kgw_wgrad_bf16 with a choice of operand layout (`layout`,
+ * KGW_A_M_MAJOR | KGW_B_K_MAJOR | KGW_RAGGED flags as above; any other bit, or
+ * KGW_RAGGED with another combination, is KGW_ERROR_INVALID_VALUE) and of
+ * output form (cuDNN page, section "Output modes": one dense tensor, or discrete
+ * per-expert outputs through an array of pointers, wgrad_ptrs).  Exactly one of
+ * `out` and `out_ptrs` is non-NULL:
  *   out       the dense (num_experts, hidden, n) output, as for kgw_wgrad_bf16;
  *   out_ptrs  DEVICE array of num_experts pointers, 8-byte aligned; entry e
  *             points to expert e's own (hidden, n) row-major matrix of
@@ -147,7 +166,7 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
  *             nothing is computed or written for it.
  * Everything else (modes, workspace, sizes, errors) as for kgw_wgrad_bf16.
  */
-kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, const int32_t* offsets,
+kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, int32_t layout, const int32_t* offsets,
                                int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                                void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
                                void* workspace, size_t workspace_bytes, void* stream);

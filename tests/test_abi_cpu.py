@@ -157,8 +157,8 @@ def test_python_binding_rejects_bad_tensors():
         kgw.kgw_wgrad_bf16(A, B, off, accumulate=True)                         # accumulate needs out
 
 
-def call_bf16_ex(lib, out=FAKE, ptrs=None, H=256, N=512, E=4, T=1024):
-    return lib.kgw_wgrad_bf16_ex(FAKE, FAKE, FAKE, E, H, N, T, out, ptrs, 0, 0, None, 0, None)
+def call_bf16_ex(lib, out=FAKE, ptrs=None, H=256, N=512, E=4, T=1024, layout=0):
+    return lib.kgw_wgrad_bf16_ex(FAKE, FAKE, layout, FAKE, E, H, N, T, out, ptrs, 0, 0, None, 0, None)
 
 
 def call_fp8_ex(lib, sa=FAKE, sb=FAKE, fmt=0, native=0, out=FAKE, ptrs=None, H=256, N=512, T=1024):
@@ -172,6 +172,11 @@ def test_extended_entry_point_errors(lib):
     assert call_bf16_ex(lib, out=None, ptrs=FAKE + 4) == kgw.KGW_ERROR_MISALIGNED   # pointer array alignment
     assert call_bf16_ex(lib, out=None, ptrs=None, H=0) == kgw.KGW_SUCCESS         # nothing to write
     assert call_bf16_ex(lib, H=1 << 28) == kgw.KGW_ERROR_UNSUPPORTED
+    # operand layouts: unknown bits, ragged without both K-major, M-major A with hidden % 8
+    assert call_bf16_ex(lib, layout=8) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16_ex(lib, layout=kgw.KGW_RAGGED) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16_ex(lib, layout=kgw.KGW_RAGGED | kgw.KGW_A_M_MAJOR | kgw.KGW_B_K_MAJOR) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_bf16_ex(lib, layout=kgw.KGW_A_M_MAJOR, H=260) == kgw.KGW_ERROR_MISALIGNED
     assert call_fp8_ex(lib, fmt=3) == kgw.KGW_ERROR_INVALID_VALUE
     assert call_fp8_ex(lib, fmt=-1) == kgw.KGW_ERROR_INVALID_VALUE
     assert call_fp8_ex(lib, native=2) == kgw.KGW_ERROR_INVALID_VALUE
