@@ -70,6 +70,18 @@ def _load():
     lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_double]
     lib.oracle_e8m0_for_amax.restype = ctypes.c_uint8
     lib.oracle_e8m0_for_amax.argtypes = [ctypes.c_double]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e8m0_for_amax_fp4.restype = ctypes.c_uint8
+    lib.oracle_e8m0_for_amax_fp4.argtypes = [ctypes.c_double]
+    lib.oracle_wgrad_rows_fp4.restype = ctypes.c_int
+    lib.oracle_wgrad_rows_fp4.argtypes = [p, p, i64, p, p, i64, i64, i64, i64, p, i64, p]
+    lib.oracle_wgrad_fp4.restype = ctypes.c_int
+    lib.oracle_wgrad_fp4.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p]
+    lib.oracle_quantize_fp4_tokens.restype = ctypes.c_int
+    lib.oracle_quantize_fp4_tokens.argtypes = [p, i64, i64, p, p]
     lib.oracle_mgrouped_bf16.restype = ctypes.c_int
     lib.oracle_mgrouped_bf16.argtypes = [p, p, p, i64, i64, i64, i32, ctypes.c_int, p]
     lib.oracle_quantize_fp8_tokens.restype = ctypes.c_int
@@ -265,6 +277,68 @@ def unpack_scales(words, nblocks: int) -> np.ndarray:
     for j in range(4):
         out[j::4] = ((w >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
     return out[:nblocks]
+
+
+# ----------------------------------------------------------------------------
+# FP4 (e2m1) operands, one UE8M0 scale per 32 tokens, both operands token-contiguous
+# (two tokens per byte, the even token in the low nibble)
+# ----------------------------------------------------------------------------
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(int(code) & 15)
+
+
+def e2m1_encode(v: float) -> int:
+    """e2m1 code of v: round to nearest, ties to the even code, saturating at 6."""
+    return int(_load().oracle_e2m1_encode(float(v)))
+
+
+def e8m0_for_amax_fp4(amax: float) -> int:
+    """Biased UE8M0 exponent of the smallest 2^k with amax <= 6 * 2^k, clamped to [1, 254]."""
+    return int(_load().oracle_e8m0_for_amax_fp4(float(amax)))
+
+
+def wgrad_fp4(A, sfa, B, sfb, offsets) -> np.ndarray:
+    """Dense Wgrad (E, hidden, n) in float64 for e2m1 operands: A (hidden, T/2) and B (n, T/2)
+    packed bytes (token axis contiguous), sfa (T/32, hidden), sfb (T/32, n) UE8M0 bytes."""
+    a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
+    off = np.ascontiguousarray(_as_numpy(offsets).astype(np.int32))
+    hidden, half = a.shape
+    n = b.shape[0]
+    T = 2 * half
+    assert b.shape == (n, half) and sa.shape == (T // 32, hidden) and sb.shape == (T // 32, n), "shapes"
+    out = np.empty((off.size, hidden, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_fp4(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(off), off.size, hidden, n, T, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: malformed offsets")
+    return out
+
+
+def wgrad_rows_fp4(A, sfa, B, sfb, offsets, e: int, rows: Sequence[int]) -> np.ndarray:
+    """Rows `rows` of Wgrad[e] for e2m1 operands (layouts as wgrad_fp4)."""
+    a, sa, b, sb = _u8(A), _u8(sfa), _u8(B), _u8(sfb)
+    hidden, half = a.shape
+    n = b.shape[0]
+    T = 2 * half
+    begin, end = expert_range(offsets, e)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((r.size, n), dtype=np.float64)
+    rc = _load().oracle_wgrad_rows_fp4(_ptr(a), _ptr(sa), hidden, _ptr(b), _ptr(sb), T, n, begin, end, _ptr(r),
+                                       r.size, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: bad token range")
+    return out
+
+
+def quantize_fp4_tokens(x):
+    """bf16 x (rows, cols), tokens along the columns -> (q (rows, cols/2) packed e2m1 bytes,
+    s (cols/32, rows) UE8M0 bytes).  Scale: the smallest 2^k with amax <= 6 * 2^k."""
+    xb = _u16(x)
+    rows, cols = xb.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((cols // 32, rows), dtype=np.uint8)
+    if _load().oracle_quantize_fp4_tokens(_ptr(xb), rows, cols, _ptr(q), _ptr(s)) != 0:
+        raise ValueError("the token length must be a multiple of 32")
+    return q, s
 
 
 # ----------------------------------------------------------------------------

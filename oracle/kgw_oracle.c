@@ -292,3 +292,133 @@ int oracle_mgrouped_bf16(const uint16_t* A, const uint16_t* W, const int32_t* gr
     }
     return 0;
 }
+
+/*
+ * FP4 (OCP e2m1) operands with one UE8M0 scale per 32 tokens (the DeepGEMM
+ * k-grouped page's per_token_cast_to_fp4 with gran_k = 32; the MX block of the
+ * OCP formats).  e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent
+ * field 0 is subnormal (0 or 0.5); no infinities or NaN; largest 6.
+ * Both operands keep the token axis contiguous, two tokens per byte, the
+ * even token in the low nibble:
+ *   A  (hidden, tokens_sum/2) bytes, A[m][t] = nibble t%2 of byte m*T/2 + t/2;
+ *   B  (n, tokens_sum/2) bytes,      B[t][j] = nibble t%2 of byte j*T/2 + t/2;
+ *   sfa (tokens_sum/32, hidden), sfb (tokens_sum/32, n) UE8M0 bytes.
+ */
+double oracle_e2m1_value(uint8_t code) {
+    const int sign = (code >> 3) & 1;
+    const int expo = (code >> 1) & 3;
+    const int mant = code & 1;
+    const double mag = expo == 0 ? 0.5 * mant : ldexp(1.0 + 0.5 * mant, expo - 1);
+    return sign ? -mag : mag;
+}
+
+static double fp4_at(const uint8_t* rowbytes, int64_t t) {
+    const uint8_t b = rowbytes[t >> 1];
+    return oracle_e2m1_value((t & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15));
+}
+
+int oracle_wgrad_rows_fp4(const uint8_t* A, const uint8_t* sfa, int64_t hidden, const uint8_t* B,
+                          const uint8_t* sfb, int64_t tokens_sum, int64_t n, int64_t begin, int64_t end,
+                          const int64_t* rows, int64_t nrows, double* out) {
+    if (begin < 0 || end < begin || end > tokens_sum || tokens_sum % 32 != 0) return -1;
+    const int64_t half = tokens_sum / 2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t m = rows[r];
+        double* w = out + r * n;
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int64_t t = begin; t < end; ++t) {
+                const int64_t blk = t / 32;
+                const double a = fp4_at(A + m * half, t) * oracle_e8m0_value(sfa[blk * hidden + m]);
+                const double b = fp4_at(B + j * half, t) * oracle_e8m0_value(sfb[blk * n + j]);
+                acc += a * b;
+            }
+            w[j] = acc;
+        }
+    }
+    return 0;
+}
+
+int oracle_wgrad_fp4(const uint8_t* A, const uint8_t* sfa, const uint8_t* B, const uint8_t* sfb,
+                     const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
+                     int64_t tokens_sum, double* out) {
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(hidden > 0 ? hidden : 1));
+    if (!rows) return -2;
+    for (int64_t m = 0; m < hidden; ++m) rows[m] = m;
+    int rc = 0;
+    for (int32_t e = 0; e < num_experts && rc == 0; ++e) {
+        int64_t begin, end;
+        oracle_expert_range(offsets, e, &begin, &end);
+        rc = oracle_wgrad_rows_fp4(A, sfa, hidden, B, sfb, tokens_sum, n, begin, end, rows, hidden,
+                                   out + (int64_t)e * hidden * n);
+    }
+    free(rows);
+    return rc;
+}
+
+/* e2m1 code of v (round to nearest, ties to the even code, sign kept); magnitudes
+ * that round above 6 saturate to 6 (e2m1 has no infinity or NaN; NaN -> +6 here,
+ * a case the quantiser below never produces for a finite block). */
+uint8_t oracle_e2m1_encode(double v) {
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    double mag = fabs(v);
+    if (isnan(v)) return 7;
+    uint8_t best = 0;
+    for (uint8_t c = 1; c < 8; ++c) {
+        const double lo = oracle_e2m1_value((uint8_t)(c - 1)), hi = oracle_e2m1_value(c);
+        if (mag > hi) { best = c; continue; }
+        const double mid = 0.5 * (lo + hi);
+        if (mag < mid) best = (uint8_t)(c - 1);
+        else if (mag > mid) best = c;
+        else best = ((c - 1) & 1) ? c : (uint8_t)(c - 1);   /* tie: the even code */
+        break;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Biased UE8M0 exponent of the smallest 2^k with amax <= 6 * 2^k, clamped to
+ * [1, 254]; 127 for zero, 255 for NaN/inf. */
+uint8_t oracle_e8m0_for_amax_fp4(double amax) {
+    if (isnan(amax) || isinf(amax)) return 0xFF;
+    if (amax == 0.0) return 127;
+    int k = (int)ceil(log2(amax / 6.0));
+    while (amax > ldexp(6.0, k)) ++k;
+    while (amax <= ldexp(6.0, k - 1)) --k;
+    int e = k + 127;
+    if (e < 1) e = 1;
+    if (e > 254) e = 254;
+    return (uint8_t)e;
+}
+
+/* Quantise bf16 x (rows, cols), the token axis along the columns (cols % 32 == 0),
+ * to e2m1 with one UE8M0 scale per 32 tokens: q (rows, cols/2) packed bytes,
+ * s (cols/32, rows).  A block holding a NaN or an infinity gets scale 0xFF and
+ * zero codes (e2m1 has no NaN code; the scale carries it). */
+int oracle_quantize_fp4_tokens(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s) {
+    if (cols % 32 != 0) return -1;
+    const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            double amax = 0.0;
+            int bad = 0;
+            for (int64_t t = 32 * b; t < 32 * b + 32; ++t) {
+                const double v = oracle_bf16_value(x[r * cols + t]);
+                if (isnan(v) || isinf(v)) bad = 1;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            const uint8_t e = bad ? 0xFF : oracle_e8m0_for_amax_fp4(amax);
+            s[b * rows + r] = e;
+            for (int64_t t = 32 * b; t < 32 * b + 32; t += 2) {
+                uint8_t lo = 0, hi = 0;
+                if (!bad) {
+                    lo = oracle_e2m1_encode(ldexp(oracle_bf16_value(x[r * cols + t]), 127 - (int)e));
+                    hi = oracle_e2m1_encode(ldexp(oracle_bf16_value(x[r * cols + t + 1]), 127 - (int)e));
+                }
+                q[r * (cols / 2) + t / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return 0;
+}

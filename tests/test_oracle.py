@@ -556,3 +556,88 @@ def test_mgrouped_forward_dgrad_wgrad_trace_identity(oracle_lib):
     b = float(np.sum(dX * X64))
     c = float(np.sum(W64 * dW))
     assert abs(a - b) <= 1e-9 * max(1.0, abs(a)) and abs(a - c) <= 1e-9 * max(1.0, abs(a))
+
+
+# ----------------------------------------------------------------------------
+# FP4 (e2m1) operands with 32-token UE8M0 scales
+# ----------------------------------------------------------------------------
+def test_e2m1_decoder_matches_the_format_table(oracle_lib):
+    # OCP e2m1: exponent field 0 is subnormal (0, 0.5); 1..3 give 1, 1.5, 2, 3, 4, 6
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        assert v == (-1 if c & 8 else 1) * table[c & 7] and (np.signbit(v) == bool(c & 8))
+
+
+def test_e2m1_encode_round_trip_ties_and_generator():
+    for c in range(16):
+        assert oracle.e2m1_encode(oracle.e2m1_value(c)) == c
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for i in range(7):
+        mid = (mags[i] + mags[i + 1]) / 2
+        assert oracle.e2m1_encode(mid) == (i if i % 2 == 0 else i + 1)           # ties to the even code
+        assert oracle.e2m1_encode(mid - 1e-9) == i and oracle.e2m1_encode(mid + 1e-9) == i + 1
+    assert oracle.e2m1_encode(100.0) == 7 and oracle.e2m1_encode(-100.0) == 15
+    rng = np.random.default_rng(15)
+    v = rng.standard_normal(4000) * 3
+    v = np.concatenate([v, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, -0.0]])
+    assert np.array_equal(workloads.e2m1_codes(v), [oracle.e2m1_encode(x) for x in v])
+
+
+def test_fp4_quantizer_matches_generator_and_bounds():
+    g = torch.Generator().manual_seed(16)
+    x = (torch.randn(40, 256, generator=g) * torch.exp2(torch.randint(-10, 10, (40, 1), generator=g).float())
+         ).to(torch.bfloat16)
+    x[3, 32:64] = 0
+    q, s = oracle.quantize_fp4_tokens(x)
+    q_ref, s_ref = workloads.quantize_fp4_token_blocks(x)
+    assert np.array_equal(q, q_ref.numpy()) and np.array_equal(s, s_ref.numpy())
+    assert s[1, 3] == 127 and np.all(q[3, 16:32] == 0)
+    # dequantised: every block's largest magnitude lands in [3, 6] (the top binade of e2m1)
+    codes = np.stack([q & 15, q >> 4], axis=2).reshape(40, 256)
+    vals = np.vectorize(oracle.e2m1_value)(codes) * np.repeat(np.exp2(s.T.astype(np.float64) - 127), 32, axis=1)
+    blk = np.abs(vals / np.repeat(np.exp2(s.T.astype(np.float64) - 127), 32, axis=1)).reshape(40, 8, 32).max(axis=2)
+    nz = blk > 0
+    assert np.all(blk[nz] >= 3) and np.all(blk[nz] <= 6)
+
+
+def _dequant_fp4(q, s):
+    codes = np.stack([q & 15, q >> 4], axis=2).reshape(q.shape[0], -1)
+    return np.vectorize(oracle.e2m1_value)(codes) * np.repeat(np.exp2(s.T.astype(np.float64) - 127), 32, axis=1)
+
+
+def test_fp4_product_matches_dequantised_brute_force():
+    counts = [64, 0, 128, 96]
+    wl = workloads.make_fp4_operands(counts, 12, 20, seed=17)
+    W = oracle.wgrad_fp4(wl["A"], wl["sfa"], wl["B"], wl["sfb"], wl["offsets"])
+    A = _dequant_fp4(wl["A"].numpy(), wl["sfa"].numpy())          # (hidden, T)
+    B = _dequant_fp4(wl["B"].numpy(), wl["sfb"].numpy())          # (n, T)
+    start = 0
+    for e, c in enumerate(counts):
+        np.testing.assert_allclose(W[e], A[:, start:start + c] @ B[:, start:start + c].T, rtol=1e-12, atol=1e-12)
+        start += c
+
+
+def test_fp4_nibble_order_hand_example():
+    # one expert of 32 tokens, hidden = n = 1: A tokens 0, 1 are 1 and 2 (byte 0x42: 2 is code 4 in
+    # the high nibble), B tokens 0, 1 are 3 and 0.5 (byte 0x15); every other code 0; scales 1
+    A = np.zeros((1, 16), dtype=np.uint8)
+    B = np.zeros((1, 16), dtype=np.uint8)
+    A[0, 0], B[0, 0] = 0x42, 0x15
+    s = np.full((1, 1), 127, dtype=np.uint8)
+    W = oracle.wgrad_fp4(A, s, B, s, np.array([32], dtype=np.int32))
+    assert W[0, 0, 0] == 1.0 * 3.0 + 2.0 * 0.5
+    s2 = s.copy()
+    s2[0, 0] = 129                                                  # A's block scaled by 4
+    assert oracle.wgrad_fp4(A, s2, B, s, np.array([32], dtype=np.int32))[0, 0, 0] == 4 * (1.0 * 3.0 + 2.0 * 0.5)
+
+
+def test_fp4_integer_operands_exact():
+    counts = [96, 160]
+    wl = workloads.make_fp4_operands(counts, 7, 9, seed=18, integer_range=6)
+    W = oracle.wgrad_fp4(wl["A"], wl["sfa"], wl["B"], wl["sfb"], wl["offsets"])
+    A = _dequant_fp4(wl["A"].numpy(), wl["sfa"].numpy())
+    B = _dequant_fp4(wl["B"].numpy(), wl["sfb"].numpy())
+    assert np.all(A == np.round(A))
+    assert np.array_equal(W[0], (A[:, :96].astype(np.int64) @ B[:, :96].astype(np.int64).T).astype(np.float64))
+    assert np.array_equal(W[1], (A[:, 96:].astype(np.int64) @ B[:, 96:].astype(np.int64).T).astype(np.float64))

@@ -327,3 +327,66 @@ def make_mgrouped(counts: List[int], K: int, N: int, layout: str, seed: int, dev
     return MGroupedWorkload(counts=list(map(int, counts)), K=K, N=N, layout=layout, A=A, W=W,
                             offsets=torch.from_numpy(offsets_from_counts(counts)).to(device),
                             m_indices=torch.from_numpy(idx).to(device))
+
+
+# ----------------------------------------------------------------------------
+# FP4 (e2m1) test operands: token-contiguous, two tokens per byte (even token in
+# the low nibble), one UE8M0 scale per 32 tokens
+# ----------------------------------------------------------------------------
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E2M1_MAX = 6.0
+
+
+def e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code (ties to the even code, magnitudes above 6 saturate), sign bit 8."""
+    a = np.abs(v)
+    idx = np.clip(np.searchsorted(E2M1_MAGNITUDES, a, side="right") - 1, 0, 7)
+    lo = E2M1_MAGNITUDES[idx]
+    hi = E2M1_MAGNITUDES[np.minimum(idx + 1, 7)]
+    up = (a - lo > hi - a) | ((a - lo == hi - a) & (idx % 2 == 1))
+    code = np.where(idx == 7, 7, np.where(up, idx + 1, idx))
+    return (code + 8 * np.signbit(v)).astype(np.uint8)
+
+
+def quantize_fp4_token_blocks(x: torch.Tensor):
+    """bf16/fp32 (rows, tokens) -> (packed e2m1 bytes (rows, tokens/2), UE8M0 bytes (tokens/32, rows))."""
+    xf = x.to(torch.float32).cpu().numpy().astype(np.float64)
+    rows, t = xf.shape
+    assert t % 32 == 0
+    blocks = xf.reshape(rows, t // 32, 32)
+    amax = np.abs(blocks).max(axis=2)                       # (rows, t/32)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.ceil(np.log2(safe / E2M1_MAX))
+    e = np.where(safe / np.exp2(e) > E2M1_MAX, e + 1, e)
+    e = np.where(amax > 0, e, 0.0)
+    s = np.clip(e + E8M0_BIAS, 1, 254).astype(np.uint8)      # (rows, t/32)
+    scaled = blocks / np.exp2(s.astype(np.float64) - E8M0_BIAS)[:, :, None]
+    codes = e2m1_codes(scaled).reshape(rows, t)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy(np.ascontiguousarray(s.T))
+
+
+def make_fp4_operands(counts: List[int], hidden: int, n: int, seed: int, device="cpu", integer_range=None):
+    """Seeded FP4 operands of the weight gradient: A (hidden, T/2) and B (n, T/2) packed e2m1,
+    sfa (T/32, hidden) and sfb (T/32, n).  Draw order: A then B (bf16 normals, or integers in
+    [-integer_range, integer_range] taken to e2m1 exactly (no 5) with unit scales)."""
+    T = int(sum(counts))
+    g = _gen(seed, "cpu")
+    if integer_range is None:
+        a = randn_bf16((hidden, T), 1.0, g, "cpu")
+        b = randn_bf16((n, T), 1.0, g, "cpu")
+        qa, sa = quantize_fp4_token_blocks(a)
+        qb, sb = quantize_fp4_token_blocks(b)
+    else:
+        vals = torch.tensor([-6.0, -4.0, -3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0, 4.0, 6.0])
+        keep = vals[vals.abs() <= integer_range]
+        ia = keep[torch.randint(0, keep.numel(), (hidden, T), generator=g)]
+        ib = keep[torch.randint(0, keep.numel(), (n, T), generator=g)]
+        ca, cb = e2m1_codes(ia.numpy()), e2m1_codes(ib.numpy())
+        qa = torch.from_numpy((ca[:, 0::2] | (ca[:, 1::2] << 4)).astype(np.uint8))
+        qb = torch.from_numpy((cb[:, 0::2] | (cb[:, 1::2] << 4)).astype(np.uint8))
+        sa = torch.full((T // 32, hidden), E8M0_BIAS, dtype=torch.uint8)
+        sb = torch.full((T // 32, n), E8M0_BIAS, dtype=torch.uint8)
+    off = torch.from_numpy(offsets_from_counts(counts))
+    return dict(A=qa.to(device), sfa=sa.to(device), B=qb.to(device), sfb=sb.to(device), offsets=off.to(device),
+                counts=list(map(int, counts)), hidden=hidden, n=n)
