@@ -18,7 +18,8 @@ and is null when the kernel sources changed after those counters were taken.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 `secondary` reports the other workloads (the 32-expert skewed-accumulate,
 fp8 and many-small-expert configs, and the tiny one) with the same timing,
-the fp8 workload with 32-token (MX-style) packed scales, the m-grouped
+the fp8 workload with 32-token (MX-style) packed scales and with FP4
+operands, the m-grouped
 forward and dgrad of the fp8 workload's layer, and the on-device fp8
 quantiser on the fp8 workload's operand shapes.
 
@@ -46,6 +47,7 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s and % of MFMA peak, K-grouped MoE wgrad (bf16 and fp8), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10066.3     # MI355X dense fp4 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 HEADLINE = "balanced"
 
@@ -220,6 +222,34 @@ def run_mgrouped(layout: str, steps: int, warmup: int, min_warm_s: float = 0.0):
     return res
 
 
+def run_fp4(steps: int, warmup: int, min_warm_s: float = 0.0):
+    """kgw_wgrad_fp4 on the fp8 workload's shape (E=32, hidden 7168, n 4096, counts
+    roundup256(8192*U(0.7,1.3))), e2m1 operands with uniformly random codes and 32-token scales
+    drawn on the device, bf16 output."""
+    import torch
+    import grouped_gemm_expert_offsets_amd as kgw
+    import workloads
+    counts = workloads.counts_uniform(32, 8192, 256, 1)
+    wl = workloads.make_fp4_operands(counts, 7168, 4096, seed=1, device="cuda", random_codes=True)
+    sa, sb = workloads.pack_scale_words(wl["sfa"]), workloads.pack_scale_words(wl["sfb"])
+    out = torch.empty((32, 7168, 4096), dtype=torch.bfloat16, device="cuda")
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_wgrad_fp4(wl["A"], sa, wl["B"], sb, wl["offsets"], out=out),
+                                   steps, warmup, min_warm_s)
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    flops = 2.0 * 7168 * 4096 * sum(counts)
+    res = {
+        "workload": f"fp4 e2m1 32-token UE8M0 E=32 H=7168 N=4096 tokens_sum={sum(counts)}, bf16 out",
+        "ms_per_step": ms_step,
+        "launch_ms_mean": mean_launch,
+        "tflops": flops / (mean_launch * 1e-3) / 1e12,
+        "flops_per_launch": flops,
+    }
+    res["frac_of_mfma_peak"] = res["tflops"] / PEAK_FP4_TFLOPS
+    del wl, out, sa, sb
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_seconds: float):
     """Time the CPU oracle on a bounded sample of the headline workload.
 
@@ -370,6 +400,8 @@ def main():
             r = run_workload(name, sec_steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
                              scale_block=block)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+        r = run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds)
+        sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         for layout in ("nt", "nn"):
             r = run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})

@@ -26,6 +26,7 @@ import torch
 
 __all__ = [
     "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
+    "kgw_wgrad_fp4", "FP4_TOKEN_ALIGN",
     "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT", "KGW_LAYOUT_NN",
     "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
     "kgw_validate_offsets",
@@ -55,6 +56,7 @@ KGW_SCALES_PACKED = 1      # int32 (ceil(tokens/512), mn): four 128-token blocks
 KGW_SCALES_PACKED_32 = 2   # int32 (tokens/128, mn): four 32-token blocks per word
 BF16_TOKEN_ALIGN = 256
 FP8_TOKEN_ALIGN = 128
+FP4_TOKEN_ALIGN = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkgw.so")
@@ -62,7 +64,8 @@ _lib = None
 
 # Every symbol include/kgw.h declares.
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
-                    "kgw_wgrad_fp8_ex", "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
+                    "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_mgrouped_bf16",
+                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
                     "kgw_device_info")
 
 
@@ -86,6 +89,8 @@ def load_library():
     lib.kgw_wgrad_bf16_ex.argtypes = [p, p, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_ex.restype = ctypes.c_int
     lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_fp4.restype = ctypes.c_int
+    lib.kgw_wgrad_fp4.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_mgrouped_bf16.restype = ctypes.c_int
     lib.kgw_mgrouped_bf16.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
@@ -320,6 +325,41 @@ def kgw_wgrad_fp8_ex(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: t
     `outs` (see kgw_wgrad_bf16_ex); native=True uses the scaled fp8 MFMA."""
     return _fp8_call("kgw_wgrad_fp8_ex", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream,
                      split_k, scale_format=scale_format, native=native, outs=outs)
+
+
+def kgw_wgrad_fp4(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
+                  *, out: Optional[torch.Tensor] = None, outs=None, out_dtype: torch.dtype = torch.bfloat16,
+                  accumulate: bool = False, validate: bool = False, stream=None, split_k: bool = True):
+    """FP4 (e2m1) operands, both token-contiguous and packed two tokens per byte: A (hidden, T/2)
+    and B (n, T/2) uint8; scales one UE8M0 per 32 tokens, packed: sfa (T/128, hidden) and
+    sfb (T/128, n) int32 (KGW_SCALES_PACKED_32)."""
+    if A.dtype != torch.uint8 or B.dtype != torch.uint8 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("kgw_wgrad_fp4 takes packed e2m1 bytes: A (hidden, T/2), B (n, T/2) uint8")
+    if A.shape[1] != B.shape[1]:
+        raise ValueError(f"A {tuple(A.shape)} and B {tuple(B.shape)} must hold the same token count")
+    hidden, T = A.shape[0], 2 * A.shape[1]
+    n = B.shape[0]
+    (sa_shape, sdtype), (sb_shape, _) = (scale_shape(T, hidden, KGW_SCALES_PACKED_32),
+                                         scale_shape(T, n, KGW_SCALES_PACKED_32))
+    if sfa.dtype != sdtype or sfb.dtype != sdtype or tuple(sfa.shape) != sa_shape or tuple(sfb.shape) != sb_shape:
+        raise ValueError(f"scales must be int32 {sa_shape} and {sb_shape}")
+    for t in (A, B, sfa, sfb):
+        if not t.is_contiguous():
+            raise ValueError("fp4 operands and scales must be contiguous")
+    device = A.device
+    if any(t.device != device for t in (B, sfa, sfb)):
+        raise ValueError("operands and scales must be on the same device")
+    _check_offsets(offsets, device)
+    E = offsets.numel()
+    out, outs, ptrs, code = _outputs(out, outs, E, hidden, n, out_dtype, accumulate, device, stream)
+    if validate:
+        kgw_validate_offsets(offsets, T, FP4_TOKEN_ALIGN, stream=stream)
+    ws, ws_bytes = _workspace(E, hidden, n, T, True, device, stream, split_k)
+    st = load_library().kgw_wgrad_fp4(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T,
+                                      _ptr(out), _ptr(ptrs), code, int(bool(accumulate)), _ptr(ws), ws_bytes,
+                                      _stream_ptr(stream))
+    _check(st, "kgw_wgrad_fp4")
+    return out if outs is None else outs
 
 
 def scale_shape(tokens: int, mn: int, scale_format: int) -> Tuple[Tuple[int, int], torch.dtype]:

@@ -73,7 +73,7 @@ kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, 
     return KGW_SUCCESS;
 }
 
-enum class Kernel { kBf16, kFp8, kFp8Native };
+enum class Kernel { kBf16, kFp8, kFp8Native, kFp4 };
 
 // Split-K: cut every expert's token range into `split` chunks when the output
 // tiles alone would leave most CUs idle (few experts, small hidden x n) and the
@@ -112,11 +112,12 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
                  int32_t scale_format, const int32_t* offsets, int32_t num_experts, int64_t hidden, int64_t n,
                  int64_t tokens_sum, void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
                  void* workspace, size_t workspace_bytes, void* stream, int32_t layout = 0) {
-    const bool fp8 = kernel != Kernel::kBf16;
+    const bool fp8 = kernel != Kernel::kBf16;        // block-scaled operands (fp8 or fp4)
+    const bool fp4 = kernel == Kernel::kFp4;
     const int64_t bm = fp8 ? kgw::kFp8BM : kgw::kBf16BM;
     const int64_t bn = fp8 ? kgw::kFp8BN : kgw::kBf16BN;
-    const int64_t talign = fp8 ? KGW_FP8_TOKEN_ALIGN : KGW_BF16_TOKEN_ALIGN;
-    const int64_t nalign = fp8 ? 16 : 8;
+    const int64_t talign = fp4 ? KGW_FP4_TOKEN_ALIGN : (fp8 ? KGW_FP8_TOKEN_ALIGN : KGW_BF16_TOKEN_ALIGN);
+    const int64_t nalign = (fp8 && !fp4) ? 16 : 8;
     static_assert(KGW_OUT_FP32 == kgw::kOutF32 && KGW_OUT_BF16 == kgw::kOutBf16 && KGW_OUT_FP16 == kgw::kOutF16,
                   "output kind codes");
     static_assert(KGW_SCALES_U8 == kgw::kScalesU8 && KGW_SCALES_PACKED == kgw::kScalesPacked &&
@@ -129,6 +130,7 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
         scale_format != KGW_SCALES_PACKED_32)
         return KGW_ERROR_INVALID_VALUE;
     if (fp8 && tokens_sum > 0 && hidden > 0 && n > 0 && (!sfa || !sfb)) return KGW_ERROR_INVALID_VALUE;
+    if (fp4 && scale_format != KGW_SCALES_PACKED_32) return KGW_ERROR_INVALID_VALUE;
     if (fp8 && scale_format == KGW_SCALES_PACKED_32 && (((uintptr_t)sfa | (uintptr_t)sfb) & 3u))
         return KGW_ERROR_MISALIGNED;
     if (layout & ~(KGW_A_M_MAJOR | KGW_B_K_MAJOR | KGW_RAGGED)) return KGW_ERROR_INVALID_VALUE;
@@ -187,6 +189,7 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
                          : kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream);
             break;
         case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream); break;
+        case Kernel::kFp4: err = kgw::launch_wgrad_fp4(p, out_kind, grid, (hipStream_t)stream); break;
         default: err = kgw::launch_wgrad_fp8_native(p, out_kind, grid, (hipStream_t)stream); break;
     }
     if (err == hipSuccess && split)
@@ -238,6 +241,14 @@ kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, con
     if (native != 0 && native != 1) return KGW_ERROR_INVALID_VALUE;
     return run(native ? Kernel::kFp8Native : Kernel::kFp8, A, sfa, B, sfb, scale_format, offsets, num_experts,
                hidden, n, tokens_sum, out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
+}
+
+kgw_status_t kgw_wgrad_fp4(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* offsets,
+                           int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, void* out,
+                           void* const* out_ptrs, int32_t out_dtype, int32_t accumulate, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return run(Kernel::kFp4, A, sfa, B, sfb, KGW_SCALES_PACKED_32, offsets, num_experts, hidden, n, tokens_sum, out,
+               out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
 }
 
 kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,

@@ -96,6 +96,8 @@ typedef enum {
  * block, llm-infra-atlas section 3, is 128 tokens). */
 #define KGW_BF16_TOKEN_ALIGN 256
 #define KGW_FP8_TOKEN_ALIGN 128
+/* FP4 stages hold 256 tokens (one 128-byte line per operand row). */
+#define KGW_FP4_TOKEN_ALIGN 256
 
 /*
  * kgw_wgrad_bf16 -- bf16 operands, fp32 accumulation (cuDNN page, "BF16 contract":
@@ -234,6 +236,31 @@ kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, con
                               int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                               void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kgw_wgrad_fp4 -- FP4 operands: OCP e2m1 values with one UE8M0 scale per 32
+ * tokens (the DeepGEMM k-grouped page casts a and b to FP4 with gran_k = 32; the
+ * MX block), on the native scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with
+ * both formats e2m1), fp32 accumulation.  e2m1: 1 sign, 2 exponent bits (bias 1),
+ * 1 mantissa bit -- magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Every product times
+ * its scales is exact and each 32-token block's sum is exact inside the
+ * instruction, so the result differs from the exact sum only by fp32
+ * accumulation rounding.
+ *
+ *   A    e2m1 (hidden, tokens_sum) stored two tokens per byte along the token axis:
+ *        (hidden, tokens_sum/2) bytes, token t of row m in byte m*tokens_sum/2 + t/2,
+ *        low nibble for even t.  Token-contiguous (the page's a (M, K)).
+ *   B    e2m1 (tokens_sum, n) stored token-contiguous the same way: (n, tokens_sum/2)
+ *        bytes, token t of column j in byte j*tokens_sum/2 + t/2 (the page's b (N, K)).
+ *   sfa, sfb  UE8M0 per 32 tokens in the KGW_SCALES_PACKED_32 layout: int32
+ *        (tokens_sum/128, hidden) and (tokens_sum/128, n), 4-byte aligned.
+ *   out, out_ptrs, out_dtype, accumulate, workspace  as for kgw_wgrad_bf16_ex.
+ *   Counts multiples of 256 (KGW_FP4_TOKEN_ALIGN), n a multiple of 8.
+ */
+kgw_status_t kgw_wgrad_fp4(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* offsets,
+                           int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, void* out,
+                           void* const* out_ptrs, int32_t out_dtype, int32_t accumulate, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * kgw_quantize_fp8 -- produce the fp8 operands of kgw_wgrad_fp8 from bf16 on the

@@ -240,3 +240,13 @@ def test_mgrouped_binding_rejects_bad_tensors():
         kgw.kgw_mgrouped_bf16(A, W, offsets=off, layout="nn")                    # K mismatch for nn
     with pytest.raises(ValueError):
         kgw.kgw_mgrouped_bf16(A, W, offsets=off[:1])
+
+
+def test_fp4_argument_errors(lib):
+    f = lambda **k: lib.kgw_wgrad_fp4(k.get("A", FAKE), k.get("sa", FAKE), FAKE, k.get("sb", FAKE), FAKE, 4,
+                                      256, k.get("N", 512), k.get("T", 1024), FAKE, None, 1, 0, None, 0, None)
+    assert f(T=896) == kgw.KGW_ERROR_BAD_OFFSETS            # 256-token alignment
+    assert f(sa=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert f(sa=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED       # packed scale words
+    assert f(N=500) == kgw.KGW_ERROR_MISALIGNED
+    assert f(A=FAKE + 8) == kgw.KGW_ERROR_MISALIGNED

@@ -84,3 +84,12 @@ def test_mgrouped_inputs():
     assert nn.W.shape == (1, 16, 8)
     again = workloads.make_mgrouped([256, 0, 128], 64, 32, "nt", seed=2, pad_rows=128)
     assert torch.equal(again.A, wl.A) and torch.equal(again.W, wl.W)
+
+
+def test_fp4_random_codes_shapes():
+    wl = workloads.make_fp4_operands([256, 0, 512], 24, 40, seed=3, random_codes=True)
+    assert wl["A"].shape == (24, 384) and wl["B"].shape == (40, 384)
+    assert wl["sfa"].shape == (24, 24) and wl["sfb"].shape == (24, 40)
+    assert int(wl["sfa"].min()) >= 122 and int(wl["sfa"].max()) <= 132
+    again = workloads.make_fp4_operands([256, 0, 512], 24, 40, seed=3, random_codes=True)
+    assert torch.equal(again["A"], wl["A"]) and torch.equal(again["sfb"], wl["sfb"])

@@ -366,11 +366,23 @@ def quantize_fp4_token_blocks(x: torch.Tensor):
     return torch.from_numpy(packed), torch.from_numpy(np.ascontiguousarray(s.T))
 
 
-def make_fp4_operands(counts: List[int], hidden: int, n: int, seed: int, device="cpu", integer_range=None):
+def make_fp4_operands(counts: List[int], hidden: int, n: int, seed: int, device="cpu", integer_range=None,
+                      random_codes: bool = False):
     """Seeded FP4 operands of the weight gradient: A (hidden, T/2) and B (n, T/2) packed e2m1,
-    sfa (T/32, hidden) and sfb (T/32, n).  Draw order: A then B (bf16 normals, or integers in
-    [-integer_range, integer_range] taken to e2m1 exactly (no 5) with unit scales)."""
+    sfa (T/32, hidden) and sfb (T/32, n).  Draw order: A then B (bf16 normals quantised per
+    32-token block, or integers in [-integer_range, integer_range] taken to e2m1 exactly (no 5)
+    with unit scales).  random_codes=True draws every byte uniformly (each byte is two valid
+    e2m1 codes) and the scale bytes uniformly in [122, 132], on `device` -- for full-size shapes,
+    where quantising billions of values on the host would take minutes."""
     T = int(sum(counts))
+    if random_codes:
+        g = _gen(seed, device)
+        qa = torch.randint(0, 256, (hidden, T // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        qb = torch.randint(0, 256, (n, T // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        sa = torch.randint(122, 133, (T // 32, hidden), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        sb = torch.randint(122, 133, (T // 32, n), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        off = torch.from_numpy(offsets_from_counts(counts)).to(device)
+        return dict(A=qa, sfa=sa, B=qb, sfb=sb, offsets=off, counts=list(map(int, counts)), hidden=hidden, n=n)
     g = _gen(seed, "cpu")
     if integer_range is None:
         a = randn_bf16((hidden, T), 1.0, g, "cpu")
