@@ -16,6 +16,11 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 
 typedef __attribute__((address_space(3))) char lds_char;
+// Global-memory views: loads and stores through these are `global_*`, not
+// `flat_*`, instructions (flat ones also count on the LDS counter).
+typedef __attribute__((address_space(1))) char gbl_char;
+typedef __attribute__((address_space(1))) i32x4 gbl_i32x4;
+typedef __attribute__((address_space(1))) f32x4 gbl_f32x4;
 
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
