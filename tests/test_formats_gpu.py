@@ -243,6 +243,38 @@ def test_discrete_outputs_all_skipped_and_no_tokens():
         assert torch.all(t == 0) and not torch.signbit(t).any()
 
 
+def test_discrete_outputs_many_experts_mostly_empty():
+    # 300 experts of one 256x256 tile each, 40 with tokens: enough items for a full grid,
+    # where workgroups of their own zero-fill the empty experts.  Skipped (None) experts,
+    # empty or not, take no work; every other empty expert is +0.0.
+    E, hidden, n = 300, 256, 256
+    rng = np.random.default_rng(90)
+    counts = [0] * E
+    for e in rng.choice(E, 40, replace=False):
+        counts[e] = 256 * int(rng.integers(1, 4))
+    wl = workloads.make_operands(counts, hidden, n, "bf16", torch.float32, False, seed=90, device=DEV,
+                                 integer_range=4)
+    skip = set(rng.choice(E, 30, replace=False).tolist())
+    outs = _discrete(hidden, n, torch.float32, E, skip=skip)
+    kgw.kgw_wgrad_bf16_ex(wl.A, wl.B, wl.offsets, outs=outs)
+    torch.cuda.synchronize()
+    W = oracle.wgrad_bf16(wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu())
+    for e in range(E):
+        if e in skip:
+            continue
+        if counts[e]:
+            assert np.array_equal(to_f64(outs[e]), W[e]), f"expert {e}"
+        else:
+            assert torch.all(outs[e] == 0) and not torch.signbit(outs[e]).any(), f"expert {e}"
+    # the same call into one dense output: identical values, empty experts +0.0
+    dense = nan_filled((E, hidden, n), torch.float32)
+    kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, dense)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(dense), W)
+    empty = torch.tensor([e for e in range(E) if not counts[e]], device=DEV)
+    assert not torch.signbit(dense.index_select(0, empty)).any()
+
+
 # ----------------------------------------------------------------------------
 # quantiser scale layouts
 # ----------------------------------------------------------------------------
