@@ -34,7 +34,7 @@ __device__ __forceinline__ void zero_tile(const P& p, int e, int64_t m0, int64_t
     for (int c = tid; c < total; c += NT) {
         const int r = c / cpr;
         const int q = c - r * cpr;
-        *(gbl_i32x4*)(base + ((int64_t)r * p.n + q * PER_CHUNK) * ESIZE) = z;
+        __builtin_nontemporal_store(z, (gbl_i32x4*)(base + ((int64_t)r * p.n + q * PER_CHUNK) * ESIZE));
     }
 }
 
@@ -67,7 +67,7 @@ __device__ __forceinline__ void store_rows_from_lds(gbl_char* obase, int64_t m_p
                 for (int u = 0; u < 8; ++u) {
                     const int64_t m = m_pass + 4 * (q0 + u) + (lane >> 4);
                     const int64_t off = FULL || (m < H && col_ok) ? (m * N + nn8) * 2 : 0;
-                    old[u] = *(const gbl_i32x4*)(obase + off);
+                    old[u] = __builtin_nontemporal_load((const gbl_i32x4*)(obase + off));
                 }
             }
 #pragma unroll
@@ -93,7 +93,7 @@ __device__ __forceinline__ void store_rows_from_lds(gbl_char* obase, int64_t m_p
                     }
                     const i32x4 w = {(int)pack_half2<OUT>(v[0], v[1]), (int)pack_half2<OUT>(v[2], v[3]),
                                      (int)pack_half2<OUT>(v[4], v[5]), (int)pack_half2<OUT>(v[6], v[7])};
-                    *(gbl_i32x4*)(obase + (m * N + nn8) * 2) = w;
+                    __builtin_nontemporal_store(w, (gbl_i32x4*)(obase + (m * N + nn8) * 2));
                 }
             }
         }
@@ -111,7 +111,7 @@ __device__ __forceinline__ void store_rows_from_lds(gbl_char* obase, int64_t m_p
                 for (int u = 0; u < 8; ++u) {
                     const int64_t m = m_pass + 2 * (u0 + u) + lhi;
                     const int64_t off = FULL || (m < H && col_ok) ? (m * N + nn) * 4 : 0;
-                    old[u] = *(const gbl_f32x4*)(obase + off);
+                    old[u] = __builtin_nontemporal_load((const gbl_f32x4*)(obase + off));
                 }
             }
 #pragma unroll
@@ -124,7 +124,7 @@ __device__ __forceinline__ void store_rows_from_lds(gbl_char* obase, int64_t m_p
                 const int64_t m = m_pass + 2 * (u0 + u) + lhi;
                 if (!FULL && (m >= H || !col_ok)) continue;
                 if constexpr (ACC) v[u] += old[u];
-                *(gbl_f32x4*)(obase + (m * N + nn) * 4) = v[u];
+                __builtin_nontemporal_store(v[u], (gbl_f32x4*)(obase + (m * N + nn) * 4));
             }
         }
     }
@@ -144,7 +144,10 @@ __device__ __forceinline__ void store_rows_from_lds(gbl_char* obase, int64_t m_p
 // once, after the optional add).  The LDS image holds rows of 32 16-byte chunks with
 // chunk c of row r at slot c ^ (r & 31), so both the scattered writes and the
 // row reads spread over all banks.  All output accesses go through global (not
-// flat) pointers, so they never hold up the LDS reads' counter.  The caller
+// flat) pointers, so they never hold up the LDS reads' counter, and carry
+// non-temporal hints: each output byte is read (accumulate) and written once
+// per call (measured 6% faster on the E=256 fp32 workload, whose 15 GB output
+// write dominates).  The caller
 // must keep other waves' LDS traffic out of `stage` until this returns (its LDS
 // reads are complete once its last store is issued).
 template <int OUT, class P>
