@@ -27,7 +27,8 @@ import torch
 __all__ = [
     "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
     "kgw_wgrad_fp4", "FP4_TOKEN_ALIGN",
-    "kgw_quantize_fp8", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT", "KGW_LAYOUT_NN",
+    "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT",
+    "KGW_LAYOUT_NN",
     "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
     "kgw_validate_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
@@ -64,7 +65,7 @@ _lib = None
 
 # Every symbol include/kgw.h declares.
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
-                    "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_mgrouped_bf16",
+                    "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16",
                     "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
                     "kgw_device_info")
 
@@ -95,6 +96,8 @@ def load_library():
     lib.kgw_mgrouped_bf16.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
     lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, i32, p, p, p]
+    lib.kgw_quantize_fp4.restype = ctypes.c_int
+    lib.kgw_quantize_fp4.argtypes = [p, i64, i64, i32, i32, p, p, p]
     lib.kgw_workspace_bytes.restype = sz
     lib.kgw_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
     lib.kgw_validate_offsets_host.restype = ctypes.c_int
@@ -435,6 +438,38 @@ def kgw_quantize_fp8(x: torch.Tensor, token_axis: int, stream=None,
     st = load_library().kgw_quantize_fp8(_ptr(x), rows, cols, int(token_axis), int(scale_format), _ptr(q), _ptr(s),
                                          _stream_ptr(stream))
     _check(st, "kgw_quantize_fp8")
+    return q, s
+
+
+def kgw_quantize_fp4(x: torch.Tensor, token_axis: int, stream=None,
+                     scale_format: int = KGW_SCALES_PACKED_32) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 x (rows, cols) -> (packed e2m1 bytes, UE8M0 scales per 32 tokens), the operands of
+    kgw_wgrad_fp4.
+
+    token_axis 1: tokens along the columns (A (hidden, tokens)): codes (rows, cols/2), scales
+    with mn = rows; token_axis 0: tokens along the rows (B (tokens, n)): codes (cols, rows/2)
+    (token-contiguous), scales with mn = cols.  scale_format KGW_SCALES_PACKED_32 (int32
+    (tokens/128, mn), what kgw_wgrad_fp4 takes) or KGW_SCALES_U8 (uint8 (tokens/32, mn)).
+    """
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("kgw_quantize_fp4 takes a contiguous 2-D bfloat16 tensor")
+    if token_axis not in (0, 1):
+        raise ValueError("token_axis must be 0 or 1")
+    if scale_format not in (KGW_SCALES_U8, KGW_SCALES_PACKED_32):
+        raise ValueError("FP4 scales are KGW_SCALES_U8 or KGW_SCALES_PACKED_32")
+    rows, cols = x.shape
+    tokens, other = (cols, rows) if token_axis else (rows, cols)
+    if tokens % 128 != 0:
+        raise ValueError(f"the token length ({tokens}) must be a multiple of 128")
+    if scale_format == KGW_SCALES_U8:
+        shape, sdtype = (tokens // 32, other), torch.uint8
+    else:
+        shape, sdtype = scale_shape(tokens, other, scale_format)
+    q = torch.empty((other, tokens // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty(shape, dtype=sdtype, device=x.device)
+    st = load_library().kgw_quantize_fp4(_ptr(x), rows, cols, int(token_axis), int(scale_format), _ptr(q), _ptr(s),
+                                         _stream_ptr(stream))
+    _check(st, "kgw_quantize_fp4")
     return q, s
 
 

@@ -274,6 +274,28 @@ kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 
+kgw_status_t kgw_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                              void* q, void* scales, void* stream) {
+    if (token_axis != 0 && token_axis != 1) return KGW_ERROR_INVALID_VALUE;
+    if (scale_format != KGW_SCALES_U8 && scale_format != KGW_SCALES_PACKED_32) return KGW_ERROR_INVALID_VALUE;
+    if (rows < 0 || cols < 0) return KGW_ERROR_INVALID_VALUE;
+    const int64_t tokens = token_axis ? cols : rows;
+    if (tokens % 128 != 0) return KGW_ERROR_INVALID_VALUE;
+    if (rows == 0 || cols == 0) return KGW_SUCCESS;
+    if (!x || !q || !scales) return KGW_ERROR_INVALID_VALUE;
+    if (cols % 8 != 0 || !aligned16(x) || !aligned16(q)) return KGW_ERROR_MISALIGNED;
+    if (scale_format == KGW_SCALES_U8 && !token_axis && ((uintptr_t)scales & 7u)) return KGW_ERROR_MISALIGNED;
+    if (scale_format == KGW_SCALES_PACKED_32 && !aligned16(scales)) return KGW_ERROR_MISALIGNED;
+    if (rows * cols >= ((int64_t)1 << 40)) return KGW_ERROR_UNSUPPORTED;
+    DeviceProps d;
+    kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    const hipError_t err = kgw::launch_quantize_fp4(x, rows, cols, token_axis, scale_format, q, scales, d.num_cus,
+                                                    (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
 kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, const int32_t* offsets,
                                const int32_t* m_indices, int32_t num_groups, int64_t m, int64_t k, int64_t n,
                                void* out, int32_t out_dtype, int32_t accumulate, void* stream) {

@@ -97,6 +97,8 @@ hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t
 hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
                                void* q, void* s, int num_cus, hipStream_t stream);
+hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                               void* q, void* s, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 hipError_t launch_wgrad_fp4(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);

@@ -384,6 +384,269 @@ __global__ __launch_bounds__(NT) void quantize_tokens_rows(const uint16_t* __res
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP4 (OCP e2m1) quantiser: one UE8M0 scale per 32 tokens (the DeepGEMM
+// k-grouped page casts a and b to FP4 with gran_k = 32).  Per block: amax = the
+// largest |x|; the scale is the smallest power of two 2^k with amax <= 6 * 2^k
+// (6 = largest e2m1), stored as k + 127 clamped to [1, 254] (127 for an all-zero
+// block); every element becomes the nearest e2m1 of x * 2^-k (exact in fp32),
+// ties to the even code.  A block holding a NaN or an infinity gets scale byte
+// 0xFF and zero codes (e2m1 has no NaN).  Output codes are token-contiguous, two
+// per byte, the even token in the low nibble: the operand layout of the FP4
+// weight gradient (A (hidden, T/2), B (n, T/2)).
+// ---------------------------------------------------------------------------
+
+// Biased UE8M0 exponent of the smallest 2^k with amax <= 6 * 2^k, from the fp32
+// bits of amax = 1.f * 2^E: 6 * 2^(E-2) = 1.5 * 2^E covers amax when 1.f <= 1.5,
+// else 2^(E-1) is needed; clamped to [1, 254], 127 for zero.
+__device__ __forceinline__ uint32_t e8m0_for_amax_fp4(float amax) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+    if (bits == 0u) return 127u;
+    const int E = (int)(bits >> 23) - 127;               // subnormal amax gives -127: clamps to 1
+    const int k = E - 2 + ((bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+    const int e = k + 127;
+    return (uint32_t)(e < 1 ? 1 : (e > 254 ? 254 : e));
+}
+
+// e2m1 code of y (|y| <= 6 by the choice of scale; larger magnitudes give 7):
+// the magnitude index counts the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5
+// below |y|, a tie going to the even index (0, 2, 2, 4, 4, 6, 6); sign bit 8.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    const float a = fabsf(y);
+    const uint32_t m = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
+                       (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
+                       (a > 5.0f ? 1u : 0u);
+    return m | ((__builtin_bit_cast(uint32_t, y) >> 28) & 8u);
+}
+
+// Eight bf16 values (four words) times f -> eight e2m1 codes, value i in nibble i.
+__device__ __forceinline__ uint32_t e2m1_pack8(const i32x4& w, float f) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        out |= e2m1_code(bf16_lo((uint32_t)w[h]) * f) << (8 * h);
+        out |= e2m1_code(bf16_hi((uint32_t)w[h]) * f) << (8 * h + 4);
+    }
+    return out;
+}
+
+// tokens along the columns: x (rows, cols) -> q (rows, cols/2), scales with mn =
+// rows.  The fp8 kernel's tiling: a workgroup takes 64 rows x 2048 tokens, wave w
+// rows 16w .. 16w+15; in chunk k of a row lane l holds tokens 512k + 8l .. +7, so
+// a quad of lanes is one 32-token block; each lane writes 4 code bytes (a wave
+// 256 B contiguous).  Scales collect in LDS and leave as runs of 64 rows:
+// bytes (KGW_SCALES_U8, (cols/32, rows)) or the 128-token groups' words
+// (kScalesPacked32, (cols/128, rows)).
+template <int FMT>
+__global__ __launch_bounds__(NT) void quantize_fp4_cols(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t cols, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ s) {
+    constexpr bool MX = FMT == kScalesPacked32;
+    __shared__ uint32_t sc[64][64];   // [32-token block (U8) or 128-token group (MX) of the chunk][row]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t chunks = (cols + 2047) / 2048;
+    const int64_t rb = blockIdx.x / chunks;
+    const int64_t c = blockIdx.x - rb * chunks;
+    const int64_t r0 = rb * 64;
+    const int64_t nb32 = cols / 32;
+    const int64_t tl = c * 2048 + 8 * lane;
+    const int64_t rw = r0 + 16 * wave;
+    const int nrow = (int)max<int64_t>(0, min<int64_t>(16, rows - rw));
+
+    auto load_row = [&](int64_t r, i32x4 (&raw)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // cols is a multiple of 128: whole 16-lane groups are in or out
+            if (tl + 512 * k < cols) raw[k] = __builtin_nontemporal_load((const i32x4*)(x + r * cols + tl + 512 * k));
+            else raw[k] = i32x4{0, 0, 0, 0};
+        }
+    };
+    i32x4 cur[4], nxt[4];
+    if (nrow > 0) load_row(rw, cur);
+    for (int i = 0; i < nrow; ++i) {
+        if (i + 1 < nrow) load_row(rw + i + 1, nxt);
+        const int64_t r = rw + i;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float amax = 0.0f;
+            int bad = 0;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float a = bf16_lo((uint32_t)cur[k][h]), b = bf16_hi((uint32_t)cur[k][h]);
+                amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
+                bad |= (not_finite(a) || not_finite(b)) ? 1 : 0;
+            }
+            amax = group_max<4>(amax);
+            bad = group_or<4>(bad);
+            const uint32_t e = bad ? 255u : e8m0_for_amax_fp4(amax);
+            uint32_t word = 0;
+            if constexpr (MX) word = (uint32_t)group_or<16>((int)(e << (8 * ((lane >> 2) & 3))));
+            const int64_t t = tl + 512 * k;
+            if (t >= cols) continue;
+            const uint32_t codes = bad ? 0u : e2m1_pack8(cur[k], inv_scale(e));
+            __builtin_nontemporal_store(codes, (uint32_t*)(q + r * (cols / 2) + t / 2));
+            if constexpr (MX) {
+                if ((lane & 15) == 0) sc[4 * k + (lane >> 4)][16 * wave + i] = word;
+            } else {
+                if ((lane & 3) == 0) sc[16 * k + (lane >> 2)][16 * wave + i] = e;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+    }
+    __syncthreads();
+
+    const int64_t vrows = min<int64_t>(64, rows - r0);
+    if constexpr (FMT == kScalesU8) {
+        // block j = tid >> 2 (0..63) of the chunk, rows 16*(tid & 3) .. +15
+        const int tid = threadIdx.x;
+        const int j = tid >> 2;
+        const int64_t b = c * 64 + j;
+        const int i0 = 16 * (tid & 3);
+        if (b < nb32 && i0 < vrows) {
+            uint8_t* dst = s + b * rows + r0 + i0;
+            if (i0 + 16 <= vrows && ((uintptr_t)dst & 15u) == 0) {
+                i32x4 v;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    v[m] = (int)((sc[j][i0 + 4 * m] & 0xFF) | ((sc[j][i0 + 4 * m + 1] & 0xFF) << 8) |
+                                 ((sc[j][i0 + 4 * m + 2] & 0xFF) << 16) | ((sc[j][i0 + 4 * m + 3] & 0xFF) << 24));
+                *(i32x4*)dst = v;
+            } else {
+                for (int ii = 0; ii < 16 && i0 + ii < vrows; ++ii) dst[ii] = (uint8_t)sc[j][i0 + ii];
+            }
+        }
+    } else {
+        // group j = 4*wave + (lane >> 4) of the chunk, rows 4*(lane & 15) .. +3
+        const int j = 4 * wave + (lane >> 4);
+        const int64_t g = c * 16 + j;
+        const int i0 = 4 * (lane & 15);
+        if (g < cols / 128 && i0 < vrows) {
+            uint32_t* dst = (uint32_t*)s + g * rows + r0 + i0;
+            if (i0 + 4 <= vrows && ((uintptr_t)dst & 15u) == 0)
+                *(i32x4*)dst = i32x4{(int)sc[j][i0], (int)sc[j][i0 + 1], (int)sc[j][i0 + 2], (int)sc[j][i0 + 3]};
+            else
+                for (int rr = 0; rr < 4 && i0 + rr < vrows; ++rr) dst[rr] = sc[j][i0 + rr];
+        }
+    }
+}
+
+// tokens along the rows: x (rows, cols) -> q (cols, rows/2), the token axis made
+// contiguous (the FP4 weight gradient's B layout), scales with mn = cols.  A
+// workgroup takes 256 tokens x 64 columns: wave w tokens 64w .. 64w+63, lane l
+// columns 8*(l & 7) .. +7 and tokens 8*(l >> 3) .. +7 of the wave's 64 (each load
+// 8 rows x 128 bytes; eight consecutive tokens make one 4-byte code word per
+// column).  A 32-token block is 4 lanes (xor 8, 16).  The code words collect in
+// LDS so each column's 128 bytes leave as whole-line stores (scattered 4-byte
+// stores ran at a third of the speed); scales as bytes ((rows/32, cols)) or as the
+// 128-token groups' words, assembled through LDS.  A trailing 128-token half tile
+// is skipped by waves 2-3.
+template <int FMT>
+__global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t cols, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ s) {
+    constexpr bool MX = FMT == kScalesPacked32;
+    __shared__ uint32_t codes_lds[2][64][33];   // [column][token group of 8] (+1: bank spread)
+    __shared__ uint8_t red_e[2][8][64];         // [32-token block of the tile][column]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int cg = lane & 7, tg = lane >> 3;
+    const int64_t cchunks = (cols + 63) / 64;
+    const int64_t tchunks = (rows + 255) / 256;
+    const int64_t units = tchunks * cchunks;
+    int par = 0;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x, par ^= 1) {
+        const int64_t b = u / cchunks;
+        const int64_t c0 = (u - b * cchunks) * 64;
+        const int64_t n0 = c0 + 8 * cg;
+        const int64_t tw = 256 * b + 64 * wave;         // the wave's first token
+        const bool wave_live = tw < rows;                // rows is a multiple of 128: whole waves
+        const bool active = wave_live && n0 < cols;      // cols is a multiple of 8
+        const int64_t t0 = tw + 8 * tg;
+        i32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (active) v[i] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + i) * cols + n0));
+            else v[i] = i32x4{0, 0, 0, 0};
+        }
+        float amax[8];
+        int bad = 0;                                     // bit j: column j holds a NaN or an infinity
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax[j] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float a = bf16_lo((uint32_t)v[i][h]), c = bf16_hi((uint32_t)v[i][h]);
+                amax[2 * h] = fmaxf(amax[2 * h], fabsf(a));
+                amax[2 * h + 1] = fmaxf(amax[2 * h + 1], fabsf(c));
+                bad |= (not_finite(a) ? 1 : 0) << (2 * h);
+                bad |= (not_finite(c) ? 1 : 0) << (2 * h + 1);
+            }
+#pragma unroll
+        for (int m = 8; m < 32; m <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], m, 64));
+            bad |= __shfl_xor(bad, m, 64);
+        }
+        uint32_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = ((bad >> j) & 1) ? 255u : e8m0_for_amax_fp4(amax[j]);
+        // column j's eight tokens: value i of the word is token t0 + i
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = inv_scale(e[j] == 255u ? 127u : e[j]);
+            uint32_t codes = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t w = (uint32_t)v[i][j >> 1];
+                codes |= e2m1_code(((j & 1) ? bf16_hi(w) : bf16_lo(w)) * f) << (4 * i);
+            }
+            if ((bad >> j) & 1) codes = 0;
+            codes_lds[par][8 * cg + j][8 * wave + tg] = codes;
+        }
+        const int blk = 2 * wave + (tg >> 2);            // 32-token block of the tile
+        if constexpr (!MX) {
+            if ((tg & 3) == 0 && active) {
+                const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
+                                  (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
+                *(i32x2*)(s + (8 * b + blk) * cols + n0) = sw;
+            }
+        } else {
+            if ((tg & 3) == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) red_e[par][blk][8 * cg + j] = (uint8_t)e[j];
+            }
+        }
+        __syncthreads();
+        // codes: thread -> column tid >> 2, bytes 32*(tid & 3) .. +31 of the tile's 128
+        {
+            const int tid = threadIdx.x;
+            const int col = tid >> 2, part = tid & 3;
+            const int64_t tpart = 256 * b + 64 * part;    // the part's first token
+            if (c0 + col < cols && tpart < rows) {
+                const uint32_t* src = &codes_lds[par][col][8 * part];
+                uint8_t* dst = q + (c0 + col) * (rows / 2) + tpart / 2;
+                __builtin_nontemporal_store(i32x4{(int)src[0], (int)src[1], (int)src[2], (int)src[3]}, (i32x4*)dst);
+                __builtin_nontemporal_store(i32x4{(int)src[4], (int)src[5], (int)src[6], (int)src[7]}, (i32x4*)(dst + 16));
+            }
+        }
+        if constexpr (MX) {
+            // the tile's two 128-token groups: word (group, column) from blocks 4*group .. +3
+            const int tid = threadIdx.x;
+            const int grp = tid >> 6, col = tid & 63;
+            const int64_t gg = 2 * b + grp;
+            if (grp < 2 && c0 + col < cols && 128 * gg < rows) {
+                const uint32_t w = (uint32_t)red_e[par][4 * grp][col] | ((uint32_t)red_e[par][4 * grp + 1][col] << 8) |
+                                   ((uint32_t)red_e[par][4 * grp + 2][col] << 16) |
+                                   ((uint32_t)red_e[par][4 * grp + 3][col] << 24);
+                ((uint32_t*)s)[gg * cols + c0 + col] = w;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 template <int FMT>
@@ -395,6 +658,33 @@ static void launch_fmt(const void* x, int64_t rows, int64_t cols, int32_t token_
     else
         hipLaunchKernelGGL(quantize_tokens_rows<FMT>, dim3((unsigned)blocks), dim3(NT), 0, stream,
                            (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+}
+
+hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
+                               void* q, void* s, int num_cus, hipStream_t stream) {
+    const bool mx = scale_format == kScalesPacked32;
+    if (token_axis) {
+        const int64_t blocks = ((rows + 63) / 64) * ((cols + 2047) / 2048);
+        if (blocks < 1 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+        if (mx)
+            hipLaunchKernelGGL(quantize_fp4_cols<kScalesPacked32>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                               (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+        else
+            hipLaunchKernelGGL(quantize_fp4_cols<kScalesU8>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                               (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+    } else {
+        int64_t blocks = ((rows + 255) / 256) * ((cols + 63) / 64);
+        const int64_t cap = (int64_t)num_cus * 16;
+        if (blocks > cap) blocks = cap;
+        if (blocks < 1) blocks = 1;
+        if (mx)
+            hipLaunchKernelGGL(quantize_fp4_rows<kScalesPacked32>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                               (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+        else
+            hipLaunchKernelGGL(quantize_fp4_rows<kScalesU8>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+                               (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,

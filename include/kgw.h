@@ -297,6 +297,39 @@ kgw_status_t kgw_wgrad_fp4(const void* A, const void* sfa, const void* B, const 
 kgw_status_t kgw_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis,
                               int32_t scale_format, void* q, void* scales, void* stream);
 
+/*
+ * kgw_quantize_fp4 -- produce the FP4 operands of kgw_wgrad_fp4 from bf16 on the
+ * device: OCP e2m1 codes with one UE8M0 scale per 32 tokens (the DeepGEMM
+ * k-grouped page casts a and b to FP4 with gran_k = 32).  The page does not fix
+ * how the scale is chosen; here, per block, the scale is the smallest power of
+ * two 2^k with amax <= 6 * 2^k (amax = largest |x| of the block, 6 = largest
+ * e2m1), its byte k + 127 clamped to [1, 254] (127 for an all-zero block), and
+ * every element is the e2m1 value nearest to x / 2^k, ties to the even code
+ * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 have codes 0..7, sign in bit 3).  A
+ * block holding a NaN or an infinity gets scale byte 0xFF and zero codes (e2m1
+ * has no NaN).  Codes are stored token-contiguous, two per byte, the even token
+ * in the low nibble -- the layout kgw_wgrad_fp4 takes for both operands.
+ *
+ *   x       bf16 (rows, cols), row-major, device, 16-byte aligned.
+ *   token_axis  1: tokens along the columns -- A of the weight gradient,
+ *           (hidden, tokens_sum): q is (rows, cols/2) bytes, scales with mn = rows.
+ *           0: tokens along the rows -- B, (tokens_sum, n): q is (cols, rows/2)
+ *           bytes (the token axis made contiguous), scales with mn = cols.
+ *   scale_format  KGW_SCALES_U8: uint8 (tokens/32, mn), one byte per 32 tokens
+ *           (8-byte aligned when token_axis == 0); KGW_SCALES_PACKED_32: int32
+ *           (tokens/128, mn), the layout kgw_wgrad_fp4 takes (16-byte aligned).
+ *   q       uint8, shape as above, device, 16-byte aligned.
+ *   stream  hipStream_t (NULL = default stream); asynchronous.
+ *
+ * The token length (cols for token_axis 1, rows for 0) must be a multiple of
+ * 128 (else KGW_ERROR_INVALID_VALUE) and cols a multiple of 8
+ * (KGW_ERROR_MISALIGNED); an unknown token_axis or scale_format (KGW_SCALES_PACKED
+ * included) is KGW_ERROR_INVALID_VALUE.  rows or cols == 0 does nothing.  Every
+ * output byte is a function of x alone: results are bit-for-bit reproducible.
+ */
+kgw_status_t kgw_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_t token_axis,
+                              int32_t scale_format, void* q, void* scales, void* stream);
+
 /* Weight layout of the m-grouped product (DeepGEMM's "nt" / "nn" naming). */
 typedef enum {
     KGW_LAYOUT_NT = 0,   /* forward: W (num_groups, n, k), k contiguous; out = A @ W[g]^T */

@@ -196,6 +196,21 @@ def test_quantizer_argument_errors(lib):
     assert q(FAKE, 0, 256, 1, 1, None, None, None) == kgw.KGW_SUCCESS                    # empty
 
 
+def test_fp4_quantizer_argument_errors(lib):
+    q = lib.kgw_quantize_fp4
+    assert q(FAKE, 256, 256, 1, kgw.KGW_SCALES_PACKED, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE   # 128-token bytes
+    assert q(FAKE, 256, 256, 1, 3, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # unknown format
+    assert q(FAKE, 256, 256, 2, 0, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # unknown axis
+    assert q(FAKE, 256, 224, 1, 0, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE      # tokens % 128
+    assert q(FAKE, 96, 256, 0, 2, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE       # tokens (rows) % 128
+    assert q(FAKE, 256, 252, 0, 0, FAKE, FAKE, None) == kgw.KGW_ERROR_MISALIGNED         # cols % 8
+    assert q(FAKE, 256, 256, 0, 2, FAKE, FAKE + 4, None) == kgw.KGW_ERROR_MISALIGNED     # packed-32 needs 16 B
+    assert q(FAKE, 256, 256, 0, 0, FAKE, FAKE + 4, None) == kgw.KGW_ERROR_MISALIGNED     # bytes, rows: 8 B
+    assert q(FAKE + 8, 256, 256, 1, 2, FAKE, FAKE, None) == kgw.KGW_ERROR_MISALIGNED     # x needs 16 B
+    assert q(FAKE, 0, 256, 1, 2, None, None, None) == kgw.KGW_SUCCESS                    # empty
+    assert q(None, 256, 256, 1, 2, FAKE, FAKE, None) == kgw.KGW_ERROR_INVALID_VALUE
+
+
 def test_scale_shapes():
     import torch
     assert kgw.scale_shape(1280, 7, kgw.KGW_SCALES_U8) == ((10, 7), torch.uint8)
