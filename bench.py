@@ -19,9 +19,8 @@ and is null when the kernel sources changed after those counters were taken.
 `secondary` reports the other workloads (the 32-expert skewed-accumulate,
 fp8 and many-small-expert configs, and the tiny one) with the same timing,
 the fp8 workload with 32-token (MX-style) packed scales and with FP4
-operands, the m-grouped
-forward and dgrad of the fp8 workload's layer, and the on-device fp8
-quantiser on the fp8 workload's operand shapes.
+operands, the m-grouped forward and dgrad of the fp8 workload's layer, and the
+on-device fp8 and FP4 quantisers on the fp8 workload's operand shapes.
 
 Warm-up: from idle the GPU needs about 100 ms of continuous load before its
 clocks settle (the first launches of the headline run ~15% slower than the
@@ -167,10 +166,11 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
     return res
 
 
-def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0.0):
-    """kgw_quantize_fp8 on the fp8 workload's bf16 operand shape (A: (hidden, tokens_sum),
-    token_axis 1; B: (tokens_sum, n), token_axis 0).  HBM-bound: 2 bytes read and 1 written per
-    element plus one scale byte per 128."""
+def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0.0, fp4: bool = False):
+    """kgw_quantize_fp8 (or kgw_quantize_fp4, 32-token scales packed as the FP4 product takes
+    them) on the fp8 workload's bf16 operand shape (A: (hidden, tokens_sum), token_axis 1; B:
+    (tokens_sum, n), token_axis 0).  HBM-bound: per element 2 bytes read and 1 (fp8) or 0.5
+    (fp4) written, plus one scale byte per 128 (fp8) or 32 (fp4) tokens."""
     import torch
     import grouped_gemm_expert_offsets_amd as kgw
     import workloads
@@ -179,11 +179,13 @@ def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0
     shape = (H, T) if token_axis else (T, N)
     g = torch.Generator(device="cuda").manual_seed(1)
     x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
-    ms_step, launch_ms = time_call(lambda: kgw.kgw_quantize_fp8(x, token_axis), steps, warmup, min_warm_s)
+    fn = kgw.kgw_quantize_fp4 if fp4 else kgw.kgw_quantize_fp8
+    ms_step, launch_ms = time_call(lambda: fn(x, token_axis), steps, warmup, min_warm_s)
     mean_launch = sum(launch_ms) / len(launch_ms)
-    nbytes = 3.0 * x.numel() + x.numel() / 128
+    nbytes = (2.5 * x.numel() + x.numel() / 32) if fp4 else (3.0 * x.numel() + x.numel() / 128)
+    kind = "fp4" if fp4 else "fp8"
     res = {
-        "workload": f"quantize_fp8_{'A' if token_axis else 'B'} {shape[0]}x{shape[1]} bf16 (fp8 workload operand)",
+        "workload": f"quantize_{kind}_{'A' if token_axis else 'B'} {shape[0]}x{shape[1]} bf16 (fp8 workload operand)",
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "algorithmic_bytes": nbytes,
@@ -405,9 +407,10 @@ def main():
         for layout in ("nt", "nn"):
             r = run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds)
             sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
-        for axis in (1, 0):
-            r = run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds)
-            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+        for fp4 in (False, True):
+            for axis in (1, 0):
+                r = run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4)
+                sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
         line["secondary"] = sec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
