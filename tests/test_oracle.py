@@ -601,6 +601,28 @@ def test_fp4_quantizer_matches_generator_and_bounds():
     assert np.all(blk[nz] >= 3) and np.all(blk[nz] <= 6)
 
 
+def test_fp4_quantizer_special_blocks():
+    # closed-form cases of the stated rule: all-zero block -> scale 127 and zero codes; a NaN
+    # or an infinity -> scale 0xFF and zero codes; -0 keeps its sign (code 8); amax exactly
+    # 6 * 2^k -> byte 127 + k, one bf16 step above -> 128 + k; an amax below 6 * 2^-126 clamps the
+    # byte to 1
+    def col(vals):
+        v = np.zeros(32)
+        v[:len(vals)] = vals
+        return v
+    blocks = [col([]), col([1.0, np.nan]), col([np.inf, 2.0]), col([-0.0, 6.0]),
+              col([6.0 * 8, 3.0 * 8]), col([6.0 * 8 * (1 + 2.0 ** -7)]), col([2.0 ** -130])]
+    x = torch.tensor(np.concatenate(blocks)[None, :], dtype=torch.float32).to(torch.bfloat16)
+    q, s = oracle.quantize_fp4_tokens(x)
+    assert s[:, 0].tolist() == [127, 255, 255, 127, 130, 131, 1]
+    codes = np.stack([q[0] & 15, q[0] >> 4], axis=1).reshape(-1)
+    assert np.all(codes[0:32] == 0) and np.all(codes[32:64] == 0) and np.all(codes[64:96] == 0)
+    assert codes[96] == 8 and codes[97] == 7                         # -0 and 6 at scale 2^0
+    assert codes[128] == 7 and codes[129] == 5                      # 48 and 24 at scale 2^3: 6 and 3
+    assert codes[160] == 5                                          # bf16(48.375) = 48.5 at 2^4: 3.03 -> 3
+    assert codes[192] == 0                                          # 2^-130 (a bf16 subnormal) at 2^-126: 1/16
+
+
 def _dequant_fp4(q, s):
     codes = np.stack([q & 15, q >> 4], axis=2).reshape(q.shape[0], -1)
     return np.vectorize(oracle.e2m1_value)(codes) * np.repeat(np.exp2(s.T.astype(np.float64) - 127), 32, axis=1)
