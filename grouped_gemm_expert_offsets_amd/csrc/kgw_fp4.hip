@@ -22,8 +22,9 @@
 // 256x256 tile).  A and B move in 256-token stages (256 rows x 128 B: one full
 // 128-byte line per row) through 2-slot rings, their scale words through a
 // 2-slot scale ring; a stage covers four steps.  Stage y's 24 loads per wave
-// (8 A, 8 B, 4 + 4 scale words) are issued in steps 4y-5 and 4y-4, twelve each,
-// spread between the MFMAs, so they have two to three steps to land.  Slots only
+// (8 A, 8 B, 4 + 4 scale words) are issued in steps 4y-5, 4y-4 and 4y-3, eight
+// each, spread between the MFMAs, so they have two to four steps to land (two
+// steps of twelve measured 2% slower, four of six 2% slower again).  Slots only
 // change at stage boundaries, so the only barrier is at the start of each
 // stage's last step: it publishes the next stage (after all its loads have
 // landed) and certifies that the stage before has been read.  The fragments
@@ -164,11 +165,16 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
             }
         };
         // Loads of step s (and of the prologue's virtual steps): steps with
-        // s & 3 == 3 issue the first half of stage (s+5)/4, steps with s & 3 == 0
-        // the second half of stage (s+4)/4, twelve loads each.
+        // s & 3 == 3, 0 and 1 issue the first, second and third eight of the 24 loads
+        // of stage (s+5)/4, (s+4)/4 and (s+3)/4 (dma_half order: A, B, scale words).
+        auto dma_third = [&](int y, int k, int d) __attribute__((always_inline)) {
+            const int g = 8 * k + d;
+            dma_half(y, g >= 12 ? 1 : 0, g >= 12 ? g - 12 : g);
+        };
         auto dma_step = [&](int s, int d) __attribute__((always_inline)) {
-            if ((s & 3) == 3) dma_half((s + 5) / 4, 0, d);
-            else if ((s & 3) == 0) dma_half((s + 4) / 4, 1, d);
+            if ((s & 3) == 3) dma_third((s + 5) / 4, 0, d);
+            else if ((s & 3) == 0) dma_third((s + 4) / 4, 1, d);
+            else if ((s & 3) == 1) dma_third((s + 3) / 4, 2, d);
         };
 
         f32x16 acc[4][4];
@@ -210,27 +216,29 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
 
         // The partial vmcnt waits count only this item's direct loads.
         wait_vmcnt<0>();
-        // Prologue: stage 0 (virtual steps -5, -4) and the first half of stage 1
-        // (-1); step 0 needs stage 0, with the 12 loads of stage 1's half later.
+        // Prologue: stage 0 (virtual steps -5, -4, -3) and the first third of stage 1
+        // (-1); step 0 needs stage 0, with the 8 loads of stage 1's third later.
 #pragma unroll
-        for (int d = 0; d < 12; ++d) dma_step(-5, d);
+        for (int d = 0; d < 8; ++d) dma_step(-5, d);
 #pragma unroll
-        for (int d = 0; d < 12; ++d) dma_step(-4, d);
+        for (int d = 0; d < 8; ++d) dma_step(-4, d);
 #pragma unroll
-        for (int d = 0; d < 12; ++d) dma_step(-1, d);
-        wait_vmcnt<12>();
+        for (int d = 0; d < 8; ++d) dma_step(-3, d);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) dma_step(-1, d);
+        wait_vmcnt<8>();
         barrier_no_fence();
         Frags f0, f1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) read_one(0, r, f0);
 
         // Step s = 4y + Q.  At the start of a stage's last step (Q == 3) the next
-        // stage must have landed (its loads were issued in steps s-4 and s-3, none
-        // since): wait for all loads, then a barrier publishes it and certifies
+        // stage must have landed (its loads were issued in steps s-4, s-3 and s-2,
+        // none since): wait for all loads, then a barrier publishes it and certifies
         // that every wave is done reading the stage before (its slot is refilled
-        // from this step on).  16 MFMAs; the twelve loads of steps with Q == 3 or
-        // Q == 0 after MFMAs 4g + {0, 1, 2}; the 16 reads of step s+1 after MFMAs
-        // 8..15, two each.  sched_barrier(0) pins the interleaving.
+        // from this step on).  16 MFMAs; the eight loads of steps with Q != 2 after
+        // the even MFMAs; the 16 reads of step s+1 after MFMAs 8..15, two each.
+        // sched_barrier(0) pins the interleaving.
         auto body = [&](int s, auto q_tag, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
             constexpr int Q = decltype(q_tag)::value;
             wait_lgkmcnt0();
@@ -243,8 +251,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
             for (int k = 0; k < 16; ++k) {
                 mfma_one(cur, k);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (Q == 3 || Q == 0) {
-                    if ((k & 3) != 3) dma_step(s, 3 * (k >> 2) + (k & 3));
+                if constexpr (Q != 2) {
+                    if ((k & 1) == 0) dma_step(s, k >> 1);
                 }
                 if (k >= 8) {
                     read_one(s + 1, 2 * (k - 8), nxt);
