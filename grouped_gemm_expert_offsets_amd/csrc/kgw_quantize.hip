@@ -408,26 +408,54 @@ __device__ __forceinline__ uint32_t e8m0_for_amax_fp4(float amax) {
     return (uint32_t)(e < 1 ? 1 : (e > 254 ? 254 : e));
 }
 
-// e2m1 code of y (|y| <= 6 by the choice of scale; larger magnitudes give 7):
-// the magnitude index counts the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5
-// below |y|, a tie going to the even index (0, 2, 2, 4, 4, 6, 6); sign bit 8.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-    const float a = fabsf(y);
-    const uint32_t m = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
-                       (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
-                       (a > 5.0f ? 1u : 0u);
-    return m | ((__builtin_bit_cast(uint32_t, y) >> 28) & 8u);
+// 2^(e - 127) as an fp32, for e in [1, 254] (always normal).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
+
+// Magnitude bit patterns of the two bf16 of a word (sign bits cleared).  Their
+// integer order is the order of the magnitudes for finite values; +inf is
+// 0x7F80 and every NaN lies above it, so the largest pattern of a block gives
+// both its amax and whether it holds a NaN or an infinity.
+constexpr uint32_t kBf16MagMask = 0x7FFF7FFFu;
+constexpr uint32_t kBf16Inf = 0x7F80u;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
 }
 
-// Eight bf16 values (four words) times f -> eight e2m1 codes, value i in nibble i.
-__device__ __forceinline__ uint32_t e2m1_pack8(const i32x4& w, float f) {
-    uint32_t out = 0;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        out |= e2m1_code(bf16_lo((uint32_t)w[h]) * f) << (8 * h);
-        out |= e2m1_code(bf16_hi((uint32_t)w[h]) * f) << (8 * h + 4);
-    }
-    return out;
+// Unsigned maximum over an aligned group of G lanes (see group_max).
+template <int G>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+    static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
+    v = max(v, (uint32_t)dpp_mov<kDppXor1>((int)v));
+    v = max(v, (uint32_t)dpp_mov<kDppXor2>((int)v));
+    if constexpr (G >= 8) v = max(v, (uint32_t)dpp_mov<kDppHalfMirror>((int)v));
+    if constexpr (G >= 16) v = max(v, (uint32_t)dpp_mov<kDppMirror>((int)v));
+    return v;
+}
+
+// UE8M0 byte of a block from its largest magnitude pattern (255 for NaN / inf).
+__device__ __forceinline__ uint32_t fp4_block_exponent(uint32_t mag_bits) {
+    return mag_bits >= kBf16Inf ? 255u : e8m0_for_amax_fp4(__builtin_bit_cast(float, mag_bits << 16));
+}
+
+// Two bf16 (a word, the low half first) -> two e2m1 codes of value / scale in byte
+// SEL of `acc`, the first value in the low nibble: v_cvt_scalef32_pk_fp4_bf16.
+// For a power-of-two scale the division is exact, and the conversion rounds to
+// the nearest e2m1 value, ties to the even code, and saturates at 6.  That is
+// the encoding the format defines (checked on the GPU over every tie point, signed zeros and
+// values beyond 6).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t acc, uint32_t word, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, word), scale, SEL);
+}
+
+// Eight bf16 values (four words) / scale -> eight e2m1 codes, value i in nibble i.
+__device__ __forceinline__ uint32_t e2m1_pack8(const i32x4& w, float scale) {
+    uint32_t out = e2m1_pair<0>(0u, (uint32_t)w[0], scale);
+    out = e2m1_pair<1>(out, (uint32_t)w[1], scale);
+    out = e2m1_pair<2>(out, (uint32_t)w[2], scale);
+    return e2m1_pair<3>(out, (uint32_t)w[3], scale);
 }
 
 // tokens along the columns: x (rows, cols) -> q (rows, cols/2), scales with mn =
@@ -469,22 +497,14 @@ __global__ __launch_bounds__(NT) void quantize_fp4_cols(const uint16_t* __restri
         const int64_t r = rw + i;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float amax = 0.0f;
-            int bad = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float a = bf16_lo((uint32_t)cur[k][h]), b = bf16_hi((uint32_t)cur[k][h]);
-                amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
-                bad |= (not_finite(a) || not_finite(b)) ? 1 : 0;
-            }
-            amax = group_max<4>(amax);
-            bad = group_or<4>(bad);
-            const uint32_t e = bad ? 255u : e8m0_for_amax_fp4(amax);
+            const uint32_t m2 = max_u16x2(max_u16x2((uint32_t)cur[k][0] & kBf16MagMask, (uint32_t)cur[k][1] & kBf16MagMask),
+                                          max_u16x2((uint32_t)cur[k][2] & kBf16MagMask, (uint32_t)cur[k][3] & kBf16MagMask));
+            const uint32_t e = fp4_block_exponent(group_umax<4>(max(m2 & 0xFFFFu, m2 >> 16)));
             uint32_t word = 0;
             if constexpr (MX) word = (uint32_t)group_or<16>((int)(e << (8 * ((lane >> 2) & 3))));
             const int64_t t = tl + 512 * k;
             if (t >= cols) continue;
-            const uint32_t codes = bad ? 0u : e2m1_pack8(cur[k], inv_scale(e));
+            const uint32_t codes = e == 255u ? 0u : e2m1_pack8(cur[k], e8m0_scale(e));
             __builtin_nontemporal_store(codes, (uint32_t*)(q + r * (cols / 2) + t / 2));
             if constexpr (MX) {
                 if ((lane & 15) == 0) sc[4 * k + (lane >> 4)][16 * wave + i] = word;
@@ -570,40 +590,31 @@ __global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restri
             if (active) v[i] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + i) * cols + n0));
             else v[i] = i32x4{0, 0, 0, 0};
         }
-        float amax[8];
-        int bad = 0;                                     // bit j: column j holds a NaN or an infinity
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax[j] = 0.0f;
+        // largest magnitude pattern of columns 2h (low half) and 2h+1 (high half)
+        uint32_t mag[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float a = bf16_lo((uint32_t)v[i][h]), c = bf16_hi((uint32_t)v[i][h]);
-                amax[2 * h] = fmaxf(amax[2 * h], fabsf(a));
-                amax[2 * h + 1] = fmaxf(amax[2 * h + 1], fabsf(c));
-                bad |= (not_finite(a) ? 1 : 0) << (2 * h);
-                bad |= (not_finite(c) ? 1 : 0) << (2 * h + 1);
-            }
+            for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)v[i][h] & kBf16MagMask);
 #pragma unroll
-        for (int m = 8; m < 32; m <<= 1) {
+        for (int m = 8; m < 32; m <<= 1)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], m, 64));
-            bad |= __shfl_xor(bad, m, 64);
-        }
+            for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)__shfl_xor((int)mag[h], m, 64));
         uint32_t e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = ((bad >> j) & 1) ? 255u : e8m0_for_amax_fp4(amax[j]);
-        // column j's eight tokens: value i of the word is token t0 + i
+        for (int j = 0; j < 8; ++j) e[j] = fp4_block_exponent((j & 1) ? mag[j >> 1] >> 16 : mag[j >> 1] & 0xFFFFu);
+        // column j's eight tokens: value i of the word is token t0 + i; tokens 2p and
+        // 2p+1 of the column are joined into one bf16 pair (v_perm_b32) and converted
+        // together into byte p
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float f = inv_scale(e[j] == 255u ? 127u : e[j]);
-            uint32_t codes = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t w = (uint32_t)v[i][j >> 1];
-                codes |= e2m1_code(((j & 1) ? bf16_hi(w) : bf16_lo(w)) * f) << (4 * i);
-            }
-            if ((bad >> j) & 1) codes = 0;
+            const float sc_j = e8m0_scale(e[j] == 255u ? 127u : e[j]);
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t codes = e2m1_pair<0>(0u, __builtin_amdgcn_perm((uint32_t)v[1][j >> 1], (uint32_t)v[0][j >> 1], sel), sc_j);
+            codes = e2m1_pair<1>(codes, __builtin_amdgcn_perm((uint32_t)v[3][j >> 1], (uint32_t)v[2][j >> 1], sel), sc_j);
+            codes = e2m1_pair<2>(codes, __builtin_amdgcn_perm((uint32_t)v[5][j >> 1], (uint32_t)v[4][j >> 1], sel), sc_j);
+            codes = e2m1_pair<3>(codes, __builtin_amdgcn_perm((uint32_t)v[7][j >> 1], (uint32_t)v[6][j >> 1], sel), sc_j);
+            if (e[j] == 255u) codes = 0;
             codes_lds[par][8 * cg + j][8 * wave + tg] = codes;
         }
         const int blk = 2 * wave + (tg >> 2);            // 32-token block of the tile
