@@ -87,6 +87,37 @@ def test_special_blocks_both_axes(fmt):
     _check(xb.t().contiguous(), 1, fmt)
 
 
+def _tie_neighbour_column():
+    """Blocks whose maximum is 6 * 2^k (so the scale is 2^k) holding every e2m1 rounding
+    midpoint 0.25 .. 5 times 2^k and the bf16 values one unit in the last place either
+    side of it, both signs, for k = -3, 0 and 5: the encoder's tie and near-tie cases
+    away from scale 1."""
+    ties = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=torch.bfloat16)
+    bits = ties.view(torch.int16)
+    near = torch.cat([ties, (bits + 1).view(torch.bfloat16), (bits - 1).view(torch.bfloat16)]).float()
+    vals = torch.cat([near, -near])                                          # 42 values
+    blocks = []
+    for k in (-3, 0, 5):
+        for part in (vals[:31], vals[31:]):
+            b = torch.zeros(32)
+            b[0] = 6.0
+            b[1:1 + len(part)] = part
+            blocks.append(b * 2.0 ** k)
+    col = torch.cat(blocks + [torch.zeros(32)] * 2)                          # 8 blocks = 256 tokens
+    perm = torch.randperm(32, generator=torch.Generator().manual_seed(95))
+    shuffled = col.view(8, 32)[:, perm].reshape(-1)
+    return torch.stack([col, -col, shuffled, -shuffled, col.flip(0), shuffled.flip(0), col * 0.5, shuffled * 4],
+                       dim=1)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_tie_neighbours_at_several_scales(fmt):
+    xb = _tie_neighbour_column().to(torch.bfloat16)                          # (256, 8): tokens along rows
+    assert torch.equal(xb.float(), _tie_neighbour_column())                  # every value exact in bf16
+    _check(xb.contiguous(), 0, fmt)
+    _check(xb.t().contiguous(), 1, fmt)
+
+
 def test_quantised_operands_feed_the_fp4_wgrad():
     # end to end on the device: quantise bf16 A (hidden, T) and B (T, n), then kgw_wgrad_fp4 on
     # those bytes equals the oracle's FP4 weight gradient of the same bytes
