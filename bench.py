@@ -168,14 +168,17 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
 
 def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0.0, fp4: bool = False):
     """kgw_quantize_fp8 (or kgw_quantize_fp4, 32-token scales packed as the FP4 product takes
-    them) on the fp8 workload's bf16 operand shape (A: (hidden, tokens_sum), token_axis 1; B:
-    (tokens_sum, n), token_axis 0).  HBM-bound: per element 2 bytes read and 1 (fp8) or 0.5
-    (fp4) written, plus one scale byte per 128 (fp8) or 32 (fp4) tokens."""
+    them) on the bf16 operand shape of the product it feeds (A: (hidden, tokens_sum),
+    token_axis 1; B: (tokens_sum, n), token_axis 0): the fp8 workload's, or for fp4 the FP4
+    line's (the same counts rounded up to 256 tokens, as the FP4 product requires).
+    HBM-bound: per element 2 bytes read and 1 (fp8) or 0.5 (fp4) written, plus one scale byte
+    per 128 (fp8) or 32 (fp4) tokens."""
     import torch
     import grouped_gemm_expert_offsets_amd as kgw
     import workloads
     spec = workloads.config_spec("fp8", 1)
-    T, H, N = sum(spec["counts"]), spec["hidden"], spec["n"]
+    counts = workloads.counts_uniform(32, 8192, 256, 1) if fp4 else spec["counts"]
+    T, H, N = sum(counts), spec["hidden"], spec["n"]
     shape = (H, T) if token_axis else (T, N)
     g = torch.Generator(device="cuda").manual_seed(1)
     x = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
@@ -185,7 +188,8 @@ def run_quantize(token_axis: int, steps: int, warmup: int, min_warm_s: float = 0
     nbytes = (2.5 * x.numel() + x.numel() / 32) if fp4 else (3.0 * x.numel() + x.numel() / 128)
     kind = "fp4" if fp4 else "fp8"
     res = {
-        "workload": f"quantize_{kind}_{'A' if token_axis else 'B'} {shape[0]}x{shape[1]} bf16 (fp8 workload operand)",
+        "workload": f"quantize_{kind}_{'A' if token_axis else 'B'} {shape[0]}x{shape[1]} bf16 "
+                    f"({'fp4' if fp4 else 'fp8'} workload operand)",
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "algorithmic_bytes": nbytes,
