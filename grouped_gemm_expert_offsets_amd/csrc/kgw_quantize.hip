@@ -554,33 +554,34 @@ __global__ __launch_bounds__(NT) void quantize_fp4_cols(const uint16_t* __restri
 
 // tokens along the rows: x (rows, cols) -> q (cols, rows/2), the token axis made
 // contiguous (the FP4 weight gradient's B layout), scales with mn = cols.  A
-// workgroup takes 256 tokens x 64 columns: wave w tokens 64w .. 64w+63, lane l
-// columns 8*(l & 7) .. +7 and tokens 8*(l >> 3) .. +7 of the wave's 64 (each load
-// 8 rows x 128 bytes; eight consecutive tokens make one 4-byte code word per
-// column).  A 32-token block is 4 lanes (xor 8, 16).  The code words collect in
-// LDS so each column's 128 bytes leave as whole-line stores (scattered 4-byte
-// stores ran at a third of the speed); scales as bytes ((rows/32, cols)) or as the
-// 128-token groups' words, assembled through LDS.  A trailing 128-token half tile
-// is skipped by waves 2-3.
+// workgroup of 512 threads takes 256 tokens x 128 columns: wave w (0..7) tokens
+// 32w .. 32w+31 -- one 32-token block -- and lane l columns 8*(l & 15) .. +7 and
+// tokens 8*(l >> 4) .. +7 of the wave's 32 (each load 4 rows x 256 bytes; eight
+// consecutive tokens make one 4-byte code word per column).  The code words
+// collect in LDS so each column's 128 bytes leave as whole-line stores
+// (scattered 4-byte stores ran at a third of the speed); scales as bytes
+// ((rows/32, cols)) or as the 128-token groups' words, assembled through LDS.  A
+// trailing 128-token half tile is skipped by waves 4-7.
+constexpr int NT_FP4_ROWS = 512;
 template <int FMT>
-__global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restrict__ x, int64_t rows,
-                                                       int64_t cols, uint8_t* __restrict__ q,
-                                                       uint8_t* __restrict__ s) {
+__global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t cols, uint8_t* __restrict__ q,
+                                                                uint8_t* __restrict__ s) {
     constexpr bool MX = FMT == kScalesPacked32;
-    __shared__ uint32_t codes_lds[2][64][33];   // [column][token group of 8] (+1: bank spread)
-    __shared__ uint8_t red_e[2][8][64];         // [32-token block of the tile][column]
+    __shared__ uint32_t codes_lds[2][128][33];  // [column][token group of 8] (+1: bank spread)
+    __shared__ uint8_t red_e[2][8][128];        // [32-token block of the tile][column]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int cg = lane & 7, tg = lane >> 3;
-    const int64_t cchunks = (cols + 63) / 64;
+    const int cg = lane & 15, tg = lane >> 4;
+    const int64_t cchunks = (cols + 127) / 128;
     const int64_t tchunks = (rows + 255) / 256;
     const int64_t units = tchunks * cchunks;
     int par = 0;
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x, par ^= 1) {
         const int64_t b = u / cchunks;
-        const int64_t c0 = (u - b * cchunks) * 64;
+        const int64_t c0 = (u - b * cchunks) * 128;
         const int64_t n0 = c0 + 8 * cg;
-        const int64_t tw = 256 * b + 64 * wave;         // the wave's first token
+        const int64_t tw = 256 * b + 32 * wave;         // the wave's first token
         const bool wave_live = tw < rows;                // rows is a multiple of 128: whole waves
         const bool active = wave_live && n0 < cols;      // cols is a multiple of 8
         const int64_t t0 = tw + 8 * tg;
@@ -591,13 +592,14 @@ __global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restri
             else v[i] = i32x4{0, 0, 0, 0};
         }
         // largest magnitude pattern of columns 2h (low half) and 2h+1 (high half)
+        // over the lane's 8 tokens, then over the 4 lanes of the 32-token block
         uint32_t mag[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)v[i][h] & kBf16MagMask);
 #pragma unroll
-        for (int m = 8; m < 32; m <<= 1)
+        for (int m = 16; m < 64; m <<= 1)
 #pragma unroll
             for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)__shfl_xor((int)mag[h], m, 64));
         uint32_t e[8];
@@ -615,19 +617,18 @@ __global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restri
             codes = e2m1_pair<2>(codes, __builtin_amdgcn_perm((uint32_t)v[5][j >> 1], (uint32_t)v[4][j >> 1], sel), sc_j);
             codes = e2m1_pair<3>(codes, __builtin_amdgcn_perm((uint32_t)v[7][j >> 1], (uint32_t)v[6][j >> 1], sel), sc_j);
             if (e[j] == 255u) codes = 0;
-            codes_lds[par][8 * cg + j][8 * wave + tg] = codes;
+            codes_lds[par][8 * cg + j][4 * wave + tg] = codes;
         }
-        const int blk = 2 * wave + (tg >> 2);            // 32-token block of the tile
         if constexpr (!MX) {
-            if ((tg & 3) == 0 && active) {
+            if (tg == 0 && active) {
                 const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
                                   (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
-                *(i32x2*)(s + (8 * b + blk) * cols + n0) = sw;
+                *(i32x2*)(s + (8 * b + wave) * cols + n0) = sw;
             }
         } else {
-            if ((tg & 3) == 0) {
+            if (tg == 0) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) red_e[par][blk][8 * cg + j] = (uint8_t)e[j];
+                for (int j = 0; j < 8; ++j) red_e[par][wave][8 * cg + j] = (uint8_t)e[j];
             }
         }
         __syncthreads();
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(NT) void quantize_fp4_rows(const uint16_t* __restri
         if constexpr (MX) {
             // the tile's two 128-token groups: word (group, column) from blocks 4*group .. +3
             const int tid = threadIdx.x;
-            const int grp = tid >> 6, col = tid & 63;
+            const int grp = tid >> 7, col = tid & 127;
             const int64_t gg = 2 * b + grp;
             if (grp < 2 && c0 + col < cols && 128 * gg < rows) {
                 const uint32_t w = (uint32_t)red_e[par][4 * grp][col] | ((uint32_t)red_e[par][4 * grp + 1][col] << 8) |
@@ -684,15 +685,15 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_
             hipLaunchKernelGGL(quantize_fp4_cols<kScalesU8>, dim3((unsigned)blocks), dim3(NT), 0, stream,
                                (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
     } else {
-        int64_t blocks = ((rows + 255) / 256) * ((cols + 63) / 64);
-        const int64_t cap = (int64_t)num_cus * 16;
+        int64_t blocks = ((rows + 255) / 256) * ((cols + 127) / 128);
+        const int64_t cap = (int64_t)num_cus * 8;
         if (blocks > cap) blocks = cap;
         if (blocks < 1) blocks = 1;
         if (mx)
-            hipLaunchKernelGGL(quantize_fp4_rows<kScalesPacked32>, dim3((unsigned)blocks), dim3(NT), 0, stream,
-                               (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
+            hipLaunchKernelGGL(quantize_fp4_rows<kScalesPacked32>, dim3((unsigned)blocks), dim3(NT_FP4_ROWS), 0,
+                               stream, (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
         else
-            hipLaunchKernelGGL(quantize_fp4_rows<kScalesU8>, dim3((unsigned)blocks), dim3(NT), 0, stream,
+            hipLaunchKernelGGL(quantize_fp4_rows<kScalesU8>, dim3((unsigned)blocks), dim3(NT_FP4_ROWS), 0, stream,
                                (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
     }
     return hipGetLastError();
