@@ -10,8 +10,10 @@
 // Per block: amax = the largest |x|; the scale is the smallest power of two
 // 2^k with amax <= 448 * 2^k (448 = largest e4m3fn), stored as the biased
 // exponent k + 127 clamped to [1, 254] (127 for an all-zero block); every
-// element becomes e4m3fn(x * 2^-k), rounded to nearest, ties to even
-// (v_cvt_pk_fp8_f32; x * 2^-k is exact in fp32).  A block holding a NaN or an
+// element becomes e4m3fn(x * 2^-k), rounded to nearest, ties to even (tokens
+// along the columns: v_cvt_scalef32_pk_fp8_bf16 on bf16 pairs with the block's
+// scale; along the rows, where a lane's pairs span two columns' scales:
+// v_cvt_pk_fp8_f32 after the exact multiply by 2^-k).  A block holding a NaN or an
 // infinity gets scale byte 0xFF (the E8M0 NaN) and NaN bytes 0x7F.
 //
 // Roofline: HBM.  Per element 2 bytes read and 1 written, plus one scale byte
@@ -74,19 +76,6 @@ constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
 template <int G>
-__device__ __forceinline__ float group_max(float v) {
-    static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
-    auto step = [&](auto ctrl) {
-        v = fmaxf(v, __builtin_bit_cast(float, dpp_mov<decltype(ctrl)::value>(__builtin_bit_cast(int, v))));
-    };
-    step(std::integral_constant<int, kDppXor1>{});
-    step(std::integral_constant<int, kDppXor2>{});
-    if constexpr (G >= 8) step(std::integral_constant<int, kDppHalfMirror>{});
-    if constexpr (G >= 16) step(std::integral_constant<int, kDppMirror>{});
-    return v;
-}
-
-template <int G>
 __device__ __forceinline__ int group_or(int v) {
     static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
     v |= dpp_mov<kDppXor1>(v);
@@ -94,6 +83,52 @@ __device__ __forceinline__ int group_or(int v) {
     if constexpr (G >= 8) v |= dpp_mov<kDppHalfMirror>(v);
     if constexpr (G >= 16) v |= dpp_mov<kDppMirror>(v);
     return v;
+}
+
+// 2^(e - 127) as an fp32, for e in [1, 254] (always normal).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
+
+// Magnitude bit patterns of the two bf16 of a word (sign bits cleared).  Their
+// integer order is the order of the magnitudes for finite values; +inf is
+// 0x7F80 and every NaN lies above it, so the largest pattern of a block gives
+// both its amax and whether it holds a NaN or an infinity.
+constexpr uint32_t kBf16MagMask = 0x7FFF7FFFu;
+constexpr uint32_t kBf16Inf = 0x7F80u;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Unsigned maximum over an aligned group of G lanes (as group_or).
+template <int G>
+__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
+    static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
+    v = max(v, (uint32_t)dpp_mov<kDppXor1>((int)v));
+    v = max(v, (uint32_t)dpp_mov<kDppXor2>((int)v));
+    if constexpr (G >= 8) v = max(v, (uint32_t)dpp_mov<kDppHalfMirror>((int)v));
+    if constexpr (G >= 16) v = max(v, (uint32_t)dpp_mov<kDppMirror>((int)v));
+    return v;
+}
+
+// UE8M0 byte of a 448-range (e4m3fn) block from its largest magnitude pattern
+// (255 for NaN / inf).
+__device__ __forceinline__ uint32_t fp8_block_exponent(uint32_t mag_bits) {
+    return mag_bits >= kBf16Inf ? 255u : e8m0_for_amax(__builtin_bit_cast(float, mag_bits << 16));
+}
+
+// Four bf16 (two words, low halves first) / scale -> four e4m3fn bytes in that
+// order: v_cvt_scalef32_pk_fp8_bf16 writes a word's two values into the low or
+// high half of the result.  For a power-of-two scale the division is exact and
+// the conversion rounds to nearest even (checked on the GPU on every finite bf16
+// pattern at five scales for |value / scale| <= 448, subnormals and ties
+// included; the quantiser's scale keeps every value in that range).
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+__device__ __forceinline__ int e4m3_quad(int w0, int w1, float scale) {
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w1), scale, true);
+    return __builtin_bit_cast(int, r);
 }
 
 // Four fp32 -> four e4m3fn bytes (little-endian order).
@@ -163,17 +198,9 @@ __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* __res
         const int64_t r = rw + i;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float amax = 0.0f;
-            int bad = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const float a = bf16_lo((uint32_t)cur[k][h]), b = bf16_hi((uint32_t)cur[k][h]);
-                amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
-                bad |= (not_finite(a) || not_finite(b)) ? 1 : 0;
-            }
-            amax = group_max<RED>(amax);
-            bad = group_or<RED>(bad);
-            const uint32_t e = bad ? 255u : e8m0_for_amax(amax);
+            const uint32_t m2 = max_u16x2(max_u16x2((uint32_t)cur[k][0] & kBf16MagMask, (uint32_t)cur[k][1] & kBf16MagMask),
+                                          max_u16x2((uint32_t)cur[k][2] & kBf16MagMask, (uint32_t)cur[k][3] & kBf16MagMask));
+            const uint32_t e = fp8_block_exponent(group_umax<RED>(max(m2 & 0xFFFFu, m2 >> 16)));
             uint32_t word = 0;
             if constexpr (MX) {
                 // byte j of the 128-token group's word: the scale of its lanes 4j .. 4j+3
@@ -182,15 +209,12 @@ __global__ __launch_bounds__(NT) void quantize_tokens_cols(const uint16_t* __res
             const int64_t t = tl + 512 * k;
             if (t >= cols) continue;
             i32x2 out;
-            if (bad) {
+            if (e == 255u) {
                 out = i32x2{0x7F7F7F7F, 0x7F7F7F7F};
             } else {
-                const float f = inv_scale(e);
-                const i32x4 w = cur[k];
-                out[0] = cvt4(bf16_lo((uint32_t)w[0]) * f, bf16_hi((uint32_t)w[0]) * f, bf16_lo((uint32_t)w[1]) * f,
-                              bf16_hi((uint32_t)w[1]) * f);
-                out[1] = cvt4(bf16_lo((uint32_t)w[2]) * f, bf16_hi((uint32_t)w[2]) * f, bf16_lo((uint32_t)w[3]) * f,
-                              bf16_hi((uint32_t)w[3]) * f);
+                const float sc = e8m0_scale(e);
+                out[0] = e4m3_quad(cur[k][0], cur[k][1], sc);
+                out[1] = e4m3_quad(cur[k][2], cur[k][3], sc);
             }
             __builtin_nontemporal_store(out, (i32x2*)(q + r * cols + t));
             if ((lane & 15) == 0) sc[4 * k + (lane >> 4)][16 * wave + i] = MX ? word : e;
@@ -406,32 +430,6 @@ __device__ __forceinline__ uint32_t e8m0_for_amax_fp4(float amax) {
     const int k = E - 2 + ((bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
     const int e = k + 127;
     return (uint32_t)(e < 1 ? 1 : (e > 254 ? 254 : e));
-}
-
-// 2^(e - 127) as an fp32, for e in [1, 254] (always normal).
-__device__ __forceinline__ float e8m0_scale(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
-
-// Magnitude bit patterns of the two bf16 of a word (sign bits cleared).  Their
-// integer order is the order of the magnitudes for finite values; +inf is
-// 0x7F80 and every NaN lies above it, so the largest pattern of a block gives
-// both its amax and whether it holds a NaN or an infinity.
-constexpr uint32_t kBf16MagMask = 0x7FFF7FFFu;
-constexpr uint32_t kBf16Inf = 0x7F80u;
-typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
-__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                  __builtin_bit_cast(u16x2, b)));
-}
-
-// Unsigned maximum over an aligned group of G lanes (see group_max).
-template <int G>
-__device__ __forceinline__ uint32_t group_umax(uint32_t v) {
-    static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
-    v = max(v, (uint32_t)dpp_mov<kDppXor1>((int)v));
-    v = max(v, (uint32_t)dpp_mov<kDppXor2>((int)v));
-    if constexpr (G >= 8) v = max(v, (uint32_t)dpp_mov<kDppHalfMirror>((int)v));
-    if constexpr (G >= 16) v = max(v, (uint32_t)dpp_mov<kDppMirror>((int)v));
-    return v;
 }
 
 // UE8M0 byte of a block from its largest magnitude pattern (255 for NaN / inf).
