@@ -8,7 +8,8 @@
 //
 // Work decomposition: one item per (expert, K chunk, 256x256 output tile).
 // Items run expert-major, then K chunk (one unless split-K), then tile, M
-// first in columns of four tiles; a persistent grid of one workgroup per CU
+// first in columns of p.group_m tiles (four, or eight for short experts: see
+// the host's choice); a persistent grid of one workgroup per CU
 // strides over them, workgroup ids remapped so each XCD owns a contiguous run of
 // items (shared A/B panels in its L2).  An item whose expert has no tokens
 // zero-fills its tile in overwrite mode and does nothing in accumulate mode.
@@ -60,7 +61,6 @@ constexpr int BM = kBf16BM, BN = kBf16BN, BK = kBf16BK;
 constexpr int NT = 256;
 constexpr int TC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two K steps)
 constexpr int TR_STAGE = BK * 256 * 2;      // 16 KiB: 32 token rows x 512 B (one K step)
-constexpr int GROUP_M = 4;
 
 enum Pair { kTRTR = 0, kTRTC = 1, kTCTC = 2, kTCTR = 3 };
 
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         const int eo = c * p.num_experts + e;
         if (p.out_ptrs && !p.out_ptrs[eo]) continue;
         int tm, tn;
-        tile_coords(local, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
+        tile_coords(local, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
         const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
