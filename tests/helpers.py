@@ -88,3 +88,27 @@ def sample_rows(hidden: int, k: int, seed: int) -> np.ndarray:
     rows = {0, hidden - 1}
     rows.update(rng.integers(0, hidden, size=max(0, k - 2)).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def every_bf16_up_to(limit: float) -> torch.Tensor:
+    """Every finite bf16 value with |x| <= limit (both signs, zeros and subnormals
+    included), as float32 in increasing bit-pattern order."""
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    x = bits.view(torch.bfloat16).float()
+    return x[torch.isfinite(x) & (x.abs() <= limit)]
+
+
+def anchored_blocks(values: torch.Tensor, anchor: float, block: int, multiple: int, seed: int) -> torch.Tensor:
+    """`values` shuffled into blocks of `block` tokens whose first entry is `anchor`
+    (the block maximum, which fixes the block's scale), zero-padded to a multiple of
+    `multiple` tokens: every value meets the scale that the anchor selects."""
+    g = torch.Generator().manual_seed(seed)
+    v = values[torch.randperm(len(values), generator=g)]
+    per = block - 1
+    nblk = -(-len(v) // per)
+    body = torch.zeros(nblk * per)
+    body[:len(v)] = v
+    out = torch.cat([torch.full((nblk, 1), anchor), body.view(nblk, per)], dim=1)
+    flat = out.reshape(-1)
+    pad = (-len(flat)) % multiple
+    return torch.cat([flat, torch.zeros(pad)])

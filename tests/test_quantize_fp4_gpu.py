@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import grouped_gemm_expert_offsets_amd as kgw
+import helpers
 import oracle
 import workloads
 
@@ -116,6 +117,19 @@ def test_tie_neighbours_at_several_scales(fmt):
     assert torch.equal(xb.float(), _tie_neighbour_column())                  # every value exact in bf16
     _check(xb.contiguous(), 0, fmt)
     _check(xb.t().contiguous(), 1, fmt)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_every_bf16_value_under_a_fixed_scale(fmt):
+    """Every finite bf16 value with |x| <= 6, shuffled into 32-token blocks whose maximum is
+    6 (scale 2^0), the whole row then scaled by 2^k for eight k from -40 to 30: each value
+    meets the e2m1 encoding at its block's scale, on both token axes."""
+    v = helpers.every_bf16_up_to(6.0)
+    ks = (0, -12, 9, -40, 30, 1, -1, 5)
+    rows = [helpers.anchored_blocks(v, 6.0, 32, 256, seed=100 + i) * 2.0 ** k for i, k in enumerate(ks)]
+    x = torch.stack(rows).to(torch.bfloat16)                                 # (8, T): tokens along the columns
+    _check(x.contiguous(), 1, fmt)
+    _check(x.t().contiguous(), 0, fmt)
 
 
 def test_quantised_operands_feed_the_fp4_wgrad():

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import grouped_gemm_expert_offsets_amd as kgw
+import helpers
 import oracle
 import workloads
 
@@ -44,6 +45,19 @@ def test_tokens_along_columns_random(shape):
 @pytest.mark.parametrize("shape", [(384, 200), (1280, 72), (128, 8)])
 def test_tokens_along_rows_random(shape):
     _check(_spread_bf16(shape, 0, seed=72), 0)
+
+
+def test_every_bf16_value_under_a_fixed_scale():
+    """Every finite bf16 value with |x| <= 448, shuffled into 128-token blocks whose maximum
+    is 448 (scale 2^0), the whole row then scaled by 2^k for eight k from -40 to 30: each
+    value meets the e4m3fn rounding at its block's scale (subnormals and ties included), on
+    both token axes."""
+    v = helpers.every_bf16_up_to(448.0)
+    ks = (0, -12, 9, -40, 30, 1, -1, 5)
+    rows = [helpers.anchored_blocks(v, 448.0, 128, 128, seed=200 + i) * 2.0 ** k for i, k in enumerate(ks)]
+    x = torch.stack(rows).to(torch.bfloat16)                                 # (8, T): tokens along the columns
+    _check(x.contiguous(), 1)
+    _check(x.t().contiguous(), 0)
 
 
 def _special_column(n=128):
