@@ -120,9 +120,10 @@ __device__ __forceinline__ uint32_t fp8_block_exponent(uint32_t mag_bits) {
 // Four bf16 (two words, low halves first) / scale -> four e4m3fn bytes in that
 // order: v_cvt_scalef32_pk_fp8_bf16 writes a word's two values into the low or
 // high half of the result.  For a power-of-two scale the division is exact and
-// the conversion rounds to nearest even (checked on the GPU on every finite bf16
-// pattern at five scales for |value / scale| <= 448, subnormals and ties
-// included; the quantiser's scale keeps every value in that range).
+// the conversion rounds to nearest even wherever |value / scale| <= 448, which
+// the quantiser's scale guarantees (tests/test_quantize_gpu.py pushes every
+// finite bf16 value through it at block scales 2^-40 .. 2^30, subnormals and ties
+// included, and compares with the oracle bit for bit).
 typedef __attribute__((ext_vector_type(2))) short s16x2;
 __device__ __forceinline__ int e4m3_quad(int w0, int w1, float scale) {
     s16x2 r = {0, 0};
@@ -440,9 +441,10 @@ __device__ __forceinline__ uint32_t fp4_block_exponent(uint32_t mag_bits) {
 // Two bf16 (a word, the low half first) -> two e2m1 codes of value / scale in byte
 // SEL of `acc`, the first value in the low nibble: v_cvt_scalef32_pk_fp4_bf16.
 // For a power-of-two scale the division is exact, and the conversion rounds to
-// the nearest e2m1 value, ties to the even code, and saturates at 6.  That is
-// the encoding the format defines (checked on the GPU over every tie point, signed zeros and
-// values beyond 6).
+// the nearest e2m1 value, ties to the even code, and saturates at 6: the
+// encoding the format defines (tests/test_quantize_fp4_gpu.py pushes every finite
+// bf16 value through it at block scales 2^-40 .. 2^30, plus every tie point's
+// neighbours and signed zeros, and compares with the oracle bit for bit).
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1_pair(uint32_t acc, uint32_t word, float scale) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(acc, __builtin_bit_cast(bf16x2, word), scale, SEL);
