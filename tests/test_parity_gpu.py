@@ -341,6 +341,31 @@ def test_fp8_integer_inputs_with_scales_bit_exact(accumulate, native):
     assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
 
 
+@pytest.mark.parametrize("native", [False, True])
+def test_fp8_every_code_dequantised_exactly(native):
+    """A holds every finite e4m3fn code under per-row scales 2^-20 .. 2^20 and B is one-hot
+    (the code of 1.0 on its diagonal, scale 2^0), so each output element is one dequantised
+    A value: the device's dequantisation of every code at each of those scales must equal
+    the oracle's bit for bit (fp32 output)."""
+    T, hidden, n = 128, 256, 128
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # 0x7F, 0xFF: NaN
+    a = codes[(np.arange(hidden)[:, None] * T + np.arange(T)[None, :]) % len(codes)]
+    b = np.zeros((T, n), np.uint8)
+    b[np.arange(n), np.arange(n)] = 0x38                                             # e4m3fn 1.0
+    sfa = (127 + (np.arange(hidden) % 41) - 20).astype(np.uint8)[None, :]
+    sfb = np.full((1, n), 127, np.uint8)
+    off = torch.tensor([T], dtype=torch.int32)
+    assert len(np.unique(a)) == 254
+    fn = kgw.kgw_wgrad_fp8_native if native else kgw.kgw_wgrad_fp8
+    out = fn(torch.from_numpy(a).to(DEV), torch.from_numpy(sfa).to(DEV), torch.from_numpy(b).to(DEV),
+             torch.from_numpy(sfb).to(DEV), off.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.wgrad_fp8(a, sfa, b, sfb, off)
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
+
+
 def test_fp8_native_random_small_within_its_bound():
     counts = [128, 0, 384, 256, 640]
     wl = workloads.make_operands(counts, 264, 400, "fp8", torch.float32, False, seed=31, device=DEV)
