@@ -81,12 +81,14 @@ def profile_traffic(workload: str):
 
 
 def algorithmic_bytes(wl) -> float:
-    """Read A and B once, write the output once (read it too when accumulating), plus scales."""
+    """Read A and B once, write the output once (read it too when accumulating), plus scales.
+    In accumulate mode an expert without tokens is left untouched, so its output counts zero."""
     import torch
-    H, N, T, E = wl.hidden, wl.n, wl.tokens_sum, wl.num_experts
+    H, N, T = wl.hidden, wl.n, wl.tokens_sum
     el_in = 1 if wl.kind == "fp8" else 2
     el_out = 4 if wl.out_dtype == torch.float32 else 2
-    b = (H * T + T * N) * el_in + E * H * N * el_out * (2 if wl.accumulate else 1)
+    touched = sum(1 for c in wl.counts if c > 0) if wl.accumulate else len(wl.counts)
+    b = (H * T + T * N) * el_in + touched * H * N * el_out * (2 if wl.accumulate else 1)
     if wl.kind == "fp8":
         b += (T // 128) * (H + N)
     return float(b)
@@ -388,7 +390,8 @@ def main():
             "traffic": traffic,
             "traffic_source": traffic_src,
             "algorithmic_bytes": head["algorithmic_bytes"],
-            "kernel": "wgrad_bf16_kernel" if kind == "bf16" else "wgrad_fp8_kernel",
+            "kernel": ("wgrad_bf16_kernel" if kind == "bf16" else
+                       "wgrad_fp8_native_kernel" if args.native_fp8 else "wgrad_fp8_kernel"),
             "launch_ms_mean": head["launch_ms_mean"],
             "launch_ms_min": head["launch_ms_min"],
             "launch_ms_max": head["launch_ms_max"],

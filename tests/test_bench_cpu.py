@@ -46,7 +46,7 @@ def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
 
 def _wl(name):
     spec = workloads.config_spec(name, 1)
-    return SimpleNamespace(hidden=spec["hidden"], n=spec["n"], tokens_sum=sum(spec["counts"]),
+    return SimpleNamespace(hidden=spec["hidden"], n=spec["n"], tokens_sum=sum(spec["counts"]), counts=spec["counts"],
                            num_experts=len(spec["counts"]), kind=spec["kind"], out_dtype=spec["out_dtype"],
                            accumulate=spec["accumulate"])
 
@@ -59,8 +59,17 @@ def test_algorithmic_bytes_closed_form(name):
         inputs = H * T + T * N + (T // 128) * (H + N)          # e4m3 bytes + one scale byte per 128 tokens
     else:
         inputs = 2 * (H * T + T * N)                            # bf16
-    out = E * H * N * (4 if w.out_dtype == torch.float32 else 2)
+    # accumulate leaves experts without tokens untouched; overwrite zero-fills them
+    touched = sum(1 for c in w.counts if c > 0) if w.accumulate else E
+    out = touched * H * N * (4 if w.out_dtype == torch.float32 else 2)
     assert bench.algorithmic_bytes(w) == inputs + out * (2 if w.accumulate else 1)
+
+
+def test_skewed_accumulate_skips_empty_experts():
+    w = _wl("skewed")
+    assert w.accumulate and sum(1 for c in w.counts if c == 0) == 4
+    full = 2 * (w.hidden * w.tokens_sum + w.tokens_sum * w.n) + 32 * w.hidden * w.n * 4 * 2
+    assert bench.algorithmic_bytes(w) == full - 4 * w.hidden * w.n * 4 * 2
 
 
 def test_headline_workload_bytes_and_flops():
