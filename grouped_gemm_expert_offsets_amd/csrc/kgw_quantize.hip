@@ -576,6 +576,21 @@ __global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t*
     const int64_t cchunks = (cols + 127) / 128;
     const int64_t tchunks = (rows + 255) / 256;
     const int64_t units = tchunks * cchunks;
+    // unit u's input block for this lane (zeros for lanes outside the tensor)
+    auto load_unit = [&](int64_t u, i32x4 (&v)[8]) __attribute__((always_inline)) {
+        const int64_t b = u / cchunks;
+        const int64_t n0 = (u - b * cchunks) * 128 + 8 * cg;
+        const int64_t tw = 256 * b + 32 * wave;
+        const bool active = tw < rows && n0 < cols;
+        const int64_t t0 = tw + 8 * tg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (active) v[i] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + i) * cols + n0));
+            else v[i] = i32x4{0, 0, 0, 0};
+        }
+    };
+    i32x4 v[8], vn[8];
+    if (blockIdx.x < units) load_unit(blockIdx.x, v);
     int par = 0;
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x, par ^= 1) {
         const int64_t b = u / cchunks;
@@ -584,13 +599,6 @@ __global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t*
         const int64_t tw = 256 * b + 32 * wave;         // the wave's first token
         const bool wave_live = tw < rows;                // rows is a multiple of 128: whole waves
         const bool active = wave_live && n0 < cols;      // cols is a multiple of 8
-        const int64_t t0 = tw + 8 * tg;
-        i32x4 v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (active) v[i] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + i) * cols + n0));
-            else v[i] = i32x4{0, 0, 0, 0};
-        }
         // largest magnitude pattern of columns 2h (low half) and 2h+1 (high half)
         // over the lane's 8 tokens, then over the 4 lanes of the 32-token block
         uint32_t mag[4] = {0u, 0u, 0u, 0u};
@@ -631,6 +639,8 @@ __global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t*
                 for (int j = 0; j < 8; ++j) red_e[par][wave][8 * cg + j] = (uint8_t)e[j];
             }
         }
+        // the next unit's loads go out before this unit's code stores
+        if (u + gridDim.x < units) load_unit(u + gridDim.x, vn);
         __syncthreads();
         // codes: thread -> column tid >> 2, bytes 32*(tid & 3) .. +31 of the tile's 128
         {
@@ -656,6 +666,8 @@ __global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t*
                 ((uint32_t*)s)[gg * cols + c0 + col] = w;
             }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = vn[i];
     }
 }
 
