@@ -9,9 +9,10 @@
 // Work decomposition: one item per (expert, K chunk, 256x256 output tile).
 // Items run expert-major, then K chunk (one unless split-K), then tile, M
 // first in columns of p.group_m tiles (four, or eight for short experts: see
-// the host's choice); a persistent grid of one workgroup per CU
-// strides over them, workgroup ids remapped so each XCD owns a contiguous run of
-// items (shared A/B panels in its L2).  An item whose expert has no tokens
+// the host's choice); a persistent grid of one workgroup per CU strides over
+// them (for long experts, odd rounds take the slots in reverse), workgroup ids
+// remapped so each XCD owns a contiguous run of items (shared A/B panels in its
+// L2).  An item whose expert has no tokens
 // zero-fills its tile in overwrite mode and does nothing in accumulate mode.
 //
 // Inside an item (MFMA 32x32x16, fp32 accumulation): 4 waves, each a 128x128
@@ -126,7 +127,12 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     const int G = gridDim.x;
     const int slot = xcd_slot(blockIdx.x, G, p.num_xcds);
 
-    for (int item = slot; item < p.num_items; item += G) {
+    // Round r covers items [r*G, (r+1)*G); with p.snake the slots of odd rounds run in
+    // reverse, so a workgroup alternates between the front and the back of consecutive
+    // rounds (each XCD still holds a contiguous run of 32 items).
+    for (int r = 0; r * G < p.num_items; ++r) {
+        const int item = r * G + ((r & 1) && p.snake ? G - 1 - slot : slot);
+        if (item >= p.num_items) continue;
         const int ec = item / TT;
         const int local = item - ec * TT;
         const int e = ec / p.split;

@@ -171,7 +171,14 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     // tile, the output stores dominate) columns of eight.  Measured on one box, one
     // process: E=256 / hidden 7168 / N 2048 / 256 tokens per expert 4.07 -> 3.90 ms with
     // eight, while E=8 / 4096 / 2048 / ~4448 tokens went 0.482 -> 0.494 ms.
-    p.group_m = tokens_sum < (int64_t)kShortExpertTokens * num_experts ? 8 : 4;
+    const bool short_experts = tokens_sum < (int64_t)kShortExpertTokens * num_experts;
+    p.group_m = short_experts ? 8 : 4;
+    // Long experts: odd rounds of the persistent stride take the slots in reverse.  The
+    // workgroups that drew the shorter experts in one round draw the longer ones in the
+    // next, which evens out the per-CU token sums (balanced E=8: 0.4895 -> 0.4829 ms and
+    // 0.4924 -> 0.4847 ms, one box, one process).  With short experts it lost 2.8% on the
+    // E=256 workload (stores, not K sums, set its time), so it is off there.
+    p.snake = short_experts ? 0 : 1;
     int out_kind = out_dtype;              // KGW_OUT_* values are the kernels' output kinds
 
     // Split-K when planned and the caller's workspace holds the partials;

@@ -39,6 +39,7 @@ struct GroupedParams {
     int32_t scale_format;   // fp8 only: kScalesU8, kScalesPacked or kScalesPacked32
     int32_t ragged;         // bf16 layouts: A and B are per-expert (., n_e) blocks back to back
     int32_t group_m;        // bf16: M tiles per column of the tile order (4 or 8)
+    int32_t snake;          // bf16: odd rounds of the persistent stride run the slots in reverse
 };
 
 // Scales of the global 128-token block gb in layout FMT: the value for mn
