@@ -10,9 +10,9 @@
 // Items run expert-major, then K chunk (one unless split-K), then tile, M
 // first in columns of p.group_m tiles (four, or eight for short experts: see
 // the host's choice); a persistent grid of one workgroup per CU strides over
-// them (for long experts, odd rounds take the slots in reverse), workgroup ids
-// remapped so each XCD owns a contiguous run of items (shared A/B panels in its
-// L2).  An item whose expert has no tokens
+// them (for long experts, odd rounds take the slots in reverse).  For long
+// experts workgroup ids are remapped so each XCD owns a contiguous run of items
+// (shared A/B panels in its L2); for short ones the host turns the remap off.  An item whose expert has no tokens
 // zero-fills its tile in overwrite mode and does nothing in accumulate mode.
 //
 // Inside an item (MFMA 32x32x16, fp32 accumulation): 4 waves, each a 128x128
