@@ -279,11 +279,8 @@ def test_split_k_random(kind, out_dtype, accumulate):
         assert_bf16_close(got, ref, f"split-K {kind} bf16")
 
 
-@pytest.mark.parametrize("path", ["exact", "native"])
-@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("kind,path", [("bf16", "exact"), ("fp8", "exact"), ("fp8", "native")])
 def test_split_k_integer_bit_exact_and_same_as_one_pass(kind, path):
-    if kind == "bf16" and path == "native":
-        pytest.skip("native applies to fp8 only")
     wl = _split_case(kind, torch.float32, False, seed=62, integer_range=4)
     split = nan_filled((4, 320, 384), torch.float32)
     _run(wl, split, path, True)
