@@ -293,6 +293,16 @@ def cpu_baseline(target_seconds: float):
         flops += 2.0 * rows * wl.n * wl.counts[e]
     dt = time.perf_counter() - t0
     desc = ", ".join(f"expert {e} rows 0..{r - 1}" for e, r in plan)
+    # the same oracle on one thread: rows of expert 0 for about a tenth of the budget
+    one_rows = int(min(wl.hidden, max(1, (target_seconds / 10) * rate / threads // (2.0 * wl.n * wl.counts[0]))))
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(one_rows))
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    flops1 = 2.0 * one_rows * wl.n * wl.counts[0]
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -301,6 +311,9 @@ def cpu_baseline(target_seconds: float):
         "sample": f"{desc} of the {HEADLINE} workload, all N={wl.n} columns: {flops:.3e} FLOP in {dt:.1f} s "
                   f"(fp64 C oracle, OpenMP over rows)",
         "seconds": dt,
+        "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                          "sample": f"expert 0 rows 0..{one_rows - 1}, all N={wl.n} columns: {flops1:.3e} FLOP "
+                                    f"in {dt1:.1f} s"},
     }
 
 

@@ -58,6 +58,8 @@ def _load():
     lib.oracle_expert_range.restype = None
     lib.oracle_expert_range.argtypes = [p, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_wgrad_rows_bf16.restype = ctypes.c_int
     lib.oracle_wgrad_rows_bf16.argtypes = [p, p, i64, i64, i64, i64, p, i64, p]
     lib.oracle_wgrad_rows_fp8.restype = ctypes.c_int
@@ -149,6 +151,11 @@ def expert_range(offsets, e: int):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------

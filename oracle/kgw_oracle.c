@@ -80,6 +80,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following parallel loops (timing only: every row is summed in
+   the same order whatever the count, so results do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Rows rows[0..nrows) of Wgrad for the token range [begin, end), bf16 operands.
  * A: uint16 bf16 bits (hidden, tokens_sum); B: uint16 bf16 bits (tokens_sum, n).

@@ -663,3 +663,20 @@ def test_fp4_integer_operands_exact():
     assert np.all(A == np.round(A))
     assert np.array_equal(W[0], (A[:, :96].astype(np.int64) @ B[:, :96].astype(np.int64).T).astype(np.float64))
     assert np.array_equal(W[1], (A[:, 96:].astype(np.int64) @ B[:, 96:].astype(np.int64).T).astype(np.float64))
+
+
+def test_thread_count_does_not_change_results():
+    # every output row is summed in the same token order whatever the OpenMP thread count
+    g = torch.Generator().manual_seed(7)
+    A = torch.randn((64, 512), generator=g).to(torch.bfloat16)
+    B = torch.randn((512, 96), generator=g).to(torch.bfloat16)
+    off = torch.tensor([256, 512], dtype=torch.int32)
+    threads = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        one = oracle.wgrad_bf16(A, B, off)
+        oracle.set_num_threads(max(2, threads))
+        many = oracle.wgrad_bf16(A, B, off)
+    finally:
+        oracle.set_num_threads(threads)
+    assert np.array_equal(one, many)
