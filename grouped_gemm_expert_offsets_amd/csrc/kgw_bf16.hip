@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         else begin &= ~(2 * BK - 1);
         const int ksteps = ((end - begin) / (2 * BK)) * 2;
         if (ksteps == 0) {
-            if (!p.accumulate) zero_tile<OUT, BM, BN, NT>(p, eo, m0, n0, tid);
+            if (!p.accumulate) zero_slab_part<OUT, NT>(p, eo, local, TT, tid);
             continue;
         }
         const int rows_valid = (int)min<int64_t>(BM, H - m0);

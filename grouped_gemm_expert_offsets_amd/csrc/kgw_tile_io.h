@@ -38,6 +38,22 @@ __device__ __forceinline__ void zero_tile(const P& p, int e, int64_t m0, int64_t
     }
 }
 
+// Overwrite-mode output of an expert without tokens, written as contiguous parts:
+// part `part` of `parts` equal runs of 16-byte chunks of output matrix e (the
+// expert's whole hidden x n slab; n is a multiple of 8, so the slab is whole
+// chunks).  The `parts` items of one expert together cover its slab once.
+template <int OUT, int NT, class P>
+__device__ __forceinline__ void zero_slab_part(const P& p, int e, int part, int parts, int tid) {
+    constexpr int ESIZE = OUT == kOutF32 ? 4 : 2;
+    const int64_t chunks = p.hidden * p.n * ESIZE / 16;
+    const int64_t per = (chunks + parts - 1) / parts;
+    const int64_t c0 = (int64_t)part * per;
+    const int64_t c1 = min(chunks, c0 + per);
+    gbl_i32x4* base = (gbl_i32x4*)expert_output<OUT>(p, e);
+    const i32x4 z = {0, 0, 0, 0};
+    for (int64_t c = c0 + tid; c < c1; c += NT) __builtin_nontemporal_store(z, base + c);
+}
+
 // Rows [m_pass, m_pass + 64) x columns [nb, nb + 128) of one output matrix (base
 // `obase`, hidden x n) from their fp32 LDS image in `stage` (layout: see
 // store_wave_tile_staged), overwriting or (ACC) adding the old values first.
