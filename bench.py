@@ -1,32 +1,35 @@
 #!/usr/bin/env python3
 """Throughput of the K-grouped MoE weight-gradient GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S]
 
 One step = one kgw_wgrad_* call over one batch of seeded synthetic input
 already resident in HBM: offsets decode, tile scheduling, zero-fill, operand
 staging, the MFMA K loop and the epilogue all run inside that one launch.
-The headline workload is the balanced bf16 fc2 weight gradient (E=8,
-hidden 4096, N 2048, n_e = roundup256(4096*U(0.7,1.3)), seed 1, bf16 output,
-overwrite).  Useful work = 2 * hidden * N * tokens_sum FLOP.
+The headline workload is the largest of the five configurations: the fp8
+e4m3 weight gradient with one UE8M0 scale per 128 tokens (E=32, hidden 7168,
+N 4096, n_e = roundup128(8192*U(0.7,1.3)), seed 1, bf16 output, overwrite),
+through kgw_wgrad_fp8, the entry point that meets the accuracy bound.  Useful
+work = 2 * hidden * N * tokens_sum FLOP, priced against the dense fp8 MFMA
+peak (the exact kernel multiplies on the bf16 MFMA, whose rate is half that).
 
 Prints ONE JSON line.  `roofline.achieved` divides the useful FLOP of one
 launch by the launch's average duration, timed with HIP events recorded on
 the launch stream around every timed launch.  `roofline.traffic` comes from
 the rocprofv3 counter summary committed under profiles/ for this workload,
 and is null when the kernel sources changed after those counters were taken.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
-`secondary` reports the other workloads (the 32-expert skewed-accumulate,
-fp8 and many-small-expert configs, and the tiny one) with the same timing,
-the fp8 workload with 32-token (MX-style) packed scales and with FP4
-operands, the m-grouped forward and dgrad of the fp8 workload's layer, and the
-on-device fp8 and FP4 quantisers on the fp8 workload's operand shapes.
+`cpu_baseline` times the CPU oracle on a bounded sample of each of the five
+configurations (the headline's is the top-level value).  `secondary` reports
+the other workloads (balanced, skewed-accumulate, many-small and tiny bf16,
+the native fp8 path, 32-token (MX-style) scales, FP4 operands, the m-grouped
+forward and dgrad of the fp8 workload's layer, and the on-device fp8 and FP4
+quantisers) with the same timing.
 
 Warm-up: from idle the GPU needs about 100 ms of continuous load before its
-clocks settle (the first launches of the headline run ~15% slower than the
-steady state), so the default warm-up is 400 steps (about 0.2 s) and the
-secondary workloads warm up for at least 0.2 s each.  The numbers are
-steady-state throughput, as in a training loop.
+clocks settle, so every timed workload first runs for at least
+`--warmup-seconds` (headline, default 1 s) or `--secondary-warm-seconds`
+(default 0.2 s), and at least W launches.  The numbers are steady-state
+throughput, as in a training loop.
 """
 from __future__ import annotations
 
@@ -48,14 +51,18 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA
 PEAK_FP4_TFLOPS = 10066.3     # MI355X dense fp4 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
-HEADLINE = "balanced"
+HEADLINE = "fp8"
 
 
-# Sources the bf16 kernel (the headline workload's only kernel) is built from.
-BF16_KERNEL_SOURCES = ("kgw_bf16.hip", "kgw_device.h", "kgw_internal.h", "kgw_tile_io.h", "kgw_host.hip")
+# Sources each timed kernel is built from (the bf16 kernel for the bf16 workloads, the exact
+# fp8 kernel for the headline).
+KERNEL_SOURCES = {
+    "bf16": ("kgw_bf16.hip", "kgw_device.h", "kgw_internal.h", "kgw_tile_io.h", "kgw_host.hip"),
+    "fp8": ("kgw_fp8_exact.hip", "kgw_device.h", "kgw_internal.h", "kgw_tile_io.h", "kgw_host.hip"),
+}
 
 
-def kernel_source_hash(files=BF16_KERNEL_SOURCES) -> str:
+def kernel_source_hash(files=KERNEL_SOURCES["fp8"]) -> str:
     """Short sha256 over the named csrc files; a profile summary records it so that its
     counter readings are used only while the kernel they were taken on is unchanged."""
     h = hashlib.sha256()
@@ -66,9 +73,9 @@ def kernel_source_hash(files=BF16_KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def profile_traffic(workload: str):
+def profile_traffic(workload: str, kind: str):
     """HBM bytes per launch from profiles/<...>.md, if taken on the current kernel sources."""
-    cur = kernel_source_hash()
+    cur = kernel_source_hash(KERNEL_SOURCES[kind])
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         text = open(path).read()
         if f"workload: {workload}" not in text:
@@ -107,18 +114,25 @@ def make_call(wl, out, native=False):
     return lambda: fn(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out, accumulate=wl.accumulate)
 
 
-def time_call(call, steps: int, warmup: int, min_warm_s: float = 0.0):
+def time_call(call, steps: int, warmup: int, min_warm_s: float = 0.0, stats: dict = None):
     """Wall time of `steps` back-to-back calls plus HIP-event time of each launch, after
-    `warmup` untimed calls (continued until `min_warm_s` seconds have passed, if given)."""
+    `warmup` untimed calls (continued until `min_warm_s` seconds have passed, if given).
+    The warm-up actually run is recorded in `stats` (launches, seconds)."""
     import torch
     t_warm = time.perf_counter()
+    done = 0
     for _ in range(warmup):
         call()
+        done += 1
     torch.cuda.synchronize()
     while time.perf_counter() - t_warm < min_warm_s:
         for _ in range(4):
             call()
+        done += 4
         torch.cuda.synchronize()
+    if stats is not None:
+        stats["warmup_launches"] = done
+        stats["warmup_seconds"] = time.perf_counter() - t_warm
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -176,7 +190,8 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
         wl = workloads.make_operands(seed=seed, device="cuda", std=std, name=name, scale_block=scale_block, **spec)
     out = wl.C0 if wl.accumulate else torch.empty((wl.num_experts, wl.hidden, wl.n), dtype=wl.out_dtype,
                                                   device="cuda")
-    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup, min_warm_s)
+    warm = {}
+    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup, min_warm_s, warm)
     launch_ms.sort()
     mean_launch = sum(launch_ms) / len(launch_ms)
     res = {
@@ -189,6 +204,8 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
         "tflops": wl.flops / (mean_launch * 1e-3) / 1e12,
         "flops_per_launch": wl.flops,
         "algorithmic_bytes": algorithmic_bytes(wl),
+        "warmup_launches": warm["warmup_launches"],
+        "warmup_seconds": warm["warmup_seconds"],
     }
     peak = PEAK_FP8_TFLOPS if wl.kind == "fp8" else PEAK_BF16_TFLOPS
     res["frac_of_mfma_peak"] = res["tflops"] / peak
@@ -289,63 +306,74 @@ def run_fp4(steps: int, warmup: int, min_warm_s: float = 0.0):
     return res
 
 
-def cpu_baseline(target_seconds: float):
-    """Time the CPU oracle on a bounded sample of the headline workload.
-
-    The sample is whole experts in order (all rows, all N columns), the last one
-    cut to the rows that keep the estimated time near `target_seconds`.
-    """
+def _oracle_sample(name: str, target_seconds: float):
+    """Time the CPU oracle on a bounded sample of workload `name` (seed 1): whole rows of its
+    first non-empty expert (the tokens of that expert, all N columns), as many as fit in about
+    `target_seconds`, from the very tensors the GPU line consumes (generated on the device and
+    copied out).  The tiny workload is small enough to run whole."""
     import numpy as np
+    import torch
     import oracle
     import workloads
-    wl = workloads.make_workload(HEADLINE, seed=1, device="cuda")
-    A, B, off = wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu()
+    wl = workloads.make_workload(name, seed=1, device="cuda")
     threads = oracle.num_threads()
-    # calibrate on one row per thread of expert 0 (the oracle parallelises over rows)
-    cal_rows = min(wl.hidden, max(1, threads))
+    if name == "tiny":
+        A, B, off = wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu()
+        t0 = time.perf_counter()
+        oracle.wgrad_bf16(A, B, off)
+        dt = time.perf_counter() - t0
+        return {"value": wl.flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"the whole {name} workload: {wl.flops:.3e} FLOP in {dt:.3f} s", "seconds": dt}
+    e = next(i for i, c in enumerate(wl.counts) if c > 0)
+    begin = int(sum(wl.counts[:e]))
+    n_e = wl.counts[e]
+    rows = min(wl.hidden, max(threads, 1))
+    # one expert's tokens only, re-based so the oracle sees a one-expert problem
+    def take(r):
+        A = wl.A[:r, begin:begin + n_e].contiguous().cpu()
+        B = wl.B[begin:begin + n_e].contiguous().cpu()
+        off = torch.tensor([n_e], dtype=torch.int32)
+        if wl.kind == "bf16":
+            return lambda: oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(r))
+        sa = wl.sfa[begin // 128:(begin + n_e) // 128, :r].contiguous().cpu()
+        sb = wl.sfb[begin // 128:(begin + n_e) // 128].contiguous().cpu()
+        return lambda: oracle.wgrad_rows_fp8(A, sa, B, sb, off, 0, np.arange(r))
     t0 = time.perf_counter()
-    oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(cal_rows))
-    rate = 2.0 * cal_rows * wl.n * wl.counts[0] / max(time.perf_counter() - t0, 1e-6)
-    budget = target_seconds * rate            # FLOP to spend
-    plan = []
-    for e, n_e in enumerate(wl.counts):
-        if n_e == 0:
-            continue
-        per_row = 2.0 * wl.n * n_e
-        rows = int(min(wl.hidden, max(1, budget // per_row)))
-        plan.append((e, rows))
-        budget -= rows * per_row
-        if budget <= 0 or rows < wl.hidden:
-            break
-    flops = 0.0
+    take(rows)()                                            # calibration: one row per thread
+    per_row = (time.perf_counter() - t0) / rows
+    rows = int(min(wl.hidden, max(rows, target_seconds / max(per_row, 1e-9))))
+    call = take(rows)
+    del wl
+    torch.cuda.empty_cache()
     t0 = time.perf_counter()
-    for e, rows in plan:
-        oracle.wgrad_rows_bf16(A, B, off, e, np.arange(rows))
-        flops += 2.0 * rows * wl.n * wl.counts[e]
+    call()
     dt = time.perf_counter() - t0
-    desc = ", ".join(f"expert {e} rows 0..{r - 1}" for e, r in plan)
-    # the same oracle on one thread: rows of expert 0 for about a tenth of the budget
-    one_rows = int(min(wl.hidden, max(1, (target_seconds / 10) * rate / threads // (2.0 * wl.n * wl.counts[0]))))
+    flops = 2.0 * rows * workloads.config_spec(name, 1)["n"] * n_e
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"expert {e} ({n_e} tokens) rows 0..{rows - 1}, all N columns of the {name} workload: "
+                      f"{flops:.3e} FLOP in {dt:.1f} s (fp64 C oracle, OpenMP over rows)",
+            "seconds": dt}
+
+
+def cpu_baseline(target_seconds: float):
+    """The CPU oracle on a bounded sample of every configuration (about `target_seconds` in
+    all), plus a one-thread sample of the balanced workload; the headline's is the top level."""
+    import oracle
+    per = {}
+    names = ["tiny", "balanced", "skewed", "fp8", "many_small"]
+    for name in names:
+        per[name] = _oracle_sample(name, target_seconds / (len(names) - 1))
+    threads = oracle.num_threads()
     oracle.set_num_threads(1)
     try:
-        t1 = time.perf_counter()
-        oracle.wgrad_rows_bf16(A, B, off, 0, np.arange(one_rows))
-        dt1 = time.perf_counter() - t1
+        one = _oracle_sample("balanced", max(1.0, target_seconds / 20))
     finally:
         oracle.set_num_threads(threads)
-    flops1 = 2.0 * one_rows * wl.n * wl.counts[0]
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{desc} of the {HEADLINE} workload, all N={wl.n} columns: {flops:.3e} FLOP in {dt:.1f} s "
-                  f"(fp64 C oracle, OpenMP over rows)",
-        "seconds": dt,
-        "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
-                          "sample": f"expert 0 rows 0..{one_rows - 1}, all N={wl.n} columns: {flops1:.3e} FLOP "
-                                    f"in {dt1:.1f} s"},
-    }
+    head = dict(per[HEADLINE])
+    head["per_config"] = {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                          for k, v in per.items()}
+    head["single_thread"] = {k: v for k, v in one.items() if k != "kind"}
+    return head
 
 
 def copy_calibration(gib: float = 1.0):
@@ -363,14 +391,16 @@ def copy_calibration(gib: float = 1.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="the headline's warm-up runs at least this long (clock settling)")
     ap.add_argument("--secondary-warm-seconds", type=float, default=0.2)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--native-fp8", action="store_true", help="time kgw_wgrad_fp8_native for fp8 workloads")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -393,19 +423,23 @@ def main():
         copy_calibration()
         return
 
-    head = run_workload(args.workload, args.steps, args.warmup, native=args.native_fp8)
+    head = run_workload(args.workload, args.steps, args.warmup, native=args.native_fp8,
+                        min_warm_s=args.warmup_seconds)
     import workloads
-    spec = workloads.config_spec(args.workload.replace("_native", ""), 1)
-    traffic, traffic_src = profile_traffic(head["workload"])
+    spec = workloads.config_spec(args.workload, 1)
     kind = spec["kind"]
+    traffic, traffic_src = profile_traffic(head["workload"], kind)
     peak = PEAK_FP8_TFLOPS if kind == "fp8" else PEAK_BF16_TFLOPS
+    value = head["flops_per_launch"] / (head["ms_per_step"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
-        "value": head["flops_per_launch"] / (head["ms_per_step"] * 1e-3) / 1e12,
+        "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches": head["warmup_launches"],
+        "warmup_seconds": round(head["warmup_seconds"], 3),
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -413,7 +447,9 @@ def main():
         "dtype": "fp8" if kind == "fp8" else "bf16",
         "data": "synthetic (seeded; shapes and count distributions of the pages' MoE workloads)",
         "config": {
-            "workload": workloads.DESCRIPTIONS[args.workload.replace("_native", "")],
+            "workload": workloads.DESCRIPTIONS[args.workload],
+            "entry_point": ("kgw_wgrad_bf16" if kind == "bf16" else
+                            "kgw_wgrad_fp8_native" if args.native_fp8 else "kgw_wgrad_fp8"),
             "num_experts": len(spec["counts"]),
             "hidden": spec["hidden"],
             "n": spec["n"],
@@ -424,7 +460,7 @@ def main():
             "accumulate": spec["accumulate"],
             "parallelism": "single GPU",
         },
-        "frac_of_mfma_peak": head["flops_per_launch"] / (head["ms_per_step"] * 1e-3) / 1e12 / peak,
+        "frac_of_mfma_peak": value / peak,
         "roofline": {
             "bound": "mfma",
             "achieved": head["tflops"],
@@ -440,31 +476,33 @@ def main():
             "launch_ms_min": head["launch_ms_min"],
             "launch_ms_max": head["launch_ms_max"],
         },
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(KERNEL_SOURCES[kind]),
     }
+    if kind == "fp8" and not args.native_fp8:
+        # the exact kernel multiplies on the bf16 MFMA: its own rate ceiling is the bf16 peak
+        line["roofline"]["frac_of_bf16_mfma_peak"] = head["tflops"] / PEAK_BF16_TFLOPS
     if not args.no_secondary:
         sec = []
-        sec_steps, sec_warm = max(5, args.steps // 10), 2
-        for name, native, block in (("tiny", False, 128), ("skewed", False, 128), ("fp8", False, 128),
-                                    ("fp8", True, 128), ("fp8", False, 32), ("fp8", True, 32),
-                                    ("many_small", False, 128)):
-            if name == args.workload:
+        sec_steps, sec_warm = max(5, args.steps // 5), 2
+
+        def add(r):
+            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+
+        for name, native, block in (("balanced", False, 128), ("skewed", False, 128), ("fp8", True, 128),
+                                    ("fp8", False, 32), ("fp8", True, 32), ("many_small", False, 128),
+                                    ("tiny", False, 128)):
+            if name == args.workload and native == args.native_fp8 and block == 128:
                 continue
-            r = run_workload(name, sec_steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
-                             scale_block=block)
-            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
-        if args.workload == HEADLINE:
-            r = run_flushed(HEADLINE, 30, 50)
-            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
-        r = run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds)
-        sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+            steps = sec_steps * 10 if name in ("balanced", "tiny") else sec_steps
+            add(run_workload(name, steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
+                             scale_block=block))
+        add(run_flushed("balanced", 30, 50))
+        add(run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds))
         for layout in ("nt", "nn"):
-            r = run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds)
-            sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+            add(run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds))
         for fp4 in (False, True):
             for axis in (1, 0):
-                r = run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4)
-                sec.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+                add(run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4))
         line["secondary"] = sec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -30,7 +30,7 @@ __all__ = [
     "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT",
     "KGW_LAYOUT_NN",
     "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
-    "kgw_validate_offsets",
+    "kgw_validate_offsets", "kgw_check_offsets",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
     "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16", "KGW_OUT_FP16",
@@ -66,8 +66,8 @@ _lib = None
 # Every symbol include/kgw.h declares.
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
                     "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16",
-                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_status_string",
-                    "kgw_device_info")
+                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_check_offsets",
+                    "kgw_status_string", "kgw_device_info")
 
 
 def load_library():
@@ -104,6 +104,8 @@ def load_library():
     lib.kgw_validate_offsets_host.argtypes = [p, i32, i64, i32, ctypes.POINTER(i32)]
     lib.kgw_validate_offsets.restype = ctypes.c_int
     lib.kgw_validate_offsets.argtypes = [p, i32, i64, i32, ctypes.POINTER(i32), p]
+    lib.kgw_check_offsets.restype = ctypes.c_int
+    lib.kgw_check_offsets.argtypes = [p, i32, i64, i32, p, p]
     lib.kgw_status_string.restype = ctypes.c_char_p
     lib.kgw_status_string.argtypes = [ctypes.c_int]
     lib.kgw_device_info.restype = ctypes.c_int
@@ -543,6 +545,22 @@ def kgw_validate_offsets(offsets: torch.Tensor, tokens_sum: int, alignment: int,
         _check(st, f"kgw_validate_offsets (first bad expert {bad.value})")
 
 
+def kgw_check_offsets(offsets: torch.Tensor, tokens_sum: int, alignment: int,
+                      result: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Queue the offsets check on the device (no synchronisation): returns a one-element
+    int32 device tensor that will hold the first bad expert, or -1 (`result` if given)."""
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous 1-D int32 tensor")
+    if result is None:
+        result = torch.empty(1, dtype=torch.int32, device=offsets.device)
+    elif result.dtype != torch.int32 or result.numel() < 1 or result.device != offsets.device:
+        raise ValueError("result must be an int32 tensor on the offsets' device")
+    st = load_library().kgw_check_offsets(_ptr(offsets), offsets.numel(), int(tokens_sum), int(alignment),
+                                          _ptr(result), _stream_ptr(stream))
+    _check(st, "kgw_check_offsets")
+    return result
+
+
 def kgw_device_info() -> dict:
     cus, g950, xcds = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(load_library().kgw_device_info(ctypes.byref(cus), ctypes.byref(g950), ctypes.byref(xcds)),
@@ -552,15 +570,20 @@ def kgw_device_info() -> dict:
 
 def wgrad(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, *, sfa: Optional[torch.Tensor] = None,
           sfb: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-          out_dtype: Optional[torch.dtype] = None, accumulate: bool = False, validate: bool = False) -> torch.Tensor:
+          out_dtype: Optional[torch.dtype] = None, accumulate: bool = False, check: bool = True) -> torch.Tensor:
     """Dispatch on operand dtype like the cuDNN wrapper: bf16 operands take no scales
-    (any scale is a ValueError, section "BF16 contract"); fp8 operands need both."""
+    (any scale is a ValueError, section "BF16 contract"); fp8 operands need both.
+
+    check=True (the default, like the cuDNN page's wrapper, which rejects malformed or
+    unaligned offsets: section "Scheduling, cache, and errors") validates the offsets first,
+    which costs one synchronising copy of them to the host; check=False skips it and the
+    kernels clamp malformed ranges instead (see kgw_check_offsets for an asynchronous flag)."""
     if a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16:
         if sfa is not None or sfb is not None:
             raise ValueError("bf16 operands take no scale tensors")
         return kgw_wgrad_bf16(a, b, offsets, out, out_dtype=out_dtype or torch.float32, accumulate=accumulate,
-                              validate=validate)
+                              validate=check)
     if a.dtype in (torch.float8_e4m3fn, torch.uint8) and b.dtype in (torch.float8_e4m3fn, torch.uint8):
         return kgw_wgrad_fp8(a, sfa, b, sfb, offsets, out, out_dtype=out_dtype or torch.bfloat16,
-                             accumulate=accumulate, validate=validate)
+                             accumulate=accumulate, validate=check)
     raise ValueError(f"unsupported operand dtypes {a.dtype}, {b.dtype}")

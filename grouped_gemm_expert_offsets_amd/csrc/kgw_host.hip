@@ -398,6 +398,20 @@ kgw_status_t kgw_validate_offsets(const int32_t* offsets, int32_t num_experts, i
     return kgw_validate_offsets_host(host.data(), num_experts, tokens_sum, alignment, bad_expert);
 }
 
+kgw_status_t kgw_check_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                               int32_t alignment, int32_t* result, void* stream) {
+    if (!offsets || !result || num_experts < 1 || alignment < 1 || tokens_sum < 0) return KGW_ERROR_INVALID_VALUE;
+    if (num_experts > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
+    if (((uintptr_t)offsets | (uintptr_t)result) & 3u) return KGW_ERROR_MISALIGNED;
+    DeviceProps d;
+    const kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    const hipError_t err = kgw::launch_check_offsets(offsets, num_experts, tokens_sum, alignment, result,
+                                                     (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
 const char* kgw_status_string(kgw_status_t status) {
     switch (status) {
         case KGW_SUCCESS: return "success";

@@ -103,6 +103,9 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_
                                void* q, void* s, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8_native(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
 hipError_t launch_wgrad_fp4(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// First expert whose count breaks the offsets contract, or -1, into result[0] (one workgroup).
+hipError_t launch_check_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum, int32_t alignment,
+                                int32_t* result, hipStream_t stream);
 hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

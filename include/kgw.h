@@ -404,6 +404,21 @@ kgw_status_t kgw_validate_offsets(const int32_t* offsets, int32_t num_experts, i
                                   int32_t alignment, int32_t* bad_expert, void* stream);
 
 /*
+ * kgw_check_offsets -- the same check on DEVICE offsets, kept on the device: a
+ * kernel queued on `stream` writes to result[0] (a device int32) the first
+ * offending expert, or -1 when the offsets meet the contract.  Asynchronous and
+ * stream-ordered like the products (no copy to the host, no synchronisation, no
+ * allocation), so a caller can queue it next to a kgw_wgrad_* call and read the
+ * flag whenever it next synchronises.  The products clamp malformed ranges into
+ * [0, tokens_sum) by themselves (see the conventions above); this is how a caller
+ * that cannot afford kgw_validate_offsets' synchronisation learns that they did.
+ * KGW_ERROR_INVALID_VALUE for NULL pointers, num_experts < 1, alignment < 1 or
+ * tokens_sum < 0; KGW_ERROR_MISALIGNED for pointers not 4-byte aligned.
+ */
+kgw_status_t kgw_check_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,
+                               int32_t alignment, int32_t* result, void* stream);
+
+/*
  * kgw_status_string -- static description of a status code; never NULL.
  */
 const char* kgw_status_string(kgw_status_t status);

@@ -265,3 +265,25 @@ def test_fp4_argument_errors(lib):
     assert f(sa=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED       # packed scale words
     assert f(N=500) == kgw.KGW_ERROR_MISALIGNED
     assert f(A=FAKE + 8) == kgw.KGW_ERROR_MISALIGNED
+
+
+def test_check_offsets_argument_errors(lib):
+    # kgw_check_offsets rejects bad arguments on the host before touching a device
+    bad = kgw.KGW_ERROR_INVALID_VALUE
+    assert lib.kgw_check_offsets(None, 4, 1024, 256, FAKE, None) == bad
+    assert lib.kgw_check_offsets(FAKE, 4, 1024, 256, None, None) == bad
+    assert lib.kgw_check_offsets(FAKE, 0, 1024, 256, FAKE, None) == bad
+    assert lib.kgw_check_offsets(FAKE, 4, 1024, 0, FAKE, None) == bad
+    assert lib.kgw_check_offsets(FAKE, 4, -1, 256, FAKE, None) == bad
+    assert lib.kgw_check_offsets(FAKE + 2, 4, 1024, 256, FAKE, None) == kgw.KGW_ERROR_MISALIGNED
+    assert lib.kgw_check_offsets(FAKE, 70000, 1024, 256, FAKE, None) == kgw.KGW_ERROR_UNSUPPORTED
+
+
+def test_wgrad_wrapper_checks_offsets_by_default():
+    # The high-level wrapper validates offsets unless told not to (the cuDNN wrapper rejects
+    # malformed offsets); the raw kgw_wgrad_* bindings stay asynchronous and do not.
+    import inspect
+    assert inspect.signature(kgw.wgrad).parameters["check"].default is True
+    for fn in (kgw.kgw_wgrad_bf16, kgw.kgw_wgrad_fp8, kgw.kgw_wgrad_fp8_native, kgw.kgw_wgrad_bf16_ex,
+               kgw.kgw_wgrad_fp8_ex, kgw.kgw_wgrad_fp4):
+        assert inspect.signature(fn).parameters["validate"].default is False, fn.__name__

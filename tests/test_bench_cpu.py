@@ -24,24 +24,35 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_only_while_the_profiled_sources_are_unchanged(monkeypatch):
-    traffic, src = bench.profile_traffic("balanced")
-    if traffic is not None:                      # the committed summary matches these sources
-        assert src.startswith("profiles" + os.sep)
-        assert 5e8 < traffic < 5e9
+    for workload, kind in (("balanced", "bf16"), ("fp8", "fp8")):
+        traffic, src = bench.profile_traffic(workload, kind)
+        if traffic is not None:                  # the committed summary matches these sources
+            assert src.startswith("profiles" + os.sep)
+            assert 5e8 < traffic < 5e10
     monkeypatch.setattr(bench, "kernel_source_hash", lambda files=None: "0000000000000000")
-    assert bench.profile_traffic("balanced") == (None, None)
-    assert bench.profile_traffic("no such workload") == (None, None)
+    assert bench.profile_traffic("balanced", "bf16") == (None, None)
+    assert bench.profile_traffic("fp8", "fp8") == (None, None)
+    assert bench.profile_traffic("no such workload", "bf16") == (None, None)
 
 
-def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
+@pytest.mark.parametrize("kind,main", [("bf16", "kgw_bf16.hip"), ("fp8", "kgw_fp8_exact.hip")])
+def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch, kind, main):
     csrc = tmp_path / "grouped_gemm_expert_offsets_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for name in bench.BF16_KERNEL_SOURCES:
+    for name in bench.KERNEL_SOURCES[kind]:
         (csrc / name).write_text("x")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    h0 = bench.kernel_source_hash()
-    (csrc / "kgw_bf16.hip").write_text("y")
-    assert bench.kernel_source_hash() != h0
+    h0 = bench.kernel_source_hash(bench.KERNEL_SOURCES[kind])
+    (csrc / main).write_text("y")
+    assert bench.kernel_source_hash(bench.KERNEL_SOURCES[kind]) != h0
+
+
+def test_headline_is_the_largest_configuration():
+    # the headline runs the configuration with the most useful work, through the entry point
+    # that meets the accuracy bound
+    flops = {n: 2 * s["hidden"] * s["n"] * sum(s["counts"])
+             for n, s in ((n, workloads.config_spec(n, 1)) for n in workloads.CONFIG_NAMES)}
+    assert bench.HEADLINE == max(flops, key=flops.get) == "fp8"
 
 
 def _wl(name):
@@ -73,8 +84,9 @@ def test_skewed_accumulate_skips_empty_experts():
 
 
 def test_headline_workload_bytes_and_flops():
-    # balanced: E=8, hidden 4096, N 2048, tokens_sum 35584, bf16 output
-    w = _wl("balanced")
-    assert (w.num_experts, w.hidden, w.n, w.tokens_sum) == (8, 4096, 2048, 35584)
-    assert bench.algorithmic_bytes(w) == 571473920.0
-    assert 2 * w.hidden * w.n * w.tokens_sum == 597000454144
+    # fp8: E=32, hidden 7168, N 4096, tokens_sum 264320, e4m3 operands, bf16 output
+    w = _wl("fp8")
+    assert (w.num_experts, w.hidden, w.n, w.tokens_sum) == (32, 7168, 4096, 264320)
+    T = 264320
+    assert bench.algorithmic_bytes(w) == 7168 * T + T * 4096 + (T // 128) * (7168 + 4096) + 32 * 7168 * 4096 * 2
+    assert 2 * w.hidden * w.n * w.tokens_sum == 2 * 7168 * 4096 * 264320

@@ -2,7 +2,10 @@
 
 Inputs are seeded and synthetic (workloads/); the oracle runs on host copies
 of exactly the tensors the GPU consumed.  Small and mid sizes are compared
-element by element; the full-size workloads compare sampled rows, which the
+element by element, including mid-size cases with more work items than CUs on
+both branches of the persistent schedule.  At full size every overwrite-mode
+output starts as NaN and must come back without one; the balanced workload is
+then compared element by element, the larger ones on sampled rows that the
 oracle computes one by one, plus whole-tensor properties (zero-filled and
 untouched experts) checked on every element.
 """
@@ -149,6 +152,33 @@ def test_validate_offsets_on_device():
         kgw.kgw_validate_offsets(torch.tensor([256, 128, 768], dtype=torch.int32, device=DEV), 768, 256)
     with pytest.raises(ValueError):
         kgw.kgw_validate_offsets(good, 1024, 256)
+
+
+def test_check_offsets_flag_on_device():
+    # the asynchronous device check flags the same first bad expert as the host check
+    cases = [([256, 256, 768], 768, 256), ([256, 128, 768], 768, 256), ([256, 512], 768, 256),
+             ([-256, 0], 0, 256), ([128, 384], 384, 128), ([128, 384], 384, 256), ([0, 0, 0], 0, 256)]
+    rng = np.random.default_rng(3)
+    big = np.cumsum(256 * rng.integers(0, 4, size=3000)).astype(np.int32)
+    cases.append((big.tolist(), int(big[-1]), 256))
+    broken = big.copy()
+    broken[2500:] += 128                                           # expert 2500 loses alignment
+    cases.append((broken.tolist(), int(broken[-1]), 256))
+    for offs, T, align in cases:
+        want = kgw.kgw_validate_offsets_host(offs, T, align)[1]
+        flag = kgw.kgw_check_offsets(torch.tensor(offs, dtype=torch.int32, device=DEV), T, align)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == want, (offs[:4], T, align)
+
+
+def test_wgrad_wrapper_rejects_malformed_offsets():
+    wl = workloads.make_operands([256, 256, 256], 64, 64, "bf16", torch.float32, False, seed=4, device=DEV)
+    bad = torch.tensor([256, 128, 768], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="first bad expert 1"):
+        kgw.wgrad(wl.A, wl.B, bad)
+    out = kgw.wgrad(wl.A, wl.B, wl.offsets)
+    torch.cuda.synchronize()
+    assert_fp32_close(to_f64(out), oracle_dense(wl), "wgrad wrapper")
 
 
 def test_malformed_offsets_stay_in_bounds():
@@ -377,8 +407,88 @@ def test_fp8_native_random_small_within_its_bound():
 
 
 # ----------------------------------------------------------------------------
-# full-size workloads in the benchmark's launch configuration: sampled rows
+# the persistent schedule at mid size, every element: more items than CUs
 # ----------------------------------------------------------------------------
+# The host picks the schedule from the counts (kgw_host.hip): with at least 1024
+# tokens per expert on average ("long experts") the bf16 kernel remaps workgroups
+# so each XCD owns a contiguous run of items, walks each expert's tiles in columns
+# of four M tiles and takes odd rounds of the persistent stride in reverse; below
+# that ("short experts") it uses columns of eight M tiles and no remap.  Both
+# branches run here with more items than the 256 CUs hold, so every workgroup
+# takes several rounds, and every element is compared with the oracle.
+def _long_expert_counts(E, seed):
+    counts = workloads.counts_uniform(E, 2048, 256, seed)
+    assert sum(counts) >= 1024 * E, "long-expert branch"
+    return counts
+
+
+def _short_expert_counts(E, seed):
+    rng = np.random.default_rng(seed)
+    counts = (256 * rng.integers(0, 4, size=E)).tolist()      # 0 .. 768 tokens, about a quarter empty
+    assert sum(counts) < 1024 * E, "short-expert branch"
+    return counts
+
+
+def _items(counts, hidden, n):
+    return len(counts) * ((hidden + 255) // 256) * ((n + 255) // 256)
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("branch", ["long", "short"])
+def test_bf16_multi_round_schedule_integer_every_element(branch, accumulate):
+    if branch == "long":
+        counts, hidden, n = _long_expert_counts(6, 7), 2048, 2048          # 384 items: 2 rounds
+    else:
+        counts, hidden, n = _short_expert_counts(40, 8), 2048, 1024        # 1280 items: 5 rounds
+    assert _items(counts, hidden, n) > 256
+    wl = workloads.make_operands(counts, hidden, n, "bf16", torch.float32, accumulate, seed=71, device=DEV,
+                                 integer_range=4)
+    out = wl.C0.clone() if accumulate else nan_filled((len(counts), hidden, n), torch.float32)
+    run_bf16(wl, out=out, accumulate=accumulate)
+    W = oracle_dense(wl)
+    ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
+
+
+@pytest.mark.parametrize("branch", ["long", "short"])
+def test_bf16_multi_round_schedule_random_bf16_out(branch):
+    if branch == "long":
+        counts, hidden, n = _long_expert_counts(6, 17), 2048, 2048
+    else:
+        counts, hidden, n = _short_expert_counts(40, 18), 2048, 1024
+    wl = workloads.make_operands(counts, hidden, n, "bf16", torch.bfloat16, False, seed=72, device=DEV)
+    out = nan_filled((len(counts), hidden, n), torch.bfloat16)
+    run_bf16(wl, out=out)
+    W = oracle_dense(wl)
+    assert_bf16_close(to_f64(out), oracle.apply_output_mode(W, False), f"{branch} bf16")
+
+
+@pytest.mark.parametrize("native", [False, True])
+def test_fp8_multi_round_schedule_integer_every_element(native):
+    counts = workloads.counts_uniform(6, 2048, 128, 9)                    # 384 items: 2 rounds
+    hidden, n = 2048, 2048
+    wl = workloads.make_operands(counts, hidden, n, "fp8", torch.float32, False, seed=73, device=DEV,
+                                 integer_range=8)
+    g = torch.Generator(device=DEV).manual_seed(74)
+    wl.sfa = torch.randint(125, 130, wl.sfa.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    wl.sfb = torch.randint(125, 130, wl.sfb.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    out = nan_filled((len(counts), hidden, n), torch.float32)
+    run_fp8(wl, out=out, native=native)
+    W = oracle_dense(wl)
+    got = to_f64(out)
+    mism = np.argwhere(got != W)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {W[tuple(mism[0])]}"
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration
+# ----------------------------------------------------------------------------
+# Overwrite-mode outputs start as NaN, so a tile the schedule drops or misplaces
+# shows up in the whole-tensor NaN check; the values are then compared with the
+# oracle on every element (balanced) or on sampled rows that the oracle computes
+# one by one (the larger workloads).
 def check_sampled(wl, out, experts, rows_per_expert=6, seed=0):
     Ah, Bh, off = wl.A.cpu(), wl.B.cpu(), wl.offsets.cpu()
     if wl.kind == "fp8":
@@ -392,7 +502,7 @@ def check_sampled(wl, out, experts, rows_per_expert=6, seed=0):
         C0 = to_f64(wl.C0[e][rows]) if wl.accumulate else None
         ref = oracle.apply_output_mode(W, wl.accumulate, C0)
         got = to_f64(out[e][torch.from_numpy(rows).to(out.device)])
-        if wl.out_dtype == torch.float32:
+        if out.dtype == torch.float32:
             err = rel_frob(got, ref)
             assert err <= FP32_REL_FROB, f"{wl.name} expert {e}: rel Frobenius {err:.3e}"
         else:
@@ -408,10 +518,29 @@ def nonempty_experts(wl):
     return [e for e, c in enumerate(wl.counts) if c > 0]
 
 
-def test_full_balanced_bf16():
+def full_out(wl, dtype=None):
+    return nan_filled((wl.num_experts, wl.hidden, wl.n), dtype or wl.out_dtype)
+
+
+def assert_every_element_written(out):
+    assert not torch.isnan(out).any().item(), "NaN left in the output: some elements were never written"
+
+
+def assert_empty_experts_zero(wl, out):
+    emp = empty_experts(wl)
+    if not emp:
+        return
+    z = out.index_select(0, torch.tensor(emp, device=out.device))
+    assert torch.count_nonzero(z).item() == 0 and not torch.signbit(z).any().item()
+
+
+def test_full_balanced_bf16_every_element():
     wl = workloads.make_workload("balanced", seed=1, device=DEV)
-    out = run_bf16(wl)
-    check_sampled(wl, out, nonempty_experts(wl))
+    out = run_bf16(wl, out=full_out(wl))
+    assert_every_element_written(out)
+    W = oracle_dense(wl)
+    rms = np.sqrt(np.mean(W * W, axis=(1, 2)))
+    assert_bf16_close(to_f64(out), W, "balanced", rms=rms)
 
 
 def test_full_skewed_accumulate():
@@ -422,15 +551,27 @@ def test_full_skewed_accumulate():
     check_sampled(wl, out, nonempty_experts(wl), rows_per_expert=4)
 
 
+def test_full_skewed_overwrite_writes_every_element():
+    # the skewed workload's schedule in overwrite mode: every element written, empties +0.0
+    wl = workloads.make_workload("skewed", seed=1, device=DEV)
+    out = run_bf16(wl, out=full_out(wl), accumulate=False)
+    assert_every_element_written(out)
+    assert_empty_experts_zero(wl, out)
+    wl.accumulate = False
+    check_sampled(wl, out, nonempty_experts(wl)[::3], rows_per_expert=3, seed=5)
+
+
 def test_full_fp8():
     wl = workloads.make_workload("fp8", seed=1, device=DEV)
-    out = run_fp8(wl)
+    out = run_fp8(wl, out=full_out(wl))
+    assert_every_element_written(out)
     check_sampled(wl, out, nonempty_experts(wl)[::2], rows_per_expert=4)
 
 
 def test_full_fp8_native_within_its_bound():
     wl = workloads.make_workload("fp8", seed=1, device=DEV)
-    out = run_fp8(wl, out_dtype=torch.float32, native=True)
+    out = run_fp8(wl, out=full_out(wl, torch.float32), native=True)
+    assert_every_element_written(out)
     Ah, Bh, sah, sbh, off = wl.A.cpu(), wl.B.cpu(), wl.sfa.cpu(), wl.sfb.cpu(), wl.offsets.cpu()
     for e in nonempty_experts(wl)[::4]:
         rows = sample_rows(wl.hidden, 4, e)
@@ -442,12 +583,9 @@ def test_full_fp8_native_within_its_bound():
 
 def test_full_many_small():
     wl = workloads.make_workload("many_small", seed=1, device=DEV)
-    out = run_bf16(wl)
-    emp = empty_experts(wl)
-    idx = torch.tensor(emp, device=DEV)
-    z = out.index_select(0, idx)
-    assert torch.count_nonzero(z).item() == 0 and not torch.signbit(z).any().item()
-    del z
+    out = run_bf16(wl, out=full_out(wl))
+    assert_every_element_written(out)
+    assert_empty_experts_zero(wl, out)
     ne = nonempty_experts(wl)
     rng = np.random.default_rng(0)
     pick = sorted(set([ne[0], ne[-1]] + rng.choice(ne, 16, replace=False).tolist()))
