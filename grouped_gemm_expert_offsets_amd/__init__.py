@@ -25,7 +25,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
+    "kgw_wgrad_bf16", "kgw_wgrad_bf16_noalloc", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
     "kgw_wgrad_fp4", "FP4_TOKEN_ALIGN",
     "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT",
     "KGW_LAYOUT_NN",
@@ -64,7 +64,7 @@ library_path = os.path.join(_HERE, "libkgw.so")
 _lib = None
 
 # Every symbol include/kgw.h declares.
-EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
+EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_noalloc", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
                     "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16",
                     "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_check_offsets",
                     "kgw_status_string", "kgw_device_info")
@@ -82,6 +82,8 @@ def load_library():
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.kgw_wgrad_bf16.restype = ctypes.c_int
     lib.kgw_wgrad_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_bf16_noalloc.restype = ctypes.c_int
+    lib.kgw_wgrad_bf16_noalloc.argtypes = [p, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_wgrad_fp8.restype = ctypes.c_int
     lib.kgw_wgrad_fp8.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_native.restype = ctypes.c_int
@@ -230,6 +232,34 @@ def kgw_wgrad_bf16(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out:
     st = load_library().kgw_wgrad_bf16(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
                                        int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, "kgw_wgrad_bf16")
+    return out
+
+
+def kgw_wgrad_bf16_noalloc(A: torch.Tensor, B: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor, *,
+                           accumulate: bool = False, stream=None) -> torch.Tensor:
+    """kgw_wgrad_bf16 that allocates nothing, here or in the library: `out` must be given
+    (its dtype selects the output type), and split-K partials use the library's fixed
+    per-device scratch.  Calls that overlap in time on one device race on that scratch."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("kgw_wgrad_bf16_noalloc takes bfloat16 A and B")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (A token-contiguous, B row-major)")
+    if out is None:
+        raise ValueError("kgw_wgrad_bf16_noalloc needs `out` (it allocates nothing)")
+    device = A.device
+    if B.device != device:
+        raise ValueError("A and B must be on the same device")
+    _check_offsets(offsets, device)
+    hidden, T = A.shape
+    n = B.shape[1]
+    E = offsets.numel()
+    code = _out_code(out.dtype)
+    out = _prepare_out(out, E, hidden, n, out.dtype, accumulate, device)
+    st = load_library().kgw_wgrad_bf16_noalloc(_ptr(A), _ptr(B), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
+                                               int(bool(accumulate)), _stream_ptr(stream))
+    _check(st, "kgw_wgrad_bf16_noalloc")
     return out
 
 

@@ -11,6 +11,15 @@
 #include "kgw_device.h"
 #include "kgw_internal.h"
 
+// Scratch of kgw_wgrad_bf16_noalloc, for callers that cannot allocate: the split-K
+// partials live in this file-scope device array instead of a caller workspace.  Every
+// device the library runs on holds its own copy until the process ends; its address on a
+// device comes from hipGetSymbolAddress with that device current (in host code the
+// array's name is not a device address).  Nothing in it needs to start at zero: every
+// partial slab a call reads back was written earlier in the same call.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
 
 struct DeviceProps {
@@ -43,6 +52,20 @@ kgw_status_t current_props(DeviceProps* out) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's copy of `scratch` (NULL if its address could not be obtained).
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
 
 // Checks shared by both entry points; everything here is pure host logic.
 kgw_status_t check_common(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
@@ -228,6 +251,25 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
                             int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
     return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
                out, nullptr, out_dtype, accumulate, workspace, workspace_bytes, stream);
+}
+
+kgw_status_t kgw_wgrad_bf16_noalloc(const void* A, const void* B, const int32_t* offsets, int32_t num_experts,
+                                    int64_t hidden, int64_t n, int64_t tokens_sum, void* out, int32_t out_dtype,
+                                    int32_t accumulate, void* stream) {
+    // Same checks and kernels as kgw_wgrad_bf16; the split-K partials (when the plan splits and
+    // they fit) go to this device's scratch, so nothing is allocated.  Checked before the
+    // device is touched, like every other argument error.
+    DeviceProps d;
+    const kgw_status_t st = current_props(&d);
+    if (st == KGW_SUCCESS && d.is_gfx950) {
+        void* ws = device_scratch();
+        if (!ws) return KGW_ERROR_DEVICE;
+        return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum,
+                   out, nullptr, out_dtype, accumulate, ws, kScratchBytes, stream);
+    }
+    // no usable device: let run() report the argument errors first, then the device error
+    return run(Kernel::kBf16, A, nullptr, B, nullptr, KGW_SCALES_U8, offsets, num_experts, hidden, n, tokens_sum, out,
+               nullptr, out_dtype, accumulate, nullptr, 0, stream);
 }
 
 kgw_status_t kgw_wgrad_bf16_ex(const void* A, const void* B, int32_t layout, const int32_t* offsets,

@@ -135,6 +135,26 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
                             void* out, int32_t out_dtype, int32_t accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kgw_wgrad_bf16_noalloc -- kgw_wgrad_bf16 for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, contract, errors and kernels as kgw_wgrad_bf16, minus
+ * the workspace: where kgw_wgrad_bf16 would split K and the fp32 partials take at most
+ * 64 MiB, they go to a fixed 64 MiB scratch array the library holds on every device it
+ * runs on (until the process ends), so the result is bit for bit that of
+ * kgw_wgrad_bf16 given a workspace of kgw_workspace_bytes(...) bytes.  A shape whose
+ * partials would need more than those 64 MiB runs in one pass instead (no error: one
+ * pass needs no scratch; the result then differs only by the order of the fp32
+ * additions).  The call allocates and frees nothing.
+ * All calls on one device share that device's scratch, which keeps the last call's
+ * contents (no call needs it to start at zero): two calls that overlap in time on the
+ * same device -- on different streams, or from different threads -- race on it and may
+ * give wrong results.  Order such calls on one stream or synchronise between them.
+ */
+kgw_status_t kgw_wgrad_bf16_noalloc(const void* A, const void* B, const int32_t* offsets,
+                                    int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
+                                    void* out, int32_t out_dtype, int32_t accumulate, void* stream);
+
 /* Operand layouts of kgw_wgrad_bf16_ex (cuDNN page, "BF16 contract" table and
  * its input_order), combined as bit flags; 0 is kgw_wgrad_bf16's layout
  * (A K-major: (hidden, tokens_sum) row-major; B N-major: (tokens_sum, n)

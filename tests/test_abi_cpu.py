@@ -287,3 +287,14 @@ def test_wgrad_wrapper_checks_offsets_by_default():
     for fn in (kgw.kgw_wgrad_bf16, kgw.kgw_wgrad_fp8, kgw.kgw_wgrad_fp8_native, kgw.kgw_wgrad_bf16_ex,
                kgw.kgw_wgrad_fp8_ex, kgw.kgw_wgrad_fp4):
         assert inspect.signature(fn).parameters["validate"].default is False, fn.__name__
+
+
+def test_noalloc_entry_point_argument_errors(lib):
+    # the no-alloc variant shares kgw_wgrad_bf16's host checks (no device touched)
+    f = lib.kgw_wgrad_bf16_noalloc
+    assert f(FAKE, FAKE, FAKE, 0, 256, 512, 1024, FAKE, 0, 0, None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, 4, 256, 512, 1024, None, 0, 0, None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, 4, 256, 512, 1000, FAKE, 0, 0, None) == kgw.KGW_ERROR_BAD_OFFSETS
+    assert f(FAKE, FAKE, FAKE, 4, 256, 516, 1024, FAKE, 0, 0, None) == kgw.KGW_ERROR_MISALIGNED
+    assert f(FAKE, FAKE, FAKE, 4, 256, 512, 1024, FAKE, 3, 0, None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert f(None, None, FAKE, 4, 0, 512, 1024, None, 0, 0, None) == kgw.KGW_SUCCESS      # no output elements
