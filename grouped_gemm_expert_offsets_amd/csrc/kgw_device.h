@@ -87,6 +87,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
+// s_waitcnt lgkmcnt(N) alone: at most N of this wave's LDS / scalar reads are still
+// outstanding.  LDS reads return in issue order, so every LDS read issued before the
+// last N has returned.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
 // Workgroup barrier without the memory fence __syncthreads() adds: the fence
 // would wait for every outstanding direct-to-LDS load, collapsing the pipeline.
 // Callers order their own memory with wait_vmcnt / lgkmcnt waits.  The empty
@@ -142,6 +151,14 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
     const uint32_t bits = s == 0u ? 0x00400000u : (s == 255u ? 0x7FC00000u : (s << 23));
     return __builtin_bit_cast(float, bits);
 }
+
+// UE8M0 scale byte -> the scale operand of the v_cvt_scalef32_* conversions.  Those
+// instructions take only the exponent field of their fp32 scale operand as the scale (a
+// GPU probe over all 256 field values and a few mantissas: the mantissa bits change
+// nothing, field 0 scales by 2^-127 and field 255 gives NaN, exactly as e8m0_to_f32's
+// value does), so the byte moved into that field is the operand: one shift instead of
+// the two special cases.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t s) { return __builtin_bit_cast(float, s << 23); }
 
 // Two e4m3 bytes (bytes 2*HI and 2*HI+1 of `packed`) -> two bf16 (low half = lower
 // byte) multiplied by `scale`.  For a power-of-two scale the result is exact:

@@ -24,7 +24,11 @@
 // the block's scale bytes by byte-wide direct loads (the MX scale words by
 // dword-wide ones) into a 3-slot scale ring,
 // ten direct loads per wave per 64-token step spread over its MFMAs, one
-// barrier per step.  Inside a step the wave runs four 16-token groups of 16
+// barrier per step.  The K loop is unrolled by six steps (the period of the
+// three-slot rings), so every ring slot is a constant and a fragment read is
+// one LDS instruction on a per-lane offset: one wave issues every instruction of
+// its SIMD, and each one between two MFMAs costs MFMA time once there are more
+// than about five.  Inside a step the wave runs four 16-token groups of 16
 // bf16 MFMAs (32x32x16; 4 waves, each 128x128 of the 256x256 tile):
 //   - raw fp8 fragments of step s+1 (8-byte A reads, transposing
 //     ds_read_b64_tr_b8 B reads) are read from LDS group by group during the
@@ -34,6 +38,8 @@
 //     runs, so the conversions hide behind the MFMAs;
 //   - the finished tile leaves through the idle rings (LDS transpose, whole
 //     row segments per store).
+#include <type_traits>
+
 #include "kgw_device.h"
 #include "kgw_internal.h"
 #include "kgw_tile_io.h"
@@ -86,17 +92,28 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 
     // Fragment reads of 16-token group g (tokens 16g + 8*lhi + 0..7 of the
     // step).  A: row wm*128 + 32i + l32, 8 bytes at token offset 64*(s&1) +
-    // 16g + 8*lhi of the stage row: 16-byte chunk 4*(s&1) + g, half lhi.  B:
+    // 16g + 8*lhi of the stage row: 16-byte chunk 4*(s&1) + g, half lhi; the
+    // lane's offset for (s&1, g) is a_rd[s&1][g] and block i adds 4096.  B:
     // column 32j + l32 of the wave's half, one transposed 8x16 block at k-rows
-    // 16g + 8*lhi + 0..7; block j's offset is block 0's with the chunk XOR 2j.
+    // 16g + 8*lhi + 0..7: offset b_rd[j], group g adds 4096.  All per lane and
+    // fixed for the kernel, so each step adds only its ring slot's base.
     const int l32 = lane & 31, lhi = lane >> 5;
     const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u + (uint32_t)lhi * 8u;
     const int a_sw = (l32 >> 1) & 7;
+    uint32_t a_rd[2][4];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) a_rd[par][g] = a_frag_row + (uint32_t)(((4 * par + g) ^ a_sw) << 4);
     const int g16 = lane >> 4, i16 = lane & 15;
     const uint32_t b_frag0 = (uint32_t)(8 * (g16 >> 1) + (i16 >> 1)) * 256u +
                              (uint32_t)((8 * wn + (g16 & 1)) ^ (2 * (i16 >> 1))) * 16u + (uint32_t)(i16 & 1) * 8u;
+    uint32_t b_rd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b_rd[j] = b_frag0 ^ (uint32_t)(32 * j);
     // Scale dwords of this wave: sa row r at 4r, sb column c at 512 + 4c.
     const uint32_t sc_wave = (uint32_t)(SC_RING + wave * SC_WAVE);
+    const uint32_t sc_rd = sc_wave + 4u * (uint32_t)l32;
 
     const int TT = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;
@@ -145,6 +162,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         // memory outside the operands.
         const int64_t a_rows_bytes = min<int64_t>(BM, H - m0) * T - begin;
         const int64_t b_bytes = (T - begin) * N - n0;
+        const int64_t b_step_bytes = (int64_t)KS * N;
         const uint32_t a_voff0 = (uint32_t)(64 * wave + (lane >> 3)) * (uint32_t)T;
         const uint32_t b_voff0 = (uint32_t)(16 * wave + (lane >> 4)) * (uint32_t)N;
         // Scales: sa for rows m0 + wm*128 + 64h + lane, sb for columns
@@ -154,48 +172,40 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         constexpr uint32_t sstride = FMT == kScalesU8 ? 1u : 4u;
         const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane) * sstride;
         const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane) * sstride;
+        // Per-lane global offsets of the direct loads (the row offset of
+        // instruction t is uniform and added per load).
+        const uint32_t a_voff_even = a_voff0 + (uint32_t)a_q0 * 16u;
+        const uint32_t a_voff_odd = a_voff0 + (uint32_t)a_q1 * 16u;
+        const uint32_t b_voff_even = b_voff0 + (uint32_t)b_q0 * 16u;
+        const uint32_t b_voff_odd = b_voff0 + (uint32_t)b_q1 * 16u;
+        const uint32_t a_m0 = tiles_addr + (uint32_t)(8 * wave) * 1024u;
+        const uint32_t b_m0 = tiles_addr + (uint32_t)B_RING + (uint32_t)(4 * wave) * 1024u;
+        const uint32_t s_m0 = tiles_addr + sc_wave;
 
-        // Direct loads, as in the native fp8 kernel: A stage a (steps 2a, 2a+1;
-        // scale block a) to A slot a % NA, B step s to B slot s % NB; stages past
-        // the expert's range use an empty buffer range (the loads fetch nothing).
-        auto dma_a = [&](int a, int t) {
-            const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
-            const i32x4 r = rsrc_words(Abase + (int64_t)a * (2 * KS),
-                                       a < nblocks ? (uint32_t)(a_rows_bytes - (int64_t)a * (2 * KS)) : 0u);
-            const uint32_t voff = a_voff0 + (uint32_t)(8 * t) * (uint32_t)T + (uint32_t)((t & 1) ? a_q1 : a_q0) * 16u;
-            dma_16B(r, voff, dst);
+        // Buffer resources of the loads: A stage a (steps 2a, 2a+1; scale block a),
+        // B step sb, the scales of block a; a stage past the expert's range gets
+        // an empty range (its loads fetch nothing).  All of it is wave-uniform.
+        auto rsrc_a = [&](int a) {
+            return rsrc_words(Abase + (int64_t)a * (2 * KS),
+                              a < nblocks ? (uint32_t)(a_rows_bytes - (int64_t)a * (2 * KS)) : 0u);
         };
-        auto dma_b = [&](int sb, int t) {
-            const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) + (uint32_t)(4 * wave + t) * 1024u;
-            const i32x4 r = rsrc_words(Bbase + (int64_t)sb * KS * N,
-                                       sb < ksteps ? (uint32_t)min<int64_t>(b_bytes - (int64_t)sb * KS * N, 0xFFFFFFFFll) : 0u);
-            const uint32_t voff = b_voff0 + (uint32_t)(4 * t) * (uint32_t)N + (uint32_t)((t & 1) ? b_q1 : b_q0) * 16u;
-            dma_16B(r, voff, dst);
-        };
-        auto dma_s = [&](int a, bool b_side, int h) {
-            const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((a % NA) * SC_STAGE) +
-                                 (b_side ? 512u : 0u) + (uint32_t)h * 256u;
+        auto rsrc_s = [&](int a, bool b_side) {
             const ScaleSource src = scale_source<FMT>(b_side ? p.sfb : p.sfa, b_side ? N : H, gb0 + a);
-            const i32x4 r = rsrc_words(src.base, a < nblocks ? src.limit : 0u);
-            const uint32_t voff = (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u * sstride;
-            if constexpr (MX) dma_4B(r, voff, dst);
-            else dma_1B(r, voff, dst);
+            return rsrc_words(src.base, a < nblocks ? src.limit : 0u);
         };
-        // The loads of step s (also for the prologue's virtual steps s < 0), in
-        // issue order: B step s+3, then half of an A stage and two scale loads
-        // of its block -- for odd s the first half of A stage (s+5)/2 and its sa
-        // bytes, for even s the second half of A stage (s+4)/2 and its sb bytes.
-        // Every slot written this way was last read during step s-1 or earlier.
-        auto dma_step = [&](int s, int d) {
-            if (d < B_LOADS) {
-                if (s + NB >= 0) dma_b(s + NB, d);
-            } else if (d < 2 * B_LOADS) {
-                if (s & 1) dma_a((s + 5) / 2, d - B_LOADS);
-                else dma_a((s + 4) / 2, d);
-            } else {
-                if (s & 1) dma_s((s + 5) / 2, false, d - 2 * B_LOADS);
-                else dma_s((s + 4) / 2, true, d - 2 * B_LOADS);
-            }
+        // B: a running base and remaining byte count, advanced one step at a time.
+        const uint8_t* b_next = Bbase;
+        int64_t b_left = b_bytes;
+        int b_step = 0;
+        auto rsrc_b_next = [&]() {
+            // b_left stays positive while b_step < ksteps; a range beyond 4 GiB is cut to 4 GiB
+            const uint32_t lim = b_step < ksteps ? ((uint32_t)((uint64_t)b_left >> 32) ? 0xFFFFFFFFu : (uint32_t)b_left)
+                                                 : 0u;
+            const i32x4 r = rsrc_words(b_next, lim);
+            b_next += b_step_bytes;
+            b_left -= b_step_bytes;
+            ++b_step;
+            return r;
         };
 
         f32x16 acc[4][4];
@@ -207,7 +217,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
         // Raw fp8 fragments of one K step ([block][group], 8 bytes each) plus
-        // the block's scales; and one group's converted bf16 operands.
+        // the block's scale dwords and their conversion operands; and one group's
+        // converted bf16 operands.
         struct Raw {
             i32x2 a[4][4];
             i32x2 b[4][4];
@@ -218,38 +229,35 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
             i32x4 a[4];
             i32x4 b[4];
         };
-        // Read (g, m) of step s, made after MFMA m of group g: for m < 8 raw
-        // fragment m of group g (A block m, then B block m-4); in group 0, for
-        // m >= 8 the block's scale dword m-8 (sa blocks 0-3, then sb 0-3).
-        auto read_one = [&](int s, int g, int m, Raw& f) {
+        // Read (g, m) of step r (r = the step's index modulo 6, which fixes its
+        // ring slots: A stage (r >> 1) % NA, B step r % NB), made after MFMA m of
+        // group g: for m < 8 raw fragment m of group g (A block m, then B block
+        // m-4); in group 0, for m >= 8 the block's scale dword m-8 (sa blocks 0-3,
+        // then sb 0-3).  Every address is a per-lane offset plus a constant.
+        auto read_one = [&](auto rc, int g, int m, Raw& f) {
+            constexpr int r = decltype(rc)::value;
+            constexpr uint32_t a_slot = (uint32_t)(((r >> 1) % NA) * A_STAGE);
+            constexpr uint32_t b_slot = (uint32_t)(B_RING + (r % NB) * B_STAGE);
+            constexpr uint32_t s_slot = (uint32_t)(((r >> 1) % NA) * SC_STAGE);
             if (m >= 8) {
                 if (g != 0) return;
-                const lds_char* Sc = tiles + sc_wave + ((s >> 1) % NA) * SC_STAGE;
                 const int x = m - 8;
-                if (x < 4) f.sa[x] = lds_load_4B(Sc, (uint32_t)(4 * (32 * x + l32)));
-                else f.sb[x - 4] = lds_load_4B(Sc, (uint32_t)(512 + 4 * (32 * (x - 4) + l32)));
+                if (x < 4) f.sa[x] = lds_load_4B(tiles + s_slot, sc_rd + (uint32_t)(128 * x));
+                else f.sb[x - 4] = lds_load_4B(tiles + s_slot, sc_rd + (uint32_t)(512 + 128 * (x - 4)));
             } else if (m < 4) {
-                const lds_char* As = tiles + ((s >> 1) % NA) * A_STAGE;
-                const uint32_t chunk = (uint32_t)(((4 * (s & 1) + g) ^ a_sw) << 4);
-                f.a[m][g] = lds_load_8B(As, a_frag_row + m * 4096u + chunk);
+                f.a[m][g] = lds_load_8B(tiles + a_slot + m * 4096, a_rd[r & 1][g]);
             } else {
-                const lds_char* Bs = tiles + B_RING + (s % NB) * B_STAGE;
-                f.b[m - 4][g] = lds_read_tr8(Bs, (b_frag0 ^ (uint32_t)(32 * (m - 4))) + (uint32_t)g * 4096u);
+                f.b[m - 4][g] = lds_read_tr8(tiles + b_slot + g * 4096, b_rd[m - 4]);
             }
         };
-        // Scales of the 32-token block `sub` (0..3) of the stage (MX), or of the
-        // stage's single block, as fp32 conversion factors.
-        auto scales_to_float = [&](Raw& f, int sub) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                if constexpr (MX) {
-                    f.fa[x] = e8m0_to_f32(((uint32_t)f.sa[x] >> (8 * sub)) & 0xFFu);
-                    f.fb[x] = e8m0_to_f32(((uint32_t)f.sb[x] >> (8 * sub)) & 0xFFu);
-                } else {
-                    f.fa[x] = e8m0_to_f32((uint32_t)f.sa[x]);
-                    f.fb[x] = e8m0_to_f32((uint32_t)f.sb[x]);
-                }
-            }
+        // Conversion operand of scale x (A blocks 0-3, then B blocks 4-7) for the
+        // 32-token block `sub` (0..3) of the stage (MX), or for the stage's single
+        // block.
+        auto decode_one = [&](Raw& f, int x, int sub) {
+            const uint32_t w = (uint32_t)(x < 4 ? f.sa[x] : f.sb[x - 4]);
+            const float v = e8m0_scale_operand(MX ? (w >> (8 * sub)) & 0xFFu : w);
+            if (x < 4) f.fa[x] = v;
+            else f.fb[x - 4] = v;
         };
         // Conversion number c (0..7) of group g: A block c, then B block c-4.
         auto convert_one = [&](const Raw& f, int g, int c, Conv& cv) {
@@ -261,16 +269,53 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
             const int j = m >> 2, i = m & 3;
             acc[j][i] = mfma_bf16_32x32x16(cv.b[j], cv.a[i], acc[j][i]);
         };
+        // The loads of step s (also the prologue's virtual steps s < 0), in issue
+        // order d = 0..9: B step s+3 (its four instructions), then half of an A
+        // stage and two scale loads of its block -- for odd s the first half of
+        // A stage (s+5)/2 and its sa bytes, for even s the second half of A stage
+        // (s+4)/2 and its sb bytes.  Every slot written this way was last read
+        // during step s-1 or earlier.  `rb` is B step s+3's resource, `ra` / `rs`
+        // those of the A stage and its scales.
+        auto dma_step = [&](auto rc, int d, const i32x4& rb, const i32x4& ra, const i32x4& rs) {
+            constexpr int r = decltype(rc)::value;             // the step modulo 6 (>= 0)
+            constexpr int a_slot = ((r & 1) ? (r + 5) / 2 : (r + 4) / 2) % NA;
+            if (d < B_LOADS) {
+                const uint32_t dst = b_m0 + (uint32_t)(((r + NB) % NB) * B_STAGE) + (uint32_t)d * 1024u;
+                dma_16B(rb, ((d & 1) ? b_voff_odd : b_voff_even) + (uint32_t)(4 * d) * (uint32_t)N, dst);
+            } else if (d < 2 * B_LOADS) {
+                const int t = (r & 1) ? d - B_LOADS : d;
+                const uint32_t dst = a_m0 + (uint32_t)(a_slot * A_STAGE) + (uint32_t)t * 1024u;
+                dma_16B(ra, ((t & 1) ? a_voff_odd : a_voff_even) + (uint32_t)(8 * t) * (uint32_t)T, dst);
+            } else {
+                const int h = d - 2 * B_LOADS;
+                constexpr bool b_side = !(r & 1);
+                const uint32_t dst = s_m0 + (uint32_t)(a_slot * SC_STAGE) + (b_side ? 512u : 0u) + (uint32_t)h * 256u;
+                const uint32_t voff = (b_side ? sb_voff : sa_voff) + (uint32_t)h * 64u * sstride;
+                if constexpr (MX) dma_4B(rs, voff, dst);
+                else dma_1B(rs, voff, dst);
+            }
+        };
+        // The prologue's virtual step v (-5..-1): its residue modulo 6 is v + 6.
+        auto dma_all = [&](auto rc, int v) {
+            const int a = (v & 1) ? (v + 5) / 2 : (v + 4) / 2;
+            const i32x4 rb = v + NB >= 0 ? rsrc_b_next() : i32x4{0, 0, 0, 0};
+            const i32x4 ra = rsrc_a(a);
+            const i32x4 rs = rsrc_s(a, !(v & 1));
+#pragma unroll
+            for (int d = 0; d < LOADS_PER_STEP; ++d)
+                if (d >= B_LOADS || v + NB >= 0) dma_step(rc, d, rb, ra, rs);
+        };
 
         // The partial vmcnt waits count only this item's direct loads, so the
         // previous item's output stores must have drained first.
         wait_vmcnt<0>();
         // Prologue: the loads of virtual steps -5..-1.  Step 0's fragments need
         // A stage 0 with its scales and B step 0; 26 loads were issued after B 0.
-#pragma unroll
-        for (int v = -5; v < 0; ++v)
-#pragma unroll
-            for (int d = 0; d < LOADS_PER_STEP; ++d) dma_step(v, d);
+        dma_all(std::integral_constant<int, 1>(), -5);
+        dma_all(std::integral_constant<int, 2>(), -4);
+        dma_all(std::integral_constant<int, 3>(), -3);
+        dma_all(std::integral_constant<int, 4>(), -2);
+        dma_all(std::integral_constant<int, 5>(), -1);
         wait_vmcnt<26>();
         barrier_no_fence();
         Raw r0, r1;
@@ -278,9 +323,10 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int m = 0; m < 16; ++m) read_one(0, g, m, r0);
+            for (int m = 0; m < 16; ++m) read_one(std::integral_constant<int, 0>(), g, m, r0);
         wait_lgkmcnt0();
-        scales_to_float(r0, 0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) decode_one(r0, x, 0);
 #pragma unroll
         for (int c = 0; c < 8; ++c) convert_one(r0, 0, c, c0);
 
@@ -290,29 +336,32 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
         // (s+1)/2 and its scales completed in step s-3: at most 16 later loads
         // may remain) and certifies that every wave is done reading step s.
         // Then 64 MFMAs in four groups; after MFMA k = 16g + m: direct load k/6
-        // when k%6 == 2, read (g, m) of step s+1 (group g's raw fragments, and
-        // the scales in group 0), and every other MFMA one conversion for the
-        // next group (group 0 of step s+1 during group 3, once its reads and
-        // scales are in).  With 32-token scales (MX) groups 2g and 2g+1 share
-        // block 2*(s&1) + g of the stage: the factors of `cur` are switched to the
-        // second block before group 1 (whose conversions are group 2's).
-        // sched_barrier(0) pins the interleaving.
-        auto body = [&](int s, Raw& cur, Raw& nxt) {
+        // when k%6 == 2 (their buffer resources made a few MFMAs earlier), read (g, m)
+        // of step s+1 (group g's raw fragments, and the scales in group 0), and
+        // every other MFMA one conversion for the next group (group 0 of step s+1
+        // during group 3, each conversion after the MFMA that decodes its scale,
+        // once the scale reads of group 0 are in).  With 32-token scales (MX)
+        // groups 2g and 2g+1 share block 2*(s&1) + g of the stage: during group 1
+        // (whose conversions are group 2's) the scale operands of `cur` are
+        // switched to the second block the same way.  sched_barrier(0) pins the
+        // interleaving.
+        // `rc` carries s modulo 6 (the period of the three-slot rings), so every
+        // ring slot below is a constant.
+        auto body = [&](auto rc, int s, Raw& cur, Raw& nxt) {
+            constexpr int R = decltype(rc)::value;
+            const auto next = std::integral_constant<int, (R + 1) % 6>();
+            const int a = (R & 1) ? (s + 5) / 2 : (s + 4) / 2;
             wait_lgkmcnt0();
             wait_vmcnt<16>();
             barrier_no_fence();
             __builtin_amdgcn_sched_barrier(0);
+            i32x4 rb, ra, rs;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 Conv& cv = (g & 1) ? c1 : c0;
                 Conv& cn = (g & 1) ? c0 : c1;
-                if (MX && g == 1) {
-                    scales_to_float(cur, 2 * (s & 1) + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
                 if (g == 3) {
-                    wait_lgkmcnt0();
-                    scales_to_float(nxt, MX ? 2 * ((s + 1) & 1) : 0);
+                    wait_lgkmcnt<15>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
@@ -320,19 +369,39 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
                     const int k = 16 * g + m;
                     mfma_one(cv, m);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (k % 6 == 2 && k / 6 < LOADS_PER_STEP) dma_step(s, k / 6);
-                    read_one(s + 1, g, m, nxt);
+                    if (k == 0) rb = rsrc_b_next();
+                    if (k == 20) ra = rsrc_a(a);
+                    if (k == 44) rs = rsrc_s(a, !(R & 1));
+                    if (k % 6 == 2 && k / 6 < LOADS_PER_STEP) dma_step(rc, k / 6, rb, ra, rs);
+                    read_one(next, g, m, nxt);
                     if (m & 1) {
                         if (g < 3) convert_one(cur, g + 1, m >> 1, cn);
                         else convert_one(nxt, 0, m >> 1, cn);
+                    } else {
+                        if (MX && g == 1) decode_one(cur, m >> 1, 2 * (R & 1) + 1);
+                        if (g == 3) decode_one(nxt, m >> 1, MX ? 2 * ((R + 1) & 1) : 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
-        for (int s = 0; s < ksteps; s += 2) {
-            body(s, r0, r1);
-            body(s + 1, r1, r0);
+        // Six steps per iteration, then the remaining two or four (ksteps is even).
+        int s = 0;
+        for (; s + 6 <= ksteps; s += 6) {
+            body(std::integral_constant<int, 0>(), s, r0, r1);
+            body(std::integral_constant<int, 1>(), s + 1, r1, r0);
+            body(std::integral_constant<int, 2>(), s + 2, r0, r1);
+            body(std::integral_constant<int, 3>(), s + 3, r1, r0);
+            body(std::integral_constant<int, 4>(), s + 4, r0, r1);
+            body(std::integral_constant<int, 5>(), s + 5, r1, r0);
+        }
+        if (s < ksteps) {
+            body(std::integral_constant<int, 0>(), s, r0, r1);
+            body(std::integral_constant<int, 1>(), s + 1, r1, r0);
+            if (s + 2 < ksteps) {
+                body(std::integral_constant<int, 2>(), s + 2, r0, r1);
+                body(std::integral_constant<int, 3>(), s + 3, r1, r0);
+            }
         }
         // The rings become the output staging area: every wave must be done
         // reading them and every direct load (the empty ones past the range
