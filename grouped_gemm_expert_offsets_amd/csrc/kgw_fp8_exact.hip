@@ -30,9 +30,10 @@
 // its SIMD, and each one between two MFMAs costs MFMA time once there are more
 // than about five.  Inside a step the wave runs four 16-token groups of 16
 // bf16 MFMAs (32x32x16; 4 waves, each 128x128 of the 256x256 tile):
-//   - raw fp8 fragments of step s+1 (8-byte A reads, transposing
-//     ds_read_b64_tr_b8 B reads) are read from LDS group by group during the
-//     same group of step s, the block's scale dwords during group 0;
+//   - raw fp8 fragments of step s+1 (16-byte A reads, each serving two
+//     groups, and transposing ds_read_b64_tr_b8 B reads) are read from LDS
+//     during the matching group of step s, the scale dwords of a new block
+//     during group 0;
 //   - the eight fragments of group g+1 are converted while group g's MFMAs run
 //     (two converted sets alternate), and group 0 of step s+1 while group 3
 //     runs, so the conversions hide behind the MFMAs;
@@ -90,23 +91,27 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
     const int b_q0 = (lane & 15) ^ (2 * ((lane >> 4) & 7));
     const int b_q1 = (lane & 15) ^ (2 * ((4 + (lane >> 4)) & 7));
 
-    // Fragment reads of 16-token group g (tokens 16g + 8*lhi + 0..7 of the
-    // step).  A: row wm*128 + 32i + l32, 8 bytes at token offset 64*(s&1) +
-    // 16g + 8*lhi of the stage row: 16-byte chunk 4*(s&1) + g, half lhi; the
-    // lane's offset for (s&1, g) is a_rd[s&1][g] and block i adds 4096.  B:
-    // column 32j + l32 of the wave's half, one transposed 8x16 block at k-rows
-    // 16g + 8*lhi + 0..7: offset b_rd[j], group g adds 4096.  All per lane and
-    // fixed for the kernel, so each step adds only its ring slot's base.
+    // Fragment reads.  An MFMA's 16 K slots may hold any 16 tokens as long as
+    // both operands agree; the step's 64 tokens are four 16-token chunks, and
+    // 16-token group g takes, in lane half lhi, tokens 8*(g&1) + 0..7 of chunk
+    // 2*(g>>1) + lhi.  So one 16-byte A read (a whole chunk of one row) serves
+    // groups 2p and 2p+1, and groups 0-1 / 2-3 stay the step's first / second
+    // 32 tokens (one 32-token scale block each).  A: row wm*128 + 32i + l32,
+    // chunk 4*(s&1) + 2p + lhi of the 128-token stage row: offset a_rd[s&1][p],
+    // block i adds 4096.  B: column 32j + l32 of the wave's half, one transposed
+    // 8x16 block at k-rows 32*(g>>1) + 16*lhi + 8*(g&1) + 0..7: offset b_rd[j],
+    // group g adds 8192*(g>>1) + 2048*(g&1).  All per lane and fixed for the
+    // kernel; each step adds only its ring slot's constant base.
     const int l32 = lane & 31, lhi = lane >> 5;
-    const uint32_t a_frag_row = (uint32_t)(wm * 128 + l32) * 128u + (uint32_t)lhi * 8u;
+    const uint32_t a_row = (uint32_t)(wm * 128 + l32) * 128u;
     const int a_sw = (l32 >> 1) & 7;
-    uint32_t a_rd[2][4];
+    uint32_t a_rd[2][2];
 #pragma unroll
     for (int par = 0; par < 2; ++par)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) a_rd[par][g] = a_frag_row + (uint32_t)(((4 * par + g) ^ a_sw) << 4);
+        for (int pr = 0; pr < 2; ++pr) a_rd[par][pr] = a_row + (uint32_t)(((4 * par + 2 * pr + lhi) ^ a_sw) << 4);
     const int g16 = lane >> 4, i16 = lane & 15;
-    const uint32_t b_frag0 = (uint32_t)(8 * (g16 >> 1) + (i16 >> 1)) * 256u +
+    const uint32_t b_frag0 = (uint32_t)(16 * (g16 >> 1) + (i16 >> 1)) * 256u +
                              (uint32_t)((8 * wn + (g16 & 1)) ^ (2 * (i16 >> 1))) * 16u + (uint32_t)(i16 & 1) * 8u;
     uint32_t b_rd[4];
 #pragma unroll
@@ -216,53 +221,65 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-        // Raw fp8 fragments of one K step ([block][group], 8 bytes each) plus
-        // the block's scale dwords and their conversion operands; and one group's
-        // converted bf16 operands.
+        // Raw fp8 fragments of one K step (A: [block][group pair], 16 bytes; B:
+        // [block][group], 8 bytes) plus the step's scale dwords; one group's
+        // converted bf16 operands; and the scale operands the conversions use
+        // now (A blocks 0-3, B blocks 0-3): those of the block being converted,
+        // switched to the next block in the group that starts converting it.
         struct Raw {
-            i32x2 a[4][4];
+            i32x4 a[4][2];
             i32x2 b[4][4];
             int sa[4], sb[4];
-            float fa[4], fb[4];
         };
         struct Conv {
             i32x4 a[4];
             i32x4 b[4];
         };
+        float fa[4], fb[4];
+        // With one scale per 128 tokens, steps 2b and 2b+1 share block b: only the
+        // odd steps read and switch scales for the step after them.
+        auto reads_scales = [](int r_next) { return MX || (r_next & 1) == 0; };
         // Read (g, m) of step r (r = the step's index modulo 6, which fixes its
         // ring slots: A stage (r >> 1) % NA, B step r % NB), made after MFMA m of
-        // group g: for m < 8 raw fragment m of group g (A block m, then B block
-        // m-4); in group 0, for m >= 8 the block's scale dword m-8 (sa blocks 0-3,
-        // then sb 0-3).  Every address is a per-lane offset plus a constant.
+        // group g: for m < 4 in groups 0 and 2 A block m of the group pair, for
+        // 4 <= m < 8 B block m-4 of the group; in group 0, for m >= 8 the step's
+        // scale dword m-8 (sa blocks 0-3, then sb 0-3) when its block is new.
+        // Every address is a per-lane offset plus a constant.
         auto read_one = [&](auto rc, int g, int m, Raw& f) {
             constexpr int r = decltype(rc)::value;
             constexpr uint32_t a_slot = (uint32_t)(((r >> 1) % NA) * A_STAGE);
             constexpr uint32_t b_slot = (uint32_t)(B_RING + (r % NB) * B_STAGE);
             constexpr uint32_t s_slot = (uint32_t)(((r >> 1) % NA) * SC_STAGE);
             if (m >= 8) {
-                if (g != 0) return;
+                if (g != 0 || !reads_scales(r)) return;
                 const int x = m - 8;
                 if (x < 4) f.sa[x] = lds_load_4B(tiles + s_slot, sc_rd + (uint32_t)(128 * x));
                 else f.sb[x - 4] = lds_load_4B(tiles + s_slot, sc_rd + (uint32_t)(512 + 128 * (x - 4)));
             } else if (m < 4) {
-                f.a[m][g] = lds_load_8B(tiles + a_slot + m * 4096, a_rd[r & 1][g]);
+                if (g & 1) return;
+                f.a[m][g >> 1] = lds_load_16B(tiles + a_slot + m * 4096, a_rd[r & 1][g >> 1]);
             } else {
-                f.b[m - 4][g] = lds_read_tr8(tiles + b_slot + g * 4096, b_rd[m - 4]);
+                f.b[m - 4][g] = lds_read_tr8(tiles + b_slot + (g >> 1) * 8192 + (g & 1) * 2048, b_rd[m - 4]);
             }
         };
-        // Conversion operand of scale x (A blocks 0-3, then B blocks 4-7) for the
-        // 32-token block `sub` (0..3) of the stage (MX), or for the stage's single
-        // block.
-        auto decode_one = [&](Raw& f, int x, int sub) {
+        // Scale operand x (A blocks 0-3, then B blocks 4-7) from the step's scale
+        // dwords, for the 32-token block `sub` (0..3) of the stage (MX) or for the
+        // stage's single block.
+        auto decode_one = [&](const Raw& f, int x, int sub) {
             const uint32_t w = (uint32_t)(x < 4 ? f.sa[x] : f.sb[x - 4]);
             const float v = e8m0_scale_operand(MX ? (w >> (8 * sub)) & 0xFFu : w);
-            if (x < 4) f.fa[x] = v;
-            else f.fb[x - 4] = v;
+            if (x < 4) fa[x] = v;
+            else fb[x - 4] = v;
         };
         // Conversion number c (0..7) of group g: A block c, then B block c-4.
         auto convert_one = [&](const Raw& f, int g, int c, Conv& cv) {
-            if (c < 4) cv.a[c] = cvt_e4m3x8_bf16(f.a[c][g], f.fa[c]);
-            else cv.b[c - 4] = cvt_e4m3x8_bf16(f.b[c - 4][g], f.fb[c - 4]);
+            if (c < 4) {
+                const i32x4 q = f.a[c][g >> 1];
+                const i32x2 h = (g & 1) ? i32x2{q[2], q[3]} : i32x2{q[0], q[1]};
+                cv.a[c] = cvt_e4m3x8_bf16(h, fa[c]);
+            } else {
+                cv.b[c - 4] = cvt_e4m3x8_bf16(f.b[c - 4][g], fb[c - 4]);
+            }
         };
         // MFMA number m (0..15) of a group: N block m/4 times M block m%4.
         auto mfma_one = [&](const Conv& cv, int m) {
@@ -326,7 +343,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
             for (int m = 0; m < 16; ++m) read_one(std::integral_constant<int, 0>(), g, m, r0);
         wait_lgkmcnt0();
 #pragma unroll
-        for (int x = 0; x < 8; ++x) decode_one(r0, x, 0);
+        for (int x = 0; x < 8; ++x) decode_one(r0, x, 0);       // step 0 opens block 0
 #pragma unroll
         for (int c = 0; c < 8; ++c) convert_one(r0, 0, c, c0);
 
@@ -361,7 +378,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
                 Conv& cv = (g & 1) ? c1 : c0;
                 Conv& cn = (g & 1) ? c0 : c1;
                 if (g == 3) {
-                    wait_lgkmcnt<15>();
+                    // the scale reads of group 0 are older than the 12 reads of groups 1-2
+                    wait_lgkmcnt<12>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
@@ -379,7 +397,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_kernel(GroupedParams p) {
                         else convert_one(nxt, 0, m >> 1, cn);
                     } else {
                         if (MX && g == 1) decode_one(cur, m >> 1, 2 * (R & 1) + 1);
-                        if (g == 3) decode_one(nxt, m >> 1, MX ? 2 * ((R + 1) & 1) : 0);
+                        if (g == 3 && reads_scales((R + 1) % 6)) decode_one(nxt, m >> 1, MX ? 2 * ((R + 1) & 1) : 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
