@@ -355,6 +355,33 @@ def _oracle_sample(name: str, target_seconds: float):
             "seconds": dt}
 
 
+def run_mfma_ceiling(iters: int = 20000):
+    """What this board's MFMAs sustain on the workloads' own operand values (kgw_mfma_ceiling):
+    bf16 MFMA on N(0,1)*0.02 bf16 values (the balanced workload's distribution), bf16 MFMA on
+    e4m3 codes converted to bf16 (the exact fp8 path's operands) and the scaled fp8 MFMA on the
+    same codes (the native path), each from the seeded generators of those workloads.  MFMA power
+    depends on the data and the chip lowers its clock past its power limit, so these rates,
+    with the clock they ran at, bound what any kernel can reach on such operands."""
+    import torch
+    import grouped_gemm_expert_offsets_amd as kgw
+    import workloads
+    g = torch.Generator(device="cuda").manual_seed(1)
+    bf = workloads.randn_bf16((1024, 8192), 0.02, g, "cuda")
+    x = workloads.randn_bf16((1024, 8192), 1.0, g, "cuda")
+    codes, _ = workloads.quantize_token_blocks(x, token_axis=1)
+    out = {}
+    for name, src, kind, peak in (("bf16 MFMA, N(0,1)*0.02 bf16 operands", bf, 0, PEAK_BF16_TFLOPS),
+                                  ("bf16 MFMA, e4m3 codes as bf16 (exact fp8 path)", codes, 1, PEAK_BF16_TFLOPS),
+                                  ("scaled fp8 MFMA, e4m3 codes (native fp8 path)", codes, 2, PEAK_FP8_TFLOPS)):
+        for _ in range(3):
+            kgw.kgw_mfma_ceiling(src, kind, iters=iters // 4)
+        tflops, ghz = kgw.kgw_mfma_ceiling(src, kind, iters=iters)
+        out[name] = {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3), "frac_of_peak": round(tflops / peak, 4)}
+    del bf, x, codes
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(target_seconds: float):
     """The CPU oracle on a bounded sample of every configuration (about `target_seconds` in
     all), plus a one-thread sample of the balanced workload; the headline's is the top level."""
@@ -504,6 +531,10 @@ def main():
             for axis in (1, 0):
                 add(run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4))
         line["secondary"] = sec
+        line["mfma_ceiling"] = run_mfma_ceiling()
+        if kind == "fp8" and not args.native_fp8:
+            ceil = line["mfma_ceiling"]["bf16 MFMA, e4m3 codes as bf16 (exact fp8 path)"]["tflops"]
+            line["roofline"]["frac_of_measured_mfma_ceiling"] = head["tflops"] / ceil
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -30,7 +30,7 @@ __all__ = [
     "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT",
     "KGW_LAYOUT_NN",
     "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
-    "kgw_validate_offsets", "kgw_check_offsets",
+    "kgw_validate_offsets", "kgw_check_offsets", "kgw_mfma_ceiling",
     "kgw_validate_offsets_host", "kgw_status_string", "kgw_device_info", "wgrad",
     "KGW_SUCCESS", "KGW_ERROR_INVALID_VALUE", "KGW_ERROR_MISALIGNED", "KGW_ERROR_BAD_OFFSETS",
     "KGW_ERROR_UNSUPPORTED", "KGW_ERROR_DEVICE", "KGW_OUT_FP32", "KGW_OUT_BF16", "KGW_OUT_FP16",
@@ -67,7 +67,7 @@ _lib = None
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_noalloc", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
                     "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16",
                     "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_check_offsets",
-                    "kgw_status_string", "kgw_device_info")
+                    "kgw_mfma_ceiling", "kgw_status_string", "kgw_device_info")
 
 
 def load_library():
@@ -108,6 +108,8 @@ def load_library():
     lib.kgw_validate_offsets.argtypes = [p, i32, i64, i32, ctypes.POINTER(i32), p]
     lib.kgw_check_offsets.restype = ctypes.c_int
     lib.kgw_check_offsets.argtypes = [p, i32, i64, i32, p, p]
+    lib.kgw_mfma_ceiling.restype = ctypes.c_int
+    lib.kgw_mfma_ceiling.argtypes = [p, i64, i32, i32, i32, p, p]
     lib.kgw_status_string.restype = ctypes.c_char_p
     lib.kgw_status_string.argtypes = [ctypes.c_int]
     lib.kgw_device_info.restype = ctypes.c_int
@@ -589,6 +591,30 @@ def kgw_check_offsets(offsets: torch.Tensor, tokens_sum: int, alignment: int,
                                           _ptr(result), _stream_ptr(stream))
     _check(st, "kgw_check_offsets")
     return result
+
+
+def kgw_mfma_ceiling(src: torch.Tensor, kind: int, iters: int = 20000, workgroups: int = 1024,
+                     stream=None) -> Tuple[float, float]:
+    """Time MFMA-only loops on the bytes of `src` (kind 0 bf16, 1 e4m3 as bf16, 2 e4m3 on the scaled
+    fp8 MFMA): returns (TFLOP/s from HIP events around the launch, mean clock in GHz the loop ran
+    at).  A measurement helper: it synchronises."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    cycles = torch.zeros(2 * workgroups, dtype=torch.int64, device=src.device)
+    s = torch.cuda.current_stream(src.device) if stream is None else stream
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    st = load_library().kgw_mfma_ceiling(_ptr(src), src.numel() * src.element_size(), int(kind), int(iters),
+                                         int(workgroups), _ptr(cycles), int(s.cuda_stream))
+    end.record(s)
+    _check(st, "kgw_mfma_ceiling")
+    end.synchronize()
+    ms = start.elapsed_time(end)
+    c = cycles.view(-1, 2).double().cpu()
+    ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1
+    flop_per_mfma = 131072.0 if kind == 2 else 32768.0
+    flops = 16.0 * iters * workgroups * 4 * flop_per_mfma
+    return flops / (ms * 1e-3) / 1e12, ghz
 
 
 def kgw_device_info() -> dict:

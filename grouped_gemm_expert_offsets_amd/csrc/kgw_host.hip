@@ -454,6 +454,21 @@ kgw_status_t kgw_check_offsets(const int32_t* offsets, int32_t num_experts, int6
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 
+kgw_status_t kgw_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters, int32_t workgroups,
+                              uint64_t* cycles, void* stream) {
+    if (!src || !cycles || src_bytes < 4096 || kind < 0 || kind > 2 || iters < 1 || iters > 10000000 ||
+        workgroups < 1 || workgroups > 65536)
+        return KGW_ERROR_INVALID_VALUE;
+    if (src_bytes >= ((int64_t)1 << 34)) return KGW_ERROR_UNSUPPORTED;
+    if (((uintptr_t)src & 3u) || ((uintptr_t)cycles & 7u)) return KGW_ERROR_MISALIGNED;
+    DeviceProps d;
+    const kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    const hipError_t err = kgw::launch_mfma_ceiling(src, src_bytes, kind, iters, workgroups, cycles, (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
 const char* kgw_status_string(kgw_status_t status) {
     switch (status) {
         case KGW_SUCCESS: return "success";

@@ -106,6 +106,9 @@ hipError_t launch_wgrad_fp4(const GroupedParams& p, int out_kind, int grid, hipS
 // First expert whose count breaks the offsets contract, or -1, into result[0] (one workgroup).
 hipError_t launch_check_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum, int32_t alignment,
                                 int32_t* result, hipStream_t stream);
+// Measurement helper: MFMA-only loops on operand data from `src` (see kgw_mfma_ceiling).
+hipError_t launch_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters, int32_t workgroups,
+                               uint64_t* cycles, hipStream_t stream);
 hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

@@ -298,3 +298,16 @@ def test_noalloc_entry_point_argument_errors(lib):
     assert f(FAKE, FAKE, FAKE, 4, 256, 516, 1024, FAKE, 0, 0, None) == kgw.KGW_ERROR_MISALIGNED
     assert f(FAKE, FAKE, FAKE, 4, 256, 512, 1024, FAKE, 3, 0, None) == kgw.KGW_ERROR_INVALID_VALUE
     assert f(None, None, FAKE, 4, 0, 512, 1024, None, 0, 0, None) == kgw.KGW_SUCCESS      # no output elements
+
+
+def test_mfma_ceiling_argument_errors(lib):
+    f = lib.kgw_mfma_ceiling
+    bad = kgw.KGW_ERROR_INVALID_VALUE
+    assert f(None, 1 << 20, 0, 100, 256, FAKE, None) == bad
+    assert f(FAKE, 1 << 20, 0, 100, 256, None, None) == bad
+    assert f(FAKE, 1024, 0, 100, 256, FAKE, None) == bad            # fewer than 4096 bytes
+    assert f(FAKE, 1 << 20, 3, 100, 256, FAKE, None) == bad         # unknown kind
+    assert f(FAKE, 1 << 20, 0, 0, 256, FAKE, None) == bad
+    assert f(FAKE, 1 << 20, 0, 100, 0, FAKE, None) == bad
+    assert f(FAKE + 2, 1 << 20, 0, 100, 256, FAKE, None) == kgw.KGW_ERROR_MISALIGNED
+    assert f(FAKE, 1 << 20, 0, 100, 256, FAKE + 4, None) == kgw.KGW_ERROR_MISALIGNED

@@ -590,3 +590,13 @@ def test_full_many_small():
     rng = np.random.default_rng(0)
     pick = sorted(set([ne[0], ne[-1]] + rng.choice(ne, 16, replace=False).tolist()))
     check_sampled(wl, out, pick, rows_per_expert=4)
+
+
+def test_mfma_ceiling_helper_runs():
+    # the measurement helper: a finite rate and a clock in the chip's range for every kind
+    g = torch.Generator(device=DEV).manual_seed(9)
+    x = workloads.randn_bf16((256, 4096), 1.0, g, DEV)
+    codes, _ = workloads.quantize_token_blocks(x, token_axis=1)
+    for src, kind in ((x, 0), (codes, 1), (codes, 2)):
+        tflops, ghz = kgw.kgw_mfma_ceiling(src, kind, iters=200, workgroups=256)
+        assert 1.0 < tflops < 12000.0 and 0.3 < ghz < 3.5, (kind, tflops, ghz)
