@@ -127,18 +127,88 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
     const int G = gridDim.x;
     const int slot = xcd_slot(blockIdx.x, G, p.num_xcds);
 
-    // Round r covers items [r*G, (r+1)*G); with p.snake the slots of odd rounds run in
-    // reverse, so a workgroup alternates between the front and the back of consecutive
-    // rounds (each XCD still holds a contiguous run of 32 items).
-    for (int r = 0; r * G < p.num_items; ++r) {
-        const int item = r * G + ((r & 1) && p.snake ? G - 1 - slot : slot);
-        if (item >= p.num_items) continue;
+    // Static schedule: round r covers items [r*G, (r+1)*G); with p.snake the slots of odd
+    // rounds run in reverse, so a workgroup alternates between the front and the back of
+    // consecutive rounds (each XCD still holds a contiguous run of 32 items).
+    //
+    // Dynamic schedule (p.sched): the same runs of G/nq items per round form nq queues, one
+    // per XCD (queue q: the q-th run of every round), claimed one item at a time through
+    // the queue's counter; a workgroup drains the queue of its XCD (block id mod nq, the
+    // hardware's round-robin placement), then those of the next ones, so every claimed
+    // index is unique and every workgroup stops after at most nq empty claims.  Experts
+    // run longest first: lane k of every wave holds the expert of rank k (ties by index),
+    // so the last items to be claimed are the shortest.  Thread 0 claims the next item
+    // while the current one writes its output, and passes it on through LDS word 0 (the
+    // rings are idle between items) between two barriers.
+    const bool dyn = p.sched != nullptr;
+    int perm = lane;
+    if (dyn) {
+        const int E = p.num_experts;                        // <= kSchedMaxExperts
+        int cnt = -1;
+        if (lane < E) {
+            const int64_t b0 = lane ? (int64_t)p.offsets[lane - 1] : 0, e0 = p.offsets[lane];
+            const int64_t b1 = b0 < 0 ? 0 : (b0 > T ? T : b0);
+            const int64_t e1 = e0 < 0 ? 0 : (e0 > T ? T : e0);
+            cnt = (int)(e1 > b1 ? e1 - b1 : 0);
+        }
+        int rank = lane;
+        if (lane < E) {
+            rank = 0;
+            for (int j = 0; j < E; ++j) {
+                const int cj = __builtin_amdgcn_readlane(cnt, j);
+                rank += (cj > cnt || (cj == cnt && j < lane)) ? 1 : 0;
+            }
+        }
+        perm = __builtin_amdgcn_ds_permute(rank << 2, lane);
+    }
+    const int nq = p.num_xcds, qrun = G / p.num_xcds;
+    int q = (int)(blockIdx.x % (unsigned)nq), left = nq;    // thread 0's queue state
+    int r = 0;                                              // static: next round
+    // thread 0: the item of raw claim `idx` in queue q; an exhausted queue sends it on to
+    // the next one (claiming there), -1 once every queue is exhausted
+    auto resolve = [&](int idx) -> int {
+        for (;;) {
+            const int it = (idx / qrun) * G + q * qrun + idx % qrun;
+            if (it < p.num_items) return it;
+            if (--left == 0) return -1;
+            q = q + 1 == nq ? 0 : q + 1;
+            idx = atomicAdd(p.sched + q, 1);
+        }
+    };
+    auto broadcast = [&](int v) -> int {
+        if (tid == 0) *(__attribute__((address_space(3))) int*)tiles = v;
+        barrier_no_fence();
+        v = *(__attribute__((address_space(3))) int*)tiles;
+        barrier_no_fence();
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    auto next_static = [&]() -> int {
+        while (r * G < p.num_items) {
+            const int it = r * G + ((r & 1) && p.snake ? G - 1 - slot : slot);
+            ++r;
+            if (it < p.num_items) return it;
+        }
+        return -1;
+    };
+    int pend = 0;                                           // thread 0: raw claim of the next item
+    auto claim_next = [&]() {
+        if (dyn && tid == 0) pend = atomicAdd(p.sched + q, 1);
+    };
+    auto next_item = [&]() -> int {
+        if (!dyn) return next_static();
+        return broadcast(tid == 0 ? resolve(pend) : 0);
+    };
+    if (dyn && tid == 0) pend = atomicAdd(p.sched + q, 1);
+    for (int item = next_item(); item >= 0; item = next_item()) {
         const int ec = item / TT;
         const int local = item - ec * TT;
-        const int e = ec / p.split;
-        const int c = ec - e * p.split;
+        const int e = dyn ? __builtin_amdgcn_readlane(perm, ec) : ec / p.split;   // dynamic: split is 1
+        const int c = ec - (dyn ? ec : e * p.split);
         const int eo = c * p.num_experts + e;
-        if (p.out_ptrs && !p.out_ptrs[eo]) continue;
+        if (p.out_ptrs && !p.out_ptrs[eo]) {
+            claim_next();
+            continue;
+        }
         int tm, tn;
         tile_coords(local, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
@@ -160,6 +230,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         else begin &= ~(2 * BK - 1);
         const int ksteps = ((end - begin) / (2 * BK)) * 2;
         if (ksteps == 0) {
+            claim_next();
             if (!p.accumulate) zero_slab_part<OUT, NT>(p, eo, local, TT, tid);
             continue;
         }
@@ -396,6 +467,7 @@ __global__ __launch_bounds__(NT, 1) void wgrad_bf16_kernel(GroupedParams p) {
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
+        claim_next();
         store_wave_tile_staged<OUT>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         barrier_no_fence();
     }

@@ -113,6 +113,22 @@ struct SplitPlan {
     size_t bytes = 0;
 };
 
+// Dynamic schedule of the bf16 kernel (claim counters in the workspace, experts longest
+// first): for long experts and at least this many rounds of the persistent grid, where
+// the static stride leaves CUs unevenly loaded (skewed counts: ~5% modelled).  With only a
+// few rounds, which items meet on one CU is a matter of luck either way, and the static
+// reversed rounds do as well; short experts are bound by their output stores.
+constexpr int64_t kDynMinRounds = 8;
+
+bool dynamic_plan(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int num_cus) {
+    if (num_experts < 1 || num_experts > kgw::kSchedMaxExperts || hidden <= 0 || n <= 0 || num_cus <= 0) return false;
+    if (num_cus % 8 != 0) return false;
+    const int64_t items = ((hidden + kgw::kBf16BM - 1) / kgw::kBf16BM) * ((n + kgw::kBf16BN - 1) / kgw::kBf16BN) *
+                          num_experts;
+    const bool short_experts = tokens_sum < (int64_t)kShortExpertTokens * num_experts;
+    return !short_experts && items >= kDynMinRounds * num_cus;
+}
+
 SplitPlan split_plan(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, bool fp8, int num_cus) {
     SplitPlan plan;
     if (num_experts < 1 || hidden <= 0 || n <= 0 || tokens_sum <= 0 || num_cus <= 0) return plan;
@@ -222,8 +238,17 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
         p.accumulate = 0;
         out_kind = kgw::kOutF32;
     }
+    p.sched = nullptr;
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
-    hipError_t err;
+    hipError_t err = hipSuccess;
+    if (kernel == Kernel::kBf16 && !split && dynamic_plan(num_experts, hidden, n, tokens_sum, d.num_cus) &&
+        workspace && workspace_bytes >= kgw::kSchedWords * sizeof(int32_t) && aligned16(workspace) &&
+        grid % d.num_xcds == 0) {
+        p.sched = (int32_t*)workspace;
+        p.snake = 0;
+        err = kgw::launch_sched_reset(p.sched, (hipStream_t)stream);
+        if (err != hipSuccess) return KGW_ERROR_DEVICE;
+    }
     switch (kernel) {
         case Kernel::kBf16:
             err = layout ? kgw::launch_wgrad_bf16_layout(p, (layout & KGW_A_M_MAJOR) != 0,
@@ -404,7 +429,10 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum, int32_t fp8) {
     DeviceProps d;
     const int cus = current_props(&d) == KGW_SUCCESS ? d.num_cus : kDefaultCus;
-    return split_plan(num_experts, hidden, n, tokens_sum, fp8 != 0, cus).bytes;
+    const size_t split = split_plan(num_experts, hidden, n, tokens_sum, fp8 != 0, cus).bytes;
+    if (split) return split;
+    if (!fp8 && dynamic_plan(num_experts, hidden, n, tokens_sum, cus)) return kgw::kSchedWords * sizeof(int32_t);
+    return 0;
 }
 
 kgw_status_t kgw_validate_offsets_host(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum,

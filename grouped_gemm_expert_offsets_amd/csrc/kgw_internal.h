@@ -40,7 +40,14 @@ struct GroupedParams {
     int32_t ragged;         // bf16 layouts: A and B are per-expert (., n_e) blocks back to back
     int32_t group_m;        // bf16: M tiles per column of the tile order (4 or 8)
     int32_t snake;          // bf16: odd rounds of the persistent stride run the slots in reverse
+    int32_t* sched;         // bf16: kSchedWords zeroed counters -> dynamic schedule (NULL: static)
 };
+
+// Dynamic schedule of the bf16 kernel: one claim counter per XCD queue, zeroed by
+// launch_sched_reset on the launch stream right before the kernel.  Experts run longest
+// first (at most kSchedMaxExperts of them, each its own lane of a wave).
+constexpr int kSchedWords = 64;              // 256 bytes of the caller's workspace
+constexpr int kSchedMaxExperts = 64;
 
 // Scales of the global 128-token block gb in layout FMT: the value for mn
 // index i is the byte (kScalesU8, kScalesPacked) or the word of four 32-token
@@ -97,6 +104,8 @@ hipError_t launch_splitk_reduce(const float* ws, const int32_t* offsets, int32_t
                                 int64_t n, int64_t tokens_sum, int32_t split, void* out, void* const* out_ptrs,
                                 int out_kind, int32_t accumulate, int num_cus, hipStream_t stream);
 hipError_t launch_wgrad_fp8(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// Zeroes the kSchedWords counters of the dynamic schedule (a kernel, so graph capture records no memset).
+hipError_t launch_sched_reset(int32_t* sched, hipStream_t stream);
 hipError_t launch_quantize_fp8(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,
                                void* q, void* s, int num_cus, hipStream_t stream);
 hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_t token_axis, int32_t scale_format,

@@ -5,7 +5,8 @@
 // offending expert (or -1) to a device word, so the check stays on the stream:
 // no copy to the host, no synchronisation, nothing for the caller to allocate
 // beyond that word.  The GEMM kernels clamp malformed ranges on their own; this
-// is the flag that says it happened.
+// is the flag that says it happened.  (Also here: the reset of the bf16 kernel's
+// dynamic-schedule counters, another one-workgroup bookkeeping kernel.)
 #include "kgw_internal.h"
 
 namespace kgw {
@@ -35,7 +36,16 @@ __global__ __launch_bounds__(kCheckThreads) void check_offsets_kernel(const int3
     if (threadIdx.x == 0) result[0] = first_bad < num_experts ? first_bad : -1;
 }
 
+__global__ void sched_reset_kernel(int32_t* __restrict__ sched) {
+    if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_sched_reset(int32_t* sched, hipStream_t stream) {
+    hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(kSchedWords), 0, stream, sched);
+    return hipGetLastError();
+}
 
 hipError_t launch_check_offsets(const int32_t* offsets, int32_t num_experts, int64_t tokens_sum, int32_t alignment,
                                 int32_t* result, hipStream_t stream) {

@@ -114,15 +114,22 @@ typedef enum {
  *                  left untouched, bit for bit);
  *               0: out[e]  = Wgrad[e] (an empty expert is written with +0.0).
  *            Section "Operation" of the cuDNN page defines both modes.
- *   workspace, workspace_bytes  device scratch for split-K, owned by the caller:
- *            at least kgw_workspace_bytes(...) bytes, 16-byte aligned, not
- *            used by another call at the same time; it needs no initial
- *            contents.  When that size is 0 (most shapes) or the workspace is
- *            NULL or smaller, the call runs in one pass.  With it, each
- *            expert's token range is cut into chunks whose fp32 partials land
- *            in the workspace and a second pass sums them in chunk order before
- *            applying the output mode once: the result differs from the
- *            one-pass result only by the order of the fp32 additions.
+ *   workspace, workspace_bytes  device scratch owned by the caller: at least
+ *            kgw_workspace_bytes(...) bytes, 16-byte aligned, not used by
+ *            another call at the same time; it needs no initial contents.  When
+ *            that size is 0 or the workspace is NULL or smaller, the call runs
+ *            in one pass on the static schedule.  Otherwise it holds either
+ *            (few output tiles) split-K partials: each expert's token range is
+ *            cut into chunks whose fp32 partials land in the workspace and a
+ *            second pass sums them in chunk order before applying the output
+ *            mode once -- the result differs from the one-pass result only by
+ *            the order of the fp32 additions -- or (many rounds of output tiles,
+ *            at most 64 experts averaging 1024+ tokens) the 256-byte claim
+ *            counters of the dynamic schedule, which the call zeroes itself (a
+ *            kernel queued before the product) -- the result is bit for bit the
+ *            static schedule's, since every tile is still computed whole by one
+ *            workgroup (cuDNN page, section "Scheduling, cache, and errors":
+ *            dynamic persistent scheduling for the BF16 kernel).
  *
  * Sizes: 1 <= num_experts <= 65536; 0 <= hidden, n < 2^28; tokens_sum >= 0 and a
  * multiple of 256; n a multiple of 8; tokens_sum < 2^31 (int32 offsets).
@@ -139,13 +146,15 @@ kgw_status_t kgw_wgrad_bf16(const void* A, const void* B, const int32_t* offsets
  * kgw_wgrad_bf16_noalloc -- kgw_wgrad_bf16 for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, contract, errors and kernels as kgw_wgrad_bf16, minus
- * the workspace: where kgw_wgrad_bf16 would split K and the fp32 partials take at most
- * 64 MiB, they go to a fixed 64 MiB scratch array the library holds on every device it
- * runs on (until the process ends), so the result is bit for bit that of
- * kgw_wgrad_bf16 given a workspace of kgw_workspace_bytes(...) bytes.  A shape whose
- * partials would need more than those 64 MiB runs in one pass instead (no error: one
- * pass needs no scratch; the result then differs only by the order of the fp32
- * additions).  The call allocates and frees nothing.
+ * the workspace: where kgw_wgrad_bf16 would use one (split-K partials, or the dynamic
+ * schedule's claim counters), the call uses a fixed 64 MiB scratch array the library
+ * holds on every device it runs on (until the process ends), so the result is bit for
+ * bit that of kgw_wgrad_bf16 given a workspace of kgw_workspace_bytes(...) bytes.  The
+ * split plan keeps chunks x tiles within the compute units and a 256 x 256 fp32 tile
+ * takes 256 KiB, so on MI355X's 256 compute units every planned split fits those
+ * 64 MiB; on a device with more compute units a plan that would not fit runs in one
+ * pass instead (no error: one pass needs no scratch; the result then differs only by
+ * the order of the fp32 additions).  The call allocates and frees nothing.
  * All calls on one device share that device's scratch, which keeps the last call's
  * contents (no call needs it to start at zero): two calls that overlap in time on the
  * same device -- on different streams, or from different threads -- race on it and may
@@ -394,11 +403,15 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
 /*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape
  * on the current device (fp8 != 0 selects the fp8 entry points; 256 compute
- * units are assumed when no device is visible).  It is nonzero only when the
- * output tiles alone would leave more than half of the compute units idle and
- * the experts average at least 2048 tokens: then the call splits each expert's
- * token range into 2..16 chunks (split-K) and needs
- * chunks * num_experts * hidden * n * 4 bytes, at most 1 GiB.  0 means one pass.
+ * units are assumed when no device is visible).  Nonzero in two cases:
+ *  - the output tiles alone would leave more than half of the compute units idle
+ *    and the experts average at least 2048 tokens: the call splits each expert's
+ *    token range into 2..16 chunks (split-K) and needs
+ *    chunks * num_experts * hidden * n * 4 bytes, at most 1 GiB;
+ *  - (bf16) the output tiles fill the compute units at least 8 times over, with at
+ *    most 64 experts averaging 1024 or more tokens: 256 bytes of claim counters
+ *    for the dynamic schedule.
+ * 0 means one pass on the static schedule.
  */
 size_t kgw_workspace_bytes(int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                            int32_t fp8);

@@ -48,12 +48,14 @@ def test_workspace_is_zero(lib):
 
 
 def test_workspace_bytes_split_k_plan():
-    # the five workload shapes have enough tiles to fill the chip: one pass, no workspace
+    # the five workload shapes have enough tiles to fill the chip: no split; only the skewed one
+    # (32 long experts, 49 rounds of tiles) takes the dynamic schedule's 256 bytes of counters
     import workloads
     for name in workloads.CONFIG_NAMES:
         spec = workloads.config_spec(name, 1)
+        want = 256 if name == "skewed" else 0
         assert kgw.kgw_workspace_bytes(len(spec["counts"]), spec["hidden"], spec["n"], sum(spec["counts"]),
-                                       fp8=spec["kind"] == "fp8") == 0, name
+                                       fp8=spec["kind"] == "fp8") == want, name
     # few tiles and many tokens: split-K into chunks * E * hidden * n fp32 partials
     # (256 CUs when no device is visible: 4 tiles -> up to 16 chunks, 8 by tokens/(E*1024))
     assert kgw.kgw_workspace_bytes(2, 256, 512, 16384) == 8 * 2 * 256 * 512 * 4
@@ -62,6 +64,16 @@ def test_workspace_bytes_split_k_plan():
     assert kgw.kgw_workspace_bytes(2, 256, 512, 4096 - 256) == 0
     # more than half of the CUs already have a tile
     assert kgw.kgw_workspace_bytes(1, 256 * 16, 256 * 9, 1 << 20) == 0
+
+
+def test_workspace_bytes_dynamic_schedule_plan():
+    # 256 bytes of counters: bf16 only, long experts (>= 1024 tokens on average), at most 64 of
+    # them, and at least 8 rounds of tiles on 256 CUs (2048 items)
+    assert kgw.kgw_workspace_bytes(32, 2048, 2048, 32 * 1024) == 256          # 2048 items
+    assert kgw.kgw_workspace_bytes(32, 2048, 2048 - 256, 32 * 1024) == 0      # 1792 items
+    assert kgw.kgw_workspace_bytes(32, 2048, 2048, 32 * 1024 - 256) == 0      # short experts
+    assert kgw.kgw_workspace_bytes(65, 2048, 2048, 65 * 1024) == 0            # more than 64 experts
+    assert kgw.kgw_workspace_bytes(32, 2048, 2048, 32 * 1024, fp8=True) == 0  # fp8 kernels: static
 
 
 def validate(offsets, tokens_sum, align=256):

@@ -465,6 +465,45 @@ def test_bf16_multi_round_schedule_random_bf16_out(branch):
     assert_bf16_close(to_f64(out), oracle.apply_output_mode(W, False), f"{branch} bf16")
 
 
+def _dynamic_counts(seed):
+    # 32 experts, lognormal sizes in 256-token units, two empty, about 36k tokens: at least
+    # 1024 tokens on average and 32 x 64 = 2048 tiles of 2048 x 2048, the dynamic schedule
+    rng = np.random.default_rng(seed)
+    units = np.maximum(1, np.rint(rng.lognormal(np.log(3.0), 1.0, size=32))).astype(np.int64)
+    units = np.maximum(1, (units * 160) // units.sum())
+    units[rng.choice(32, 2, replace=False)] = 0
+    counts = (256 * units).tolist()
+    assert sum(counts) >= 1024 * 32 and kgw.kgw_workspace_bytes(32, 2048, 2048, sum(counts)) == 256
+    return counts
+
+
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_bf16_dynamic_schedule_integer_every_element(accumulate):
+    counts = _dynamic_counts(81 + accumulate)
+    wl = workloads.make_operands(counts, 2048, 2048, "bf16", torch.float32, accumulate, seed=83, device=DEV,
+                                 integer_range=4)
+    out = wl.C0.clone() if accumulate else nan_filled((32, 2048, 2048), torch.float32)
+    run_bf16(wl, out=out, accumulate=accumulate)
+    W = oracle_dense(wl)
+    ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
+    got = to_f64(out)
+    mism = np.argwhere(got != ref)
+    assert mism.size == 0, f"{len(mism)} mismatches, first {tuple(mism[0])}: {got[tuple(mism[0])]} vs {ref[tuple(mism[0])]}"
+
+
+def test_bf16_dynamic_schedule_same_bits_as_static():
+    # every tile is computed whole by one workgroup either way: identical outputs, with the
+    # workspace (dynamic) and without (static), on random operands, bf16 output
+    counts = _dynamic_counts(85)
+    wl = workloads.make_operands(counts, 2048, 2048, "bf16", torch.bfloat16, False, seed=86, device=DEV)
+    dyn = kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out_dtype=torch.bfloat16)
+    sta = kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out_dtype=torch.bfloat16, split_k=False)
+    again = kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dyn.view(torch.int16), sta.view(torch.int16))
+    assert torch.equal(dyn.view(torch.int16), again.view(torch.int16))
+
+
 @pytest.mark.parametrize("native", [False, True])
 def test_fp8_multi_round_schedule_integer_every_element(native):
     counts = workloads.counts_uniform(6, 2048, 128, 9)                    # 384 items: 2 rounds

@@ -87,3 +87,14 @@ def test_noalloc_one_pass_shape_and_scratch_bound():
     big = _case([16384, 16384], 2048, 2048, torch.float32, False, seed=94)
     assert kgw.kgw_workspace_bytes(2, 2048, 2048, 32768) == SCRATCH_BYTES
     _compare(big, torch.float32, False)
+
+
+def test_noalloc_dynamic_schedule_shape():
+    # a shape on the dynamic schedule: its claim counters live in the scratch too
+    rng = np.random.default_rng(95)
+    counts = (256 * rng.integers(3, 8, size=32)).tolist()
+    assert kgw.kgw_workspace_bytes(32, 2048, 2048, sum(counts)) == 256
+    wl = _case(counts, 2048, 2048, torch.bfloat16, False, seed=96)
+    _compare(wl, torch.bfloat16, False)
+    small = _case([2048, 4096], 256, 256, torch.float32, True, seed=97)      # then a split-K call
+    _compare(small, torch.float32, True)
