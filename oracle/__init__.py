@@ -86,6 +86,8 @@ def _load():
     lib.oracle_quantize_fp4_tokens.argtypes = [p, i64, i64, p, p]
     lib.oracle_mgrouped_bf16.restype = ctypes.c_int
     lib.oracle_mgrouped_bf16.argtypes = [p, p, p, i64, i64, i64, i32, ctypes.c_int, p]
+    lib.oracle_mgrouped_fp8.restype = ctypes.c_int
+    lib.oracle_mgrouped_fp8.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.oracle_quantize_fp8_tokens.restype = ctypes.c_int
     lib.oracle_quantize_fp8_tokens.argtypes = [p, i64, i64, ctypes.c_int, p, p, i64]
     _lib = lib
@@ -382,6 +384,28 @@ def mgrouped_bf16(A, W, *, offsets=None, m_indices=None, layout: str = "nt") -> 
     assert grp.shape == (M,)
     out = np.empty((M, N), dtype=np.float64)
     _load().oracle_mgrouped_bf16(_ptr(a), _ptr(w), _ptr(grp), M, K, N, E, int(nt), _ptr(out))
+    return out
+
+
+def mgrouped_fp8(A, sa, W, sw, *, offsets=None, m_indices=None) -> np.ndarray:
+    """(M, N) float64 result of the fp8 m-grouped forward product; rows of no group are NaN.
+
+    A e4m3 bytes (M, K), sa UE8M0 bytes (K/128, M); W e4m3 bytes (E, N, K), sw UE8M0 bytes
+    (E, K/128, N): each value is e4m3(code) * 2^(scale - 127) with the scale of its 1x128 block
+    along K.  Groups from inclusive cumulative `offsets` or per-row `m_indices`.
+    """
+    a, s_a, w, s_w = _u8(A), _u8(sa), _u8(W), _u8(sw)
+    M, K = a.shape
+    E, N = w.shape[0], w.shape[1]
+    assert K % 128 == 0 and w.shape[2] == K, "K must be a multiple of 128 and match W"
+    assert s_a.shape == (K // 128, M) and s_w.shape == (E, K // 128, N), "scale shapes"
+    if m_indices is not None:
+        grp = np.ascontiguousarray(np.asarray(_as_numpy(m_indices), dtype=np.int32))
+    else:
+        grp = row_groups_from_offsets(offsets, M)
+    assert grp.shape == (M,)
+    out = np.empty((M, N), dtype=np.float64)
+    _load().oracle_mgrouped_fp8(_ptr(a), _ptr(s_a), _ptr(w), _ptr(s_w), _ptr(grp), M, K, N, E, _ptr(out))
     return out
 
 

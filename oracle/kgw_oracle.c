@@ -304,6 +304,44 @@ int oracle_mgrouped_bf16(const uint16_t* A, const uint16_t* W, const int32_t* gr
 }
 
 /*
+ * m-grouped forward product with fp8 operands (llm-infra-atlas "05 Grouped GEMM":
+ * section 2.1 names m_grouped_fp8_gemm_nt_contiguous, section 3 gives its inputs as
+ * (values, scales) pairs with one power-of-two scale per 1x128 block along K, the
+ * scale tensor mn-major).  Row m of group g = group[m]:
+ *
+ *     out[m][j] = sum_k a(m, k) * w(g, j, k)
+ *     a(m, k)    = e4m3(A[m*K + k])       * 2^(sa[(k/128)*M + m] - 127)
+ *     w(g, j, k) = e4m3(W[(g*N + j)*K + k]) * 2^(sw[(g*(K/128) + k/128)*N + j] - 127)
+ *
+ * A (M, K) and W (E, N, K) are K-contiguous e4m3 bytes; sa (K/128, M) and sw
+ * (E, K/128, N) hold UE8M0 bytes with the row / column index contiguous.  Each sum
+ * in fp64 over k in increasing order; a row of no group is NaN.  Returns 0.
+ */
+int oracle_mgrouped_fp8(const uint8_t* A, const uint8_t* sa, const uint8_t* W, const uint8_t* sw,
+                        const int32_t* group, int64_t M, int64_t K, int64_t N, int32_t num_groups, double* out) {
+    const int64_t kb = K / 128;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t m = 0; m < M; ++m) {
+        double* o = out + m * N;
+        const int32_t g = group[m];
+        if (g < 0 || g >= num_groups) {
+            for (int64_t j = 0; j < N; ++j) o[j] = NAN;
+            continue;
+        }
+        const uint8_t* Wg = W + (int64_t)g * N * K;
+        const uint8_t* swg = sw + (int64_t)g * kb * N;
+        for (int64_t j = 0; j < N; ++j) o[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = oracle_e4m3fn_value(A[m * K + k]) * oracle_e8m0_value(sa[(k / 128) * M + m]);
+            const uint8_t* srow = swg + (k / 128) * N;
+            for (int64_t j = 0; j < N; ++j)
+                o[j] += a * (oracle_e4m3fn_value(Wg[j * K + k]) * oracle_e8m0_value(srow[j]));
+        }
+    }
+    return 0;
+}
+
+/*
  * FP4 (OCP e2m1) operands with one UE8M0 scale per 32 tokens (the DeepGEMM
  * k-grouped page's per_token_cast_to_fp4 with gran_k = 32; the MX block of the
  * OCP formats).  e2m1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent

@@ -680,3 +680,85 @@ def test_thread_count_does_not_change_results():
     finally:
         oracle.set_num_threads(threads)
     assert np.array_equal(one, many)
+
+
+# ----------------------------------------------------------------------------
+# fp8 m-grouped forward product (llm-infra-atlas section 2.1 / section 3)
+# ----------------------------------------------------------------------------
+FINITE_E4M3 = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def _e4m3_f64(codes):
+    # torch's own e4m3fn decoder: independent of the oracle's
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _fp8_mgrouped_case(counts, K, N, seed, pad_rows=0):
+    rng = np.random.default_rng(seed)
+    M, E = sum(counts) + pad_rows, len(counts)
+    A = rng.choice(FINITE_E4M3, (M, K))
+    W = rng.choice(FINITE_E4M3, (E, N, K))
+    sa = rng.integers(118, 137, (K // 128, M)).astype(np.uint8)
+    sw = rng.integers(118, 137, (E, K // 128, N)).astype(np.uint8)
+    return A, sa, W, sw, np.cumsum(counts).astype(np.int32), M
+
+
+def _dequant_rows(codes, scales_kb_by_row):
+    # codes (R, K); scales (K/128, R) -> values (R, K), each scale repeated over its 128 values
+    return _e4m3_f64(codes) * np.exp2(np.repeat(scales_kb_by_row.T.astype(np.float64) - 127.0, 128, axis=1))
+
+
+def test_mgrouped_fp8_matches_brute_force(oracle_lib):
+    counts = [3, 0, 5, 2]
+    A, sa, W, sw, off, M = _fp8_mgrouped_case(counts, 256, 6, seed=41, pad_rows=2)
+    got = oracle.mgrouped_fp8(A, sa, W, sw, offsets=off)
+    a = _dequant_rows(A, sa)
+    start = 0
+    for e, c in enumerate(counts):
+        w = _dequant_rows(W[e], sw[e])                           # (N, K)
+        want = a[start:start + c] @ w.T
+        np.testing.assert_allclose(got[start:start + c], want, rtol=1e-12, atol=1e-12 * np.abs(want).max(initial=1))
+        start += c
+    assert np.all(np.isnan(got[start:]))                         # rows past the last offset: no group
+
+
+def test_mgrouped_fp8_integers_unit_scales_exact_single_group(oracle_lib):
+    rng = np.random.default_rng(42)
+    Ai = rng.integers(-8, 9, (5, 256)).astype(np.float64)
+    Wi = rng.integers(-8, 9, (1, 7, 256)).astype(np.float64)
+    A = torch.from_numpy(Ai).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    W = torch.from_numpy(Wi).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sa = np.full((2, 5), 127, np.uint8)
+    sw = np.full((1, 2, 7), 127, np.uint8)
+    got = oracle.mgrouped_fp8(A, sa, W, sw, offsets=np.array([5], dtype=np.int32))
+    assert np.array_equal(got, Ai @ Wi[0].T)
+
+
+def test_mgrouped_fp8_scale_byte_doubles_its_block(oracle_lib):
+    # only K block 1 of A is nonzero; raising sw[g=0, kb=1, j=2] by one doubles column 2 of
+    # group 0's rows, exactly, and changes nothing else
+    A, sa, W, sw, off, M = _fp8_mgrouped_case([4, 3], 384, 5, seed=43)
+    A[:, :128] = 0
+    A[:, 256:] = 0
+    base = oracle.mgrouped_fp8(A, sa, W, sw, offsets=off)
+    sw2 = sw.copy()
+    sw2[0, 1, 2] += 1
+    got = oracle.mgrouped_fp8(A, sa, W, sw2, offsets=off)
+    assert np.array_equal(got[:4, 2], 2 * base[:4, 2])
+    keep = np.ones_like(got, dtype=bool)
+    keep[:4, 2] = False
+    assert np.array_equal(got[keep], base[keep])
+    # and a scale of A's row 5 in block 1 doubles that row (group 1) only
+    sa2 = sa.copy()
+    sa2[1, 5] += 1
+    got2 = oracle.mgrouped_fp8(A, sa2, W, sw, offsets=off)
+    assert np.array_equal(got2[5], 2 * base[5]) and np.array_equal(np.delete(got2, 5, 0), np.delete(base, 5, 0))
+
+
+def test_mgrouped_fp8_m_indices_match_offsets(oracle_lib):
+    counts = [2, 0, 3]
+    A, sa, W, sw, off, M = _fp8_mgrouped_case(counts, 128, 4, seed=44, pad_rows=1)
+    idx = np.concatenate([np.repeat(np.arange(3), counts), [-1]]).astype(np.int32)
+    a = oracle.mgrouped_fp8(A, sa, W, sw, offsets=off)
+    b = oracle.mgrouped_fp8(A, sa, W, sw, m_indices=idx)
+    assert np.array_equal(a[:5], b[:5]) and np.all(np.isnan(a[5])) and np.all(np.isnan(b[5]))

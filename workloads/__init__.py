@@ -299,6 +299,8 @@ class MGroupedWorkload:
     W: torch.Tensor = None         # bf16, see layout
     offsets: torch.Tensor = None   # int32 (E,), inclusive cumulative row counts
     m_indices: torch.Tensor = None  # int32 (M,), group id per row (-1 for pad rows)
+    sa: Optional[torch.Tensor] = None   # fp8: UE8M0 (K/128, M) scales of A
+    sw: Optional[torch.Tensor] = None   # fp8: UE8M0 (E, K/128, N) scales of W
 
     @property
     def M(self) -> int:
@@ -327,6 +329,29 @@ def make_mgrouped(counts: List[int], K: int, N: int, layout: str, seed: int, dev
     return MGroupedWorkload(counts=list(map(int, counts)), K=K, N=N, layout=layout, A=A, W=W,
                             offsets=torch.from_numpy(offsets_from_counts(counts)).to(device),
                             m_indices=torch.from_numpy(idx).to(device))
+
+
+def make_mgrouped_fp8(counts: List[int], K: int, N: int, seed: int, device="cpu", pad_rows: int = 0,
+                      integer_range: Optional[int] = None) -> MGroupedWorkload:
+    """fp8 operands of the m-grouped forward ("nt") product: the bf16 draws of make_mgrouped
+    quantised to e4m3fn with one UE8M0 scale per 1x128 block along K (llm-infra-atlas section 3),
+    scales mn-major: A -> (codes (M, K), sa (K/128, M)), W -> (codes (E, N, K), sw (E, K/128, N)).
+    With `integer_range` the values are small integers stored exactly with unit scales."""
+    wl = make_mgrouped(counts, K, N, "nt", seed, device, pad_rows=pad_rows, integer_range=integer_range)
+    E = len(counts)
+    if integer_range is None:
+        qa, sa = quantize_token_blocks(wl.A, token_axis=1)
+        qs = [quantize_token_blocks(wl.W[e], token_axis=1) for e in range(E)]
+        qw = torch.stack([q for q, _ in qs]) if E else torch.empty((0, N, K), dtype=torch.uint8, device=device)
+        sw = torch.stack([s for _, s in qs]) if E else torch.empty((0, K // 128, N), dtype=torch.uint8, device=device)
+    else:
+        qa = wl.A.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+        qw = wl.W.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+        sa = torch.full((K // 128, qa.shape[0]), E8M0_BIAS, dtype=torch.uint8, device=device)
+        sw = torch.full((E, K // 128, N), E8M0_BIAS, dtype=torch.uint8, device=device)
+    wl.A, wl.W = qa, qw.contiguous()
+    wl.sa, wl.sw = sa.contiguous(), sw.contiguous()
+    return wl
 
 
 # ----------------------------------------------------------------------------
