@@ -27,7 +27,8 @@ import torch
 __all__ = [
     "kgw_wgrad_bf16", "kgw_wgrad_bf16_noalloc", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native", "kgw_wgrad_fp8_ex",
     "kgw_wgrad_fp4", "FP4_TOKEN_ALIGN",
-    "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_workspace_bytes", "KGW_LAYOUT_NT",
+    "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16", "kgw_mgrouped_fp8", "kgw_workspace_bytes",
+    "KGW_LAYOUT_NT",
     "KGW_LAYOUT_NN",
     "KGW_A_M_MAJOR", "KGW_B_K_MAJOR", "KGW_RAGGED",
     "kgw_validate_offsets", "kgw_check_offsets", "kgw_mfma_ceiling",
@@ -66,7 +67,7 @@ _lib = None
 # Every symbol include/kgw.h declares.
 EXPORTED_SYMBOLS = ("kgw_wgrad_bf16", "kgw_wgrad_bf16_noalloc", "kgw_wgrad_bf16_ex", "kgw_wgrad_fp8", "kgw_wgrad_fp8_native",
                     "kgw_wgrad_fp8_ex", "kgw_wgrad_fp4", "kgw_quantize_fp8", "kgw_quantize_fp4", "kgw_mgrouped_bf16",
-                    "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_check_offsets",
+                    "kgw_mgrouped_fp8", "kgw_workspace_bytes", "kgw_validate_offsets_host", "kgw_validate_offsets", "kgw_check_offsets",
                     "kgw_mfma_ceiling", "kgw_status_string", "kgw_device_info")
 
 
@@ -91,11 +92,13 @@ def load_library():
     lib.kgw_wgrad_bf16_ex.restype = ctypes.c_int
     lib.kgw_wgrad_bf16_ex.argtypes = [p, p, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp8_ex.restype = ctypes.c_int
-    lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
+    lib.kgw_wgrad_fp8_ex.argtypes = [p, p, p, p, i32, i32, i32, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_wgrad_fp4.restype = ctypes.c_int
     lib.kgw_wgrad_fp4.argtypes = [p, p, p, p, p, i32, i64, i64, i64, p, p, i32, i32, p, sz, p]
     lib.kgw_mgrouped_bf16.restype = ctypes.c_int
     lib.kgw_mgrouped_bf16.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
+    lib.kgw_mgrouped_fp8.restype = ctypes.c_int
+    lib.kgw_mgrouped_fp8.argtypes = [p, p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
     lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, i32, p, p, p]
     lib.kgw_quantize_fp4.restype = ctypes.c_int
@@ -355,13 +358,18 @@ def kgw_wgrad_fp8_native(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sf
 
 def kgw_wgrad_fp8_ex(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor,
                      offsets: torch.Tensor, *, scale_format: int = KGW_SCALES_U8, native: bool = False,
-                     out: Optional[torch.Tensor] = None, outs=None, out_dtype: torch.dtype = torch.bfloat16,
-                     accumulate: bool = False, validate: bool = False, stream=None, split_k: bool = True):
+                     b_major: str = "n", out: Optional[torch.Tensor] = None, outs=None,
+                     out_dtype: torch.dtype = torch.bfloat16, accumulate: bool = False, validate: bool = False,
+                     stream=None, split_k: bool = True):
     """fp8 product with a scale layout (KGW_SCALES_*: uint8 per 128 tokens, packed int32 words of
     four 128-token blocks, or packed words of four 32-token blocks) and a dense `out` or discrete
-    `outs` (see kgw_wgrad_bf16_ex); native=True uses the scaled fp8 MFMA."""
+    `outs` (see kgw_wgrad_bf16_ex); native=True uses the scaled fp8 MFMA.  b_major "n": B is
+    (T, n) (the default); "k": B is stored (n, T), token-contiguous like A (exact path, uint8
+    scales only; the scales keep their (T/128, n) shape)."""
+    if b_major not in ("n", "k"):
+        raise ValueError("b_major is 'n' or 'k'")
     return _fp8_call("kgw_wgrad_fp8_ex", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream,
-                     split_k, scale_format=scale_format, native=native, outs=outs)
+                     split_k, scale_format=scale_format, native=native, outs=outs, b_k_major=b_major == "k")
 
 
 def kgw_wgrad_fp4(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
@@ -411,16 +419,17 @@ def scale_shape(tokens: int, mn: int, scale_format: int) -> Tuple[Tuple[int, int
 
 
 def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream, split_k,
-              scale_format=KGW_SCALES_U8, native=None, outs=None):
+              scale_format=KGW_SCALES_U8, native=None, outs=None, b_k_major=False):
     fp8_types = (torch.uint8, torch.float8_e4m3fn)
     if A.dtype not in fp8_types or B.dtype not in fp8_types:
         raise ValueError(f"{name} takes e4m3fn (or raw uint8) A and B")
     if sfa is None or sfb is None:
         raise ValueError(f"{name} needs both scale tensors sfa and sfb")
-    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
-        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1 if b_k_major else 0]:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}"
+                         f"{' (stored (n, T))' if b_k_major else ''}")
     hidden, T = A.shape
-    n = B.shape[1]
+    n = B.shape[0] if b_k_major else B.shape[1]
     (sa_shape, sdtype), (sb_shape, _) = scale_shape(T, hidden, scale_format), scale_shape(T, n, scale_format)
     if sfa.dtype != sdtype or sfb.dtype != sdtype:
         raise ValueError(f"this scale format takes {sdtype} scale tensors")
@@ -443,9 +452,9 @@ def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validat
         st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(offsets), E, hidden, n, T, _ptr(out), code,
                 int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     else:
-        st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), int(scale_format), int(bool(native)), _ptr(offsets), E,
-                hidden, n, T, _ptr(out), _ptr(ptrs), code, int(bool(accumulate)), _ptr(ws), ws_bytes,
-                _stream_ptr(stream))
+        st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), int(scale_format), int(bool(native)),
+                KGW_B_K_MAJOR if b_k_major else 0, _ptr(offsets), E, hidden, n, T, _ptr(out), _ptr(ptrs), code,
+                int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, name)
     return out if outs is None else outs
 
@@ -550,6 +559,59 @@ def kgw_mgrouped_bf16(A: torch.Tensor, W: torch.Tensor, *, offsets: Optional[tor
                                           _ptr(offsets), _ptr(m_indices), E, M, K, N, _ptr(out), code,
                                           int(bool(accumulate)), _stream_ptr(stream))
     _check(st, "kgw_mgrouped_bf16")
+    return out
+
+
+def kgw_mgrouped_fp8(A: torch.Tensor, sa: torch.Tensor, W: torch.Tensor, sw: torch.Tensor, *,
+                     offsets: Optional[torch.Tensor] = None, m_indices: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                     accumulate: bool = False, stream=None) -> torch.Tensor:
+    """m-grouped forward product with fp8 operands: out[r] = a(r) @ w(g(r))^T, where A is e4m3
+    (M, K) with UE8M0 sa (K/128, M) and W is e4m3 (E, N, K) with UE8M0 sw (E, K/128, N), one
+    scale per 1x128 block along K; groups from `offsets` or `m_indices` as for
+    kgw_mgrouped_bf16; rows of no group are left untouched."""
+    fp8_types = (torch.uint8, torch.float8_e4m3fn)
+    if A.dtype not in fp8_types or W.dtype not in fp8_types:
+        raise ValueError("kgw_mgrouped_fp8 takes e4m3fn (or raw uint8) A and W")
+    if sa is None or sw is None or sa.dtype != torch.uint8 or sw.dtype != torch.uint8:
+        raise ValueError("kgw_mgrouped_fp8 needs uint8 scale tensors sa and sw")
+    if A.dim() != 2 or W.dim() != 3:
+        raise ValueError("A must be (M, K) and W (E, N, K)")
+    for t in (A, W, sa, sw):
+        if not t.is_contiguous():
+            raise ValueError("fp8 operands and scales must be contiguous")
+    M, K = A.shape
+    E, N = W.shape[0], W.shape[1]
+    if W.shape[2] != K:
+        raise ValueError(f"W {tuple(W.shape)} does not match A's K = {K}")
+    if K % FP8_TOKEN_ALIGN != 0:
+        raise ValueError(f"K ({K}) must be a multiple of {FP8_TOKEN_ALIGN}")
+    if tuple(sa.shape) != (K // FP8_TOKEN_ALIGN, M) or tuple(sw.shape) != (E, K // FP8_TOKEN_ALIGN, N):
+        raise ValueError(f"scale shapes must be {(K // FP8_TOKEN_ALIGN, M)} and {(E, K // FP8_TOKEN_ALIGN, N)}")
+    device = A.device
+    if any(t.device != device for t in (W, sa, sw)):
+        raise ValueError("operands and scales must be on the same device")
+    if (offsets is None) == (m_indices is None):
+        raise ValueError("pass exactly one of offsets and m_indices")
+    idx = offsets if offsets is not None else m_indices
+    if idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous() or idx.device != device:
+        raise ValueError("offsets / m_indices must be a contiguous 1-D int32 tensor on the operands' device")
+    if offsets is not None and offsets.numel() != E:
+        raise ValueError(f"offsets must have one entry per group ({E})")
+    if m_indices is not None and m_indices.numel() != M:
+        raise ValueError(f"m_indices must have one entry per row ({M})")
+    if out is not None:
+        out_dtype = out.dtype
+    code = _out_code(out_dtype)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an initialised `out`")
+        out = torch.empty((M, N), dtype=out_dtype, device=device)
+    elif tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != device:
+        raise ValueError(f"out must be a contiguous {(M, N)} tensor on the operands' device")
+    st = load_library().kgw_mgrouped_fp8(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(offsets), _ptr(m_indices), E,
+                                         M, K, N, _ptr(out), code, int(bool(accumulate)), _stream_ptr(stream))
+    _check(st, "kgw_mgrouped_fp8")
     return out
 
 

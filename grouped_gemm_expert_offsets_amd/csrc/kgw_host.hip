@@ -177,6 +177,9 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     if ((layout & KGW_RAGGED) && (layout & (KGW_A_M_MAJOR | KGW_B_K_MAJOR)) != KGW_B_K_MAJOR)
         return KGW_ERROR_INVALID_VALUE;      // ragged blocks are K-contiguous for both operands
     if ((layout & KGW_A_M_MAJOR) && hidden % 8 != 0) return KGW_ERROR_MISALIGNED;
+    // fp8 / fp4: the default layout, or (exact fp8, one byte per 128 tokens) B K-major
+    if (fp8 && layout != 0 && (layout != KGW_B_K_MAJOR || kernel != Kernel::kFp8 || scale_format != KGW_SCALES_U8))
+        return KGW_ERROR_UNSUPPORTED;
     if (hidden == 0 || n == 0) return KGW_SUCCESS;                 // no output elements
     if (accumulate && tokens_sum == 0) return KGW_SUCCESS;         // adds nothing
 
@@ -256,7 +259,10 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
                                                          (hipStream_t)stream)
                          : kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream);
             break;
-        case Kernel::kFp8: err = kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream); break;
+        case Kernel::kFp8:
+            err = layout ? kgw::launch_wgrad_fp8_bk(p, out_kind, grid, (hipStream_t)stream)
+                         : kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream);
+            break;
         case Kernel::kFp4: err = kgw::launch_wgrad_fp4(p, out_kind, grid, (hipStream_t)stream); break;
         default: err = kgw::launch_wgrad_fp8_native(p, out_kind, grid, (hipStream_t)stream); break;
     }
@@ -322,12 +328,14 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
 }
 
 kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, const void* sfb, int32_t scale_format,
-                              int32_t native, const int32_t* offsets, int32_t num_experts, int64_t hidden,
-                              int64_t n, int64_t tokens_sum, void* out, void* const* out_ptrs, int32_t out_dtype,
-                              int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+                              int32_t native, int32_t layout, const int32_t* offsets, int32_t num_experts,
+                              int64_t hidden, int64_t n, int64_t tokens_sum, void* out, void* const* out_ptrs,
+                              int32_t out_dtype, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     if (native != 0 && native != 1) return KGW_ERROR_INVALID_VALUE;
     return run(native ? Kernel::kFp8Native : Kernel::kFp8, A, sfa, B, sfb, scale_format, offsets, num_experts,
-               hidden, n, tokens_sum, out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream);
+               hidden, n, tokens_sum, out, out_ptrs, out_dtype, accumulate, workspace, workspace_bytes, stream,
+               layout);
 }
 
 kgw_status_t kgw_wgrad_fp4(const void* A, const void* sfa, const void* B, const void* sfb, const int32_t* offsets,
@@ -407,6 +415,8 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
     kgw::MGroupedParams p;
     p.A = A;
     p.W = W;
+    p.sa = nullptr;
+    p.sw = nullptr;
     p.offsets = offsets;
     p.m_indices = m_indices;
     p.out = out;
@@ -423,6 +433,50 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
     p.num_xcds = d.num_xcds;
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
     const hipError_t err = kgw::launch_mgrouped_bf16(p, layout == KGW_LAYOUT_NT, out_dtype, grid, (hipStream_t)stream);
+    return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
+}
+
+kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, const uint8_t* sw,
+                              const int32_t* offsets, const int32_t* m_indices, int32_t num_groups, int64_t m,
+                              int64_t k, int64_t n, void* out, int32_t out_dtype, int32_t accumulate, void* stream) {
+    if (num_groups < 1 || m < 0 || k < 0 || n < 0) return KGW_ERROR_INVALID_VALUE;
+    if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16 && out_dtype != KGW_OUT_FP16)
+        return KGW_ERROR_INVALID_VALUE;
+    if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
+    if ((offsets != nullptr) == (m_indices != nullptr)) return KGW_ERROR_INVALID_VALUE;
+    if (num_groups > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
+    if (m > INT32_MAX || k >= ((int64_t)1 << 22) || n >= ((int64_t)1 << 24)) return KGW_ERROR_UNSUPPORTED;
+    if (k % 128 != 0 || n % 8 != 0) return KGW_ERROR_MISALIGNED;
+    if (m == 0 || n == 0) return KGW_SUCCESS;
+    if (!out || (k > 0 && (!A || !W || !sa || !sw))) return KGW_ERROR_INVALID_VALUE;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (((uintptr_t)offsets | (uintptr_t)m_indices) & 3u))
+        return KGW_ERROR_MISALIGNED;
+    if (accumulate && k == 0) return KGW_SUCCESS;
+    DeviceProps d;
+    kgw_status_t st = current_props(&d);
+    if (st != KGW_SUCCESS) return st;
+    if (!d.is_gfx950) return KGW_ERROR_DEVICE;
+    kgw::MGroupedParams p;
+    p.A = A;
+    p.W = W;
+    p.sa = sa;
+    p.sw = sw;
+    p.offsets = offsets;
+    p.m_indices = m_indices;
+    p.out = out;
+    p.out_ptrs = nullptr;
+    p.hidden = m;
+    p.n = n;
+    p.k = k;
+    p.num_groups = num_groups;
+    p.tiles_m = (int32_t)((m + 255) / 256);
+    p.tiles_n = (int32_t)((n + 255) / 256);
+    if ((int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    p.num_items = p.tiles_m * p.tiles_n;
+    p.accumulate = accumulate;
+    p.num_xcds = d.num_xcds;
+    const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
+    const hipError_t err = kgw::launch_mgrouped_fp8(p, out_dtype, grid, (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 

@@ -77,7 +77,9 @@ struct MGroupedParams {
     void* const* out_ptrs;  // always NULL (one output matrix)
     int64_t hidden;         // M
     int64_t n;              // N
-    int64_t k;              // K, a multiple of 64
+    int64_t k;              // K, a multiple of 64 (fp8: of 128)
+    const uint8_t* sa;      // fp8 only: UE8M0 scales of A, (K/128, M) bytes
+    const uint8_t* sw;      // fp8 only: UE8M0 scales of W, (E, K/128, N) bytes
     int32_t num_groups;
     int32_t tiles_m;
     int32_t tiles_n;
@@ -85,6 +87,20 @@ struct MGroupedParams {
     int32_t accumulate;
     int32_t num_xcds;
 };
+
+// Group of A row `row` (any value outside [0, num_groups) is no group): the row's
+// m_indices entry, else the first group whose inclusive offset exceeds the row
+// (num_groups past the last offset).  Uniform across a workgroup.
+__device__ __forceinline__ int group_of_row(const MGroupedParams& p, int64_t row) {
+    if (p.m_indices) return p.m_indices[row];
+    int lo = 0, hi = p.num_groups;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)p.offsets[mid] > row) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
 
 // Split-K chunks start on multiples of this many tokens (a multiple of both
 // token alignments, so no chunk splits a 128-token fp8 scale block).
@@ -119,5 +135,9 @@ hipError_t launch_check_offsets(const int32_t* offsets, int32_t num_experts, int
 hipError_t launch_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters, int32_t workgroups,
                                uint64_t* cycles, hipStream_t stream);
 hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
+// Exact fp8 (U8 scales) with B stored K-major, (n, tokens_sum): both operands token-contiguous.
+hipError_t launch_wgrad_fp8_bk(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// m-grouped forward product with fp8 operands and 1x128 UE8M0 scales (nt layout).
+hipError_t launch_mgrouped_fp8(const MGroupedParams& p, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

@@ -56,19 +56,6 @@ struct BRing {
 };
 static_assert(B_RING + 4 * BK * BN * 2 <= 160 * 1024 && B_RING + 2 * A_STAGE <= 160 * 1024, "LDS budget");
 
-// Group of row `row`: the per-row id, or the first e with offsets[e] > row
-// (num_groups: past the last offset).  Uniform across the workgroup.
-__device__ __forceinline__ int group_of_row(const MGroupedParams& p, int64_t row) {
-    if (p.m_indices) return p.m_indices[row];
-    int lo = 0, hi = p.num_groups;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((int64_t)p.offsets[mid] > row) hi = mid;
-        else lo = mid + 1;
-    }
-    return lo;
-}
-
 template <int OUT, bool BT>
 __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) {
     constexpr int NB = BRing<BT>::slots;

@@ -255,13 +255,20 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
  * MFMA), 1 as kgw_wgrad_fp8_native (the scaled fp8 MFMA, whose hardware scale
  * blocks are exactly 32 tokens: each lane hands the instruction the byte of
  * its half of the 64-token step).  out / out_ptrs as for kgw_wgrad_bf16_ex.
+ * layout is 0 (A (hidden, tokens_sum), B (tokens_sum, n), as for kgw_wgrad_fp8)
+ * or KGW_B_K_MAJOR: B stored (n, tokens_sum), token axis contiguous, element
+ * (t, j) at B[j * tokens_sum + t] -- both operands token-contiguous, the pair
+ * a (M, K), b (N, K) of the DeepGEMM k-grouped page; the scales keep their
+ * (tokens_sum/128, n) layout.  KGW_B_K_MAJOR is taken with native 0 and
+ * KGW_SCALES_U8 only; other layouts or combinations are KGW_ERROR_UNSUPPORTED
+ * (bits outside the KGW_* layout flags: KGW_ERROR_INVALID_VALUE).
  * Counts stay multiples of 128 for every format.  Everything else as for
  * kgw_wgrad_fp8; an unknown scale_format or native value is
  * KGW_ERROR_INVALID_VALUE, a misaligned KGW_SCALES_PACKED_32 pointer
  * KGW_ERROR_MISALIGNED.
  */
 kgw_status_t kgw_wgrad_fp8_ex(const void* A, const void* sfa, const void* B, const void* sfb,
-                              int32_t scale_format, int32_t native, const int32_t* offsets,
+                              int32_t scale_format, int32_t native, int32_t layout, const int32_t* offsets,
                               int32_t num_experts, int64_t hidden, int64_t n, int64_t tokens_sum,
                               void* out, void* const* out_ptrs, int32_t out_dtype, int32_t accumulate,
                               void* workspace, size_t workspace_bytes, void* stream);
@@ -399,6 +406,42 @@ typedef enum {
 kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, const int32_t* offsets,
                                const int32_t* m_indices, int32_t num_groups, int64_t m, int64_t k, int64_t n,
                                void* out, int32_t out_dtype, int32_t accumulate, void* stream);
+
+/*
+ * kgw_mgrouped_fp8 -- the m-grouped forward product with fp8 operands
+ * (llm-infra-atlas "05 Grouped GEMM": section 2.1, m_grouped_fp8_gemm_nt_contiguous,
+ * the contiguous layout; section 3, every fp8 input carries one power-of-two
+ * (UE8M0) scale per 1x128 block along K, the scale tensor mn-major).  Row r of A
+ * belongs to group g(r) and
+ *
+ *     out[r, j] = sum_k  a(r, k) * w(g(r), j, k),
+ *     a(r, k)    = e4m3(A[r, k])      * 2^(sa[k/128, r] - 127),
+ *     w(g, j, k) = e4m3(W[g, j, k])   * 2^(sw[g, k/128, j] - 127),
+ *
+ * computed as kgw_wgrad_fp8 does: each operand fragment converted exactly to bf16
+ * with its scale folded in, products summed in fp32 on the bf16 MFMA, the output
+ * rounded once to out_dtype.
+ *
+ *   A          e4m3 bytes (m, k), row-major (k contiguous), device, 16-byte aligned.
+ *   sa         uint8 (k/128, m): sa[b][r] is the biased exponent of the scale of
+ *              A[r, 128b : 128b+128].
+ *   W          e4m3 bytes (num_groups, n, k) (the "nt" layout: out = A @ W[g]^T),
+ *              device, 16-byte aligned.
+ *   sw         uint8 (num_groups, k/128, n): scale exponent of W[g, j, 128b : 128b+128].
+ *   offsets / m_indices, out, out_dtype, accumulate, stream  as for kgw_mgrouped_bf16,
+ *              with the same 128-row group contract (not checked on the host).
+ *   A scale byte of 0xFF encodes NaN and, like a NaN operand, makes the affected
+ *   outputs NaN.
+ *
+ * Sizes: 1 <= num_groups <= 65536, 0 <= m < 2^31, 0 <= k < 2^22 and a multiple of
+ * 128, 0 <= n < 2^24 and a multiple of 8 (KGW_ERROR_MISALIGNED otherwise).
+ * m == 0 or n == 0 does nothing; k == 0 writes zeros (overwrite) into the rows
+ * of a group.  Errors as for kgw_wgrad_bf16.
+ */
+kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, const uint8_t* sw,
+                              const int32_t* offsets, const int32_t* m_indices, int32_t num_groups,
+                              int64_t m, int64_t k, int64_t n, void* out, int32_t out_dtype,
+                              int32_t accumulate, void* stream);
 
 /*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape

@@ -173,8 +173,9 @@ def call_bf16_ex(lib, out=FAKE, ptrs=None, H=256, N=512, E=4, T=1024, layout=0):
     return lib.kgw_wgrad_bf16_ex(FAKE, FAKE, layout, FAKE, E, H, N, T, out, ptrs, 0, 0, None, 0, None)
 
 
-def call_fp8_ex(lib, sa=FAKE, sb=FAKE, fmt=0, native=0, out=FAKE, ptrs=None, H=256, N=512, T=1024):
-    return lib.kgw_wgrad_fp8_ex(FAKE, sa, FAKE, sb, fmt, native, FAKE, 4, H, N, T, out, ptrs, 1, 0, None, 0, None)
+def call_fp8_ex(lib, sa=FAKE, sb=FAKE, fmt=0, native=0, out=FAKE, ptrs=None, H=256, N=512, T=1024, layout=0):
+    return lib.kgw_wgrad_fp8_ex(FAKE, sa, FAKE, sb, fmt, native, layout, FAKE, 4, H, N, T, out, ptrs, 1, 0, None, 0,
+                                None)
 
 
 def test_extended_entry_point_errors(lib):
@@ -196,6 +197,14 @@ def test_extended_entry_point_errors(lib):
     assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED_32, sa=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED
     assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED, sa=FAKE + 2, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
     assert call_fp8_ex(lib, out=FAKE, ptrs=FAKE) == kgw.KGW_ERROR_INVALID_VALUE
+    # fp8 layouts: B K-major on the exact path with uint8 scales only
+    assert call_fp8_ex(lib, layout=8) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, layout=kgw.KGW_A_M_MAJOR) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, native=1) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, fmt=kgw.KGW_SCALES_PACKED) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | kgw.KGW_B_K_MAJOR) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, H=0) == kgw.KGW_SUCCESS     # nothing to write
+    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, N=520) == kgw.KGW_ERROR_MISALIGNED
 
 
 def test_quantizer_argument_errors(lib):
@@ -252,6 +261,55 @@ def test_mgrouped_argument_errors(lib):
     assert call_mg(lib, out=None) == kgw.KGW_ERROR_INVALID_VALUE
     assert call_mg(lib, M=0, out=None, A=None) == kgw.KGW_SUCCESS              # nothing to do
     assert call_mg(lib, K=0, acc=1, A=None, W=None) == kgw.KGW_SUCCESS          # adds nothing
+
+
+def call_mg8(lib, A=FAKE, sa=FAKE, W=FAKE, sw=FAKE, off=FAKE, idx=None, E=4, M=1024, K=256, N=512, out=FAKE, dt=1,
+             acc=0):
+    return lib.kgw_mgrouped_fp8(A, sa, W, sw, off, idx, E, M, K, N, out, dt, acc, None)
+
+
+def test_mgrouped_fp8_argument_errors(lib):
+    assert call_mg8(lib, E=0) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, off=None, idx=None) == kgw.KGW_ERROR_INVALID_VALUE    # no grouping
+    assert call_mg8(lib, off=FAKE, idx=FAKE) == kgw.KGW_ERROR_INVALID_VALUE    # both
+    assert call_mg8(lib, dt=5) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, acc=3) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, sa=None) == kgw.KGW_ERROR_INVALID_VALUE               # scales required
+    assert call_mg8(lib, sw=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, K=192) == kgw.KGW_ERROR_MISALIGNED                    # K % 128 (one scale block)
+    assert call_mg8(lib, N=500) == kgw.KGW_ERROR_MISALIGNED                    # N % 8
+    assert call_mg8(lib, W=FAKE + 8) == kgw.KGW_ERROR_MISALIGNED
+    assert call_mg8(lib, sa=FAKE + 1) != kgw.KGW_ERROR_MISALIGNED              # scale bytes: any address
+    assert call_mg8(lib, idx=FAKE + 2, off=None) == kgw.KGW_ERROR_MISALIGNED
+    assert call_mg8(lib, K=1 << 22) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_mg8(lib, E=65537) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_mg8(lib, out=None) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, M=0, out=None, A=None) == kgw.KGW_SUCCESS             # nothing to do
+    assert call_mg8(lib, K=0, acc=1, A=None, W=None, sa=None, sw=None) == kgw.KGW_SUCCESS   # adds nothing
+
+
+def test_mgrouped_fp8_binding_rejects_bad_tensors():
+    import torch
+    A = torch.zeros(256, 256, dtype=torch.uint8)
+    W = torch.zeros(2, 32, 256, dtype=torch.uint8)
+    sa = torch.zeros(2, 256, dtype=torch.uint8)
+    sw = torch.zeros(2, 2, 32, dtype=torch.uint8)
+    off = torch.tensor([128, 256], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa, W, sw)                                      # no grouping
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa.t().contiguous(), W, sw, offsets=off)        # scales must be (K/128, M)
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa, W, sw[:, :, :16].contiguous(), offsets=off)
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A[:, :192].contiguous(), sa[:1].contiguous(), W[:, :, :192].contiguous(),
+                             sw[:, :1].contiguous(), offsets=off)               # K % 128
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A.to(torch.bfloat16), sa, W, sw, offsets=off)      # not fp8
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa, W, sw, offsets=off[:1])
+    with pytest.raises(ValueError):
+        kgw.kgw_wgrad_fp8_ex(A, sa, W[0], sw[0], off, b_major="m")
 
 
 def test_mgrouped_binding_rejects_bad_tensors():
