@@ -101,8 +101,13 @@ def algorithmic_bytes(wl) -> float:
     return float(b)
 
 
-def make_call(wl, out, native=False):
+def make_call(wl, out, native=False, b_k_major=False):
     import grouped_gemm_expert_offsets_amd as kgw
+    if b_k_major:
+        # B stored (n, tokens_sum): both fp8 operands token-contiguous (exact path, byte scales)
+        bt = wl.B.t().contiguous()
+        return lambda: kgw.kgw_wgrad_fp8_ex(wl.A, wl.sfa, bt, wl.sfb, wl.offsets, b_major="k", out=out,
+                                            accumulate=wl.accumulate)
     if wl.kind == "bf16":
         return lambda: kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=wl.accumulate)
     if wl.scale_block == 32:
@@ -179,7 +184,7 @@ def run_flushed(name: str, steps: int, warmup: int):
 
 
 def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1, min_warm_s: float = 0.0,
-                 scale_block: int = 128):
+                 scale_block: int = 128, b_k_major: bool = False):
     import torch
     import workloads
     if scale_block == 128:
@@ -191,11 +196,12 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
     out = wl.C0 if wl.accumulate else torch.empty((wl.num_experts, wl.hidden, wl.n), dtype=wl.out_dtype,
                                                   device="cuda")
     warm = {}
-    ms_step, launch_ms = time_call(make_call(wl, out, native), steps, warmup, min_warm_s, warm)
+    ms_step, launch_ms = time_call(make_call(wl, out, native, b_k_major), steps, warmup, min_warm_s, warm)
     launch_ms.sort()
     mean_launch = sum(launch_ms) / len(launch_ms)
     res = {
-        "workload": name + ("_mx32" if scale_block == 32 else "") + ("_native" if native else ""),
+        "workload": (name + ("_mx32" if scale_block == 32 else "") + ("_native" if native else "") +
+                     ("_b_k_major" if b_k_major else "")),
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "launch_ms_median": launch_ms[len(launch_ms) // 2],
@@ -273,6 +279,34 @@ def run_mgrouped(layout: str, steps: int, warmup: int, min_warm_s: float = 0.0):
         "flops_per_launch": wl.flops,
     }
     res["frac_of_mfma_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
+    del wl, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_mgrouped_fp8(steps: int, warmup: int, min_warm_s: float = 0.0):
+    """kgw_mgrouped_fp8 on the fp8 workload's layer forward: X (T, 7168) @ W^T, W (32, 4096, 7168),
+    32 groups of roundup128(8192*U(0.7,1.3)) rows, e4m3 operands with 1x128 UE8M0 scales along K
+    (block-quantised Gaussian draws), bf16 output."""
+    import torch
+    import grouped_gemm_expert_offsets_amd as kgw
+    import workloads
+    counts = workloads.counts_uniform(32, 8192, 128, 1)
+    K, N = 7168, 4096
+    wl = workloads.make_mgrouped_fp8(counts, K, N, seed=1, device="cuda")
+    out = torch.empty((wl.M, N), dtype=torch.bfloat16, device="cuda")
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_mgrouped_fp8(wl.A, wl.sa, wl.W, wl.sw, offsets=wl.offsets,
+                                                                out=out), steps, warmup, min_warm_s)
+    mean_launch = sum(launch_ms) / len(launch_ms)
+    res = {
+        "workload": f"mgrouped_fp8_nt forward M={wl.M} K={K} N={N} E=32 e4m3 1x128 UE8M0, bf16 out",
+        "ms_per_step": ms_step,
+        "launch_ms_mean": mean_launch,
+        "tflops": wl.flops / (mean_launch * 1e-3) / 1e12,
+        "flops_per_launch": wl.flops,
+    }
+    res["frac_of_mfma_peak"] = res["tflops"] / PEAK_FP8_TFLOPS
+    res["frac_of_bf16_mfma_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
     del wl, out
     torch.cuda.empty_cache()
     return res
@@ -523,10 +557,12 @@ def main():
             steps = sec_steps * 10 if name in ("balanced", "tiny") else sec_steps
             add(run_workload(name, steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
                              scale_block=block))
+        add(run_workload("fp8", sec_steps, sec_warm, min_warm_s=args.secondary_warm_seconds, b_k_major=True))
         add(run_flushed("balanced", 30, 50))
         add(run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds))
         for layout in ("nt", "nn"):
             add(run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds))
+        add(run_mgrouped_fp8(sec_steps, sec_warm, args.secondary_warm_seconds))
         for fp4 in (False, True):
             for axis in (1, 0):
                 add(run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4))
