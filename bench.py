@@ -101,13 +101,15 @@ def algorithmic_bytes(wl) -> float:
     return float(b)
 
 
-def make_call(wl, out, native=False, b_k_major=False):
+def make_call(wl, out, native=False, layout=("k", "n")):
     import grouped_gemm_expert_offsets_amd as kgw
-    if b_k_major:
-        # B stored (n, tokens_sum): both fp8 operands token-contiguous (exact path, byte scales)
-        bt = wl.B.t().contiguous()
-        return lambda: kgw.kgw_wgrad_fp8_ex(wl.A, wl.sfa, bt, wl.sfb, wl.offsets, b_major="k", out=out,
-                                            accumulate=wl.accumulate)
+    if layout != ("k", "n"):
+        # fp8 operands stored in another layout (exact path, byte scales): A (T, hidden) for
+        # a_major "m", B (n, T) for b_major "k"
+        a = wl.A.t().contiguous() if layout[0] == "m" else wl.A
+        b = wl.B.t().contiguous() if layout[1] == "k" else wl.B
+        return lambda: kgw.kgw_wgrad_fp8_ex(a, wl.sfa, b, wl.sfb, wl.offsets, a_major=layout[0], b_major=layout[1],
+                                            out=out, accumulate=wl.accumulate)
     if wl.kind == "bf16":
         return lambda: kgw.kgw_wgrad_bf16(wl.A, wl.B, wl.offsets, out, accumulate=wl.accumulate)
     if wl.scale_block == 32:
@@ -184,7 +186,7 @@ def run_flushed(name: str, steps: int, warmup: int):
 
 
 def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1, min_warm_s: float = 0.0,
-                 scale_block: int = 128, b_k_major: bool = False):
+                 scale_block: int = 128, layout=("k", "n")):
     import torch
     import workloads
     if scale_block == 128:
@@ -196,12 +198,12 @@ def run_workload(name: str, steps: int, warmup: int, native=False, seed: int = 1
     out = wl.C0 if wl.accumulate else torch.empty((wl.num_experts, wl.hidden, wl.n), dtype=wl.out_dtype,
                                                   device="cuda")
     warm = {}
-    ms_step, launch_ms = time_call(make_call(wl, out, native, b_k_major), steps, warmup, min_warm_s, warm)
+    ms_step, launch_ms = time_call(make_call(wl, out, native, layout), steps, warmup, min_warm_s, warm)
     launch_ms.sort()
     mean_launch = sum(launch_ms) / len(launch_ms)
     res = {
         "workload": (name + ("_mx32" if scale_block == 32 else "") + ("_native" if native else "") +
-                     ("_b_k_major" if b_k_major else "")),
+                     ("" if layout == ("k", "n") else f"_a_{layout[0]}_major_b_{layout[1]}_major")),
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "launch_ms_median": launch_ms[len(launch_ms) // 2],
@@ -557,7 +559,8 @@ def main():
             steps = sec_steps * 10 if name in ("balanced", "tiny") else sec_steps
             add(run_workload(name, steps, sec_warm, native=native, min_warm_s=args.secondary_warm_seconds,
                              scale_block=block))
-        add(run_workload("fp8", sec_steps, sec_warm, min_warm_s=args.secondary_warm_seconds, b_k_major=True))
+        for layout in (("k", "k"), ("m", "n"), ("m", "k")):
+            add(run_workload("fp8", sec_steps, sec_warm, min_warm_s=args.secondary_warm_seconds, layout=layout))
         add(run_flushed("balanced", 30, 50))
         add(run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds))
         for layout in ("nt", "nn"):

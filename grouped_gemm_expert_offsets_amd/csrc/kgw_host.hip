@@ -177,9 +177,17 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     if ((layout & KGW_RAGGED) && (layout & (KGW_A_M_MAJOR | KGW_B_K_MAJOR)) != KGW_B_K_MAJOR)
         return KGW_ERROR_INVALID_VALUE;      // ragged blocks are K-contiguous for both operands
     if ((layout & KGW_A_M_MAJOR) && hidden % 8 != 0) return KGW_ERROR_MISALIGNED;
-    // fp8 / fp4: the default layout, or (exact fp8, one byte per 128 tokens) B K-major
-    if (fp8 && layout != 0 && (layout != KGW_B_K_MAJOR || kernel != Kernel::kFp8 || scale_format != KGW_SCALES_U8))
-        return KGW_ERROR_UNSUPPORTED;
+    // token rows of an M-major A are addressed with 32-bit offsets, as B's (check_common)
+    if ((layout & KGW_A_M_MAJOR) && 64 * hidden * 2 >= ((int64_t)1 << 31)) return KGW_ERROR_UNSUPPORTED;
+    // fp8 / fp4: the default layout, or (exact fp8, one byte per 128 tokens) A M-major and / or
+    // B K-major; A M-major rows of tokens move in 16-byte pieces (hidden % 16) with 32-bit
+    // offsets over 64 token rows
+    if (fp8 && layout != 0) {
+        if ((layout & KGW_RAGGED) || kernel != Kernel::kFp8 || scale_format != KGW_SCALES_U8)
+            return KGW_ERROR_UNSUPPORTED;
+        if ((layout & KGW_A_M_MAJOR) && hidden % 16 != 0) return KGW_ERROR_MISALIGNED;
+        if ((layout & KGW_A_M_MAJOR) && 64 * hidden >= ((int64_t)1 << 31)) return KGW_ERROR_UNSUPPORTED;
+    }
     if (hidden == 0 || n == 0) return KGW_SUCCESS;                 // no output elements
     if (accumulate && tokens_sum == 0) return KGW_SUCCESS;         // adds nothing
 
@@ -260,7 +268,9 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
                          : kgw::launch_wgrad_bf16(p, out_kind, grid, (hipStream_t)stream);
             break;
         case Kernel::kFp8:
-            err = layout ? kgw::launch_wgrad_fp8_bk(p, out_kind, grid, (hipStream_t)stream)
+            err = layout ? kgw::launch_wgrad_fp8_layout(p, (layout & KGW_A_M_MAJOR) != 0,
+                                                        (layout & KGW_B_K_MAJOR) != 0, out_kind, grid,
+                                                        (hipStream_t)stream)
                          : kgw::launch_wgrad_fp8(p, out_kind, grid, (hipStream_t)stream);
             break;
         case Kernel::kFp4: err = kgw::launch_wgrad_fp4(p, out_kind, grid, (hipStream_t)stream); break;

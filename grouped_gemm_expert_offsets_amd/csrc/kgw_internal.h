@@ -135,8 +135,10 @@ hipError_t launch_check_offsets(const int32_t* offsets, int32_t num_experts, int
 hipError_t launch_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters, int32_t workgroups,
                                uint64_t* cycles, hipStream_t stream);
 hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
-// Exact fp8 (U8 scales) with B stored K-major, (n, tokens_sum): both operands token-contiguous.
-hipError_t launch_wgrad_fp8_bk(const GroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// Exact fp8 (U8 scales) in the other operand layouts: A stored (tokens_sum, hidden) when
+// a_m_major, B stored (n, tokens_sum) when b_k_major (at least one of them).
+hipError_t launch_wgrad_fp8_layout(const GroupedParams& p, bool a_m_major, bool b_k_major, int out_kind, int grid,
+                                   hipStream_t stream);
 // m-grouped forward product with fp8 operands and 1x128 UE8M0 scales (nt layout).
 hipError_t launch_mgrouped_fp8(const MGroupedParams& p, int out_kind, int grid, hipStream_t stream);
 

@@ -197,14 +197,21 @@ def test_extended_entry_point_errors(lib):
     assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED_32, sa=FAKE + 2) == kgw.KGW_ERROR_MISALIGNED
     assert call_fp8_ex(lib, fmt=kgw.KGW_SCALES_PACKED, sa=FAKE + 2, T=1000) == kgw.KGW_ERROR_BAD_OFFSETS
     assert call_fp8_ex(lib, out=FAKE, ptrs=FAKE) == kgw.KGW_ERROR_INVALID_VALUE
-    # fp8 layouts: B K-major on the exact path with uint8 scales only
+    # fp8 layouts: A M-major and / or B K-major on the exact path with uint8 scales only
+    AM, BK = kgw.KGW_A_M_MAJOR, kgw.KGW_B_K_MAJOR
     assert call_fp8_ex(lib, layout=8) == kgw.KGW_ERROR_INVALID_VALUE
-    assert call_fp8_ex(lib, layout=kgw.KGW_A_M_MAJOR) == kgw.KGW_ERROR_UNSUPPORTED
-    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, native=1) == kgw.KGW_ERROR_UNSUPPORTED
-    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, fmt=kgw.KGW_SCALES_PACKED) == kgw.KGW_ERROR_UNSUPPORTED
-    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | kgw.KGW_B_K_MAJOR) == kgw.KGW_ERROR_UNSUPPORTED
-    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, H=0) == kgw.KGW_SUCCESS     # nothing to write
-    assert call_fp8_ex(lib, layout=kgw.KGW_B_K_MAJOR, N=520) == kgw.KGW_ERROR_MISALIGNED
+    for lay in (AM, BK, AM | BK):
+        assert call_fp8_ex(lib, layout=lay) == kgw.KGW_ERROR_DEVICE            # accepted, no GPU here
+        assert call_fp8_ex(lib, layout=lay, native=1) == kgw.KGW_ERROR_UNSUPPORTED
+        assert call_fp8_ex(lib, layout=lay, fmt=kgw.KGW_SCALES_PACKED) == kgw.KGW_ERROR_UNSUPPORTED
+        assert call_fp8_ex(lib, layout=lay, fmt=kgw.KGW_SCALES_PACKED_32) == kgw.KGW_ERROR_UNSUPPORTED
+        assert call_fp8_ex(lib, layout=lay, H=0) == kgw.KGW_SUCCESS           # nothing to write
+        assert call_fp8_ex(lib, layout=lay, N=520) == kgw.KGW_ERROR_MISALIGNED
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | BK) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=AM, H=264) == kgw.KGW_ERROR_MISALIGNED      # fp8 M-major rows: hidden % 16
+    assert call_fp8_ex(lib, layout=BK, H=264) == kgw.KGW_ERROR_DEVICE
+    assert call_fp8_ex(lib, layout=AM, H=1 << 25) == kgw.KGW_ERROR_UNSUPPORTED  # 32-bit row offsets
+    assert call_bf16_ex(lib, layout=AM, H=1 << 24) == kgw.KGW_ERROR_UNSUPPORTED
 
 
 def test_quantizer_argument_errors(lib):

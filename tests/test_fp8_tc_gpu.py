@@ -1,9 +1,9 @@
-"""GPU parity of the fp8 products whose operands both keep the contracted axis contiguous:
+"""GPU parity of the fp8 products in the operand layouts other than kgw_wgrad_fp8's default:
 
-  * the k-grouped weight gradient with B stored K-major, (n, tokens_sum) -- the same logical
-    operands as kgw_wgrad_fp8, stored by a plain transposed copy; the MFMAs see the same
-    token sets in the same order as the default layout, so the results must be identical
-    bit for bit, besides matching the oracle;
+  * the k-grouped weight gradient with A stored M-major (tokens_sum, hidden) and / or B stored
+    K-major (n, tokens_sum) -- the same logical operands as kgw_wgrad_fp8, stored by plain
+    transposed copies; the MFMAs see the same token sets in the same order as the default
+    layout, so the results must be identical bit for bit, besides matching the oracle;
   * the m-grouped forward product with fp8 operands and one UE8M0 scale per 1x128 block
     along K (kgw_mgrouped_fp8), against the oracle's mgrouped_fp8.
 
@@ -25,6 +25,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
 
 DEV = "cuda"
+# (a_major, b_major): both token-contiguous; both token-major; A token-major, B token-contiguous
+LAYOUTS = [("k", "k"), ("m", "n"), ("m", "k")]
 
 
 def nan_filled(shape, dtype=torch.float32):
@@ -43,16 +45,18 @@ def first_mismatch(got, ref):
 
 
 # ----------------------------------------------------------------------------
-# weight gradient, B K-major
+# weight gradient, other operand layouts
 # ----------------------------------------------------------------------------
 def fp8_oracle(wl):
     return oracle.wgrad_fp8(wl.A.cpu(), wl.sfa.cpu(), wl.B.cpu(), wl.sfb.cpu(), wl.offsets.cpu())
 
 
-def run_bk(wl, out=None, outs=None, accumulate=False, split_k=True, out_dtype=torch.float32):
-    bt = wl.B.t().contiguous()
-    r = kgw.kgw_wgrad_fp8_ex(wl.A, wl.sfa, bt, wl.sfb, wl.offsets, b_major="k", out=out, outs=outs,
-                             out_dtype=out_dtype, accumulate=accumulate, split_k=split_k)
+def run_layout(wl, layout, out=None, outs=None, accumulate=False, split_k=True, out_dtype=torch.float32):
+    a_major, b_major = layout
+    a = wl.A.t().contiguous() if a_major == "m" else wl.A
+    b = wl.B.t().contiguous() if b_major == "k" else wl.B
+    r = kgw.kgw_wgrad_fp8_ex(a, wl.sfa, b, wl.sfb, wl.offsets, a_major=a_major, b_major=b_major, out=out,
+                             outs=outs, out_dtype=out_dtype, accumulate=accumulate, split_k=split_k)
     torch.cuda.synchronize()
     return r
 
@@ -66,13 +70,14 @@ def integer_wgrad_case(counts, hidden, n, accumulate, seed):
 
 
 @pytest.mark.parametrize("accumulate", [False, True])
-def test_wgrad_b_k_major_integer_bit_exact(accumulate):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_integer_bit_exact(layout, accumulate):
     # ragged hidden and n tails, an empty expert, one- and odd-block experts (the K loop's
     # two-step remainder), 7 blocks
     counts = [256, 0, 128, 896, 384]
-    wl = integer_wgrad_case(counts, 264, 400, accumulate, seed=201)
-    out = wl.C0.clone() if accumulate else nan_filled((5, 264, 400))
-    run_bk(wl, out=out, accumulate=accumulate)
+    wl = integer_wgrad_case(counts, 272, 400, accumulate, seed=201)
+    out = wl.C0.clone() if accumulate else nan_filled((5, 272, 400))
+    run_layout(wl, layout, out=out, accumulate=accumulate)
     W = fp8_oracle(wl)
     ref = oracle.apply_output_mode(W, accumulate, to_f64(wl.C0) if accumulate else None)
     msg = first_mismatch(to_f64(out), ref)
@@ -80,36 +85,39 @@ def test_wgrad_b_k_major_integer_bit_exact(accumulate):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_wgrad_b_k_major_equals_default_layout_and_oracle(out_dtype):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_equals_default_layout_and_oracle(layout, out_dtype):
     counts = [384, 0, 1152, 256, 640]
-    wl = workloads.make_operands(counts, 328, 400, "fp8", out_dtype, False, seed=202, device=DEV)
+    wl = workloads.make_operands(counts, 336, 400, "fp8", out_dtype, False, seed=202, device=DEV)
     base = kgw.kgw_wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out_dtype=out_dtype)
-    out = run_bk(wl, out=nan_filled((5, 328, 400), out_dtype))
+    out = run_layout(wl, layout, out=nan_filled((5, 336, 400), out_dtype))
     bits = torch.int32 if out_dtype == torch.float32 else torch.int16
     assert torch.equal(out.view(bits), base.view(bits))
     ref = fp8_oracle(wl)
     if out_dtype == torch.float32:
-        assert_fp32_close(to_f64(out), ref, "fp8 B K-major fp32")
+        assert_fp32_close(to_f64(out), ref, f"fp8 {layout} fp32")
     else:
-        assert_bf16_close(to_f64(out), ref, "fp8 B K-major bf16")
+        assert_bf16_close(to_f64(out), ref, f"fp8 {layout} bf16")
 
 
-def test_wgrad_b_k_major_split_k_integer_bit_exact():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_split_k_integer_bit_exact(layout):
     counts = [4096, 0, 8192, 256]
     wl = integer_wgrad_case(counts, 320, 384, False, seed=203)
     assert kgw.kgw_workspace_bytes(4, 320, 384, sum(counts), fp8=True) > 0
-    out = run_bk(wl, out=nan_filled((4, 320, 384)))
-    one = run_bk(wl, out=nan_filled((4, 320, 384)), split_k=False)
+    out = run_layout(wl, layout, out=nan_filled((4, 320, 384)))
+    one = run_layout(wl, layout, out=nan_filled((4, 320, 384)), split_k=False)
     assert np.array_equal(to_f64(out), fp8_oracle(wl)) and torch.equal(out, one)
 
 
 @pytest.mark.parametrize("accumulate", [False, True])
-def test_wgrad_b_k_major_discrete_outputs(accumulate):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_discrete_outputs(layout, accumulate):
     counts = [256, 0, 640, 384]
     wl = integer_wgrad_case(counts, 272, 256, accumulate, seed=204)
     c0 = wl.C0 if accumulate else None
     outs = [None if e == 3 else (c0[e].clone() if accumulate else nan_filled((272, 256))) for e in range(4)]
-    run_bk(wl, outs=outs, accumulate=accumulate)
+    run_layout(wl, layout, outs=outs, accumulate=accumulate)
     W = fp8_oracle(wl)
     ref = oracle.apply_output_mode(W, accumulate, to_f64(c0) if accumulate else None)
     for e in (0, 1, 2):
@@ -117,7 +125,8 @@ def test_wgrad_b_k_major_discrete_outputs(accumulate):
         assert not msg, f"expert {e}: {msg}"
 
 
-def test_wgrad_b_k_major_full_fp8_workload_every_element():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_full_fp8_workload_every_element(layout):
     # the fp8 workload (E=32, hidden 7168, n 4096, n_e = roundup128(8192 * U(0.7, 1.3))):
     # every element written (NaN prefill), identical to the default layout, sampled rows
     # against the oracle
@@ -125,7 +134,7 @@ def test_wgrad_b_k_major_full_fp8_workload_every_element():
     wl = workloads.make_operands(spec["counts"], spec["hidden"], spec["n"], "fp8", torch.bfloat16, False, seed=1,
                                  device=DEV)
     out = nan_filled((32, 7168, 4096), torch.bfloat16)
-    run_bk(wl, out=out, out_dtype=torch.bfloat16)
+    run_layout(wl, layout, out=out, out_dtype=torch.bfloat16)
     assert not torch.isnan(out).any()
     base = kgw.kgw_wgrad_fp8(wl.A, wl.sfa, wl.B, wl.sfb, wl.offsets, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
@@ -136,7 +145,7 @@ def test_wgrad_b_k_major_full_fp8_workload_every_element():
     for e in (0, 31):
         ref = oracle.wgrad_rows_fp8(A, sa, B, sb, off, e, rows)
         got = to_f64(out[e][torch.from_numpy(rows).to(DEV)])
-        assert_bf16_close(got[None], ref[None], f"B K-major full expert {e}",
+        assert_bf16_close(got[None], ref[None], f"{layout} full expert {e}",
                           rms=np.array([np.sqrt(np.mean(ref * ref))]))
 
 
