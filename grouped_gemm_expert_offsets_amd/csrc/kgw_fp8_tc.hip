@@ -480,10 +480,9 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p
 
 // m-grouped forward product with fp8 operands: A (M, K) with sa (K/128, M); W (E, N, K)
 // with sw (E, K/128, N); K a multiple of 128; groups from offsets or m_indices, each
-// starting on a multiple of 128 rows.  Items and the two-pass treatment of a tile whose
-// 128-row halves lie in two groups follow kgw_mgrouped_bf16's kernel: in each pass the
-// other half's A rows (and their scales) read as zeros, both passes accumulate into the
-// same registers, and a half of no group is not stored.
+// starting on a multiple of 128 rows.  Items, and the treatment of a tile whose 128-row
+// halves lie in two groups (one item per half), follow kgw_mgrouped_bf16's kernel; a half
+// of no group is not stored.
 template <int OUT>
 __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
@@ -502,8 +501,13 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
     const int a_half = wave >> 1, s_half = wm;
 
     for (int item = slot; item < p.num_items; item += G) {
+        // Items num_tiles.. are the second halves of the tiles whose 128-row halves lie in
+        // two groups (see kgw_mgrouped_bf16's kernel): the first item computes half 0 with
+        // group g0, the second half 1 with g1, the other half's A rows (and scales) read as
+        // zeros.
+        const bool second = item >= p.num_tiles;
         int tm, tn;
-        tile_coords(item, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
+        tile_coords(second ? item - p.num_tiles : item, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
         const int g0 = group_of_row(p, m0);
@@ -511,12 +515,12 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
         const bool v0 = g0 >= 0 && g0 < p.num_groups;
         const bool v1 = g1 >= 0 && g1 < p.num_groups;
         if (!v0 && !v1) continue;
-        const bool two = v0 && v1 && g0 != g1;
-        const int pg0 = v0 ? g0 : g1;
-        const int pg1 = two ? g1 : pg0;
-        const int nstages = (two ? 2 : 1) * nbk;
-        if (nstages == 0) {
-            if (!p.accumulate) {
+        const bool split = v0 && v1 && g0 != g1;
+        if (second && !split) continue;
+        const int grp = second ? g1 : (v0 ? g0 : g1);
+        const int live_half = split ? (second ? 1 : 0) : -1;   // -1: both halves' rows
+        if (nbk == 0) {
+            if (!p.accumulate && !second) {
                 if (v0) zero_tile<OUT, 128, BN, NT>(p, 0, m0, n0, tid);
                 if (v1) zero_tile<OUT, 128, BN, NT>(p, 0, m0 + 128, n0, tid);
             }
@@ -525,45 +529,30 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
         const int rows_valid = (int)min<int64_t>(BM, M - m0);
         const int cols_valid = (int)min<int64_t>(BN, N - n0);
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * K;
-        // the pass's group as an offset from the first (pointers selected per pass
-        // would keep the captures in scratch memory)
-        const uint8_t* W0 = (const uint8_t*)p.W + ((int64_t)pg0 * N + n0) * K;
-        const int64_t wdelta = (int64_t)(pg1 - pg0) * N * K;
-        const uint8_t* SW0 = p.sw + (int64_t)pg0 * nbk * N + n0;
-        const int64_t swdelta = (int64_t)(pg1 - pg0) * nbk * N;
-        // Stage x of pass 1 (x >= nbk, only with two groups) is stage x - nbk of the second
-        // group; everything per stage is one add and one compare.
-        const int64_t a_bytes = (int64_t)rows_valid * K, w_bytes = (int64_t)cols_valid * K;
-        const bool a_live0 = !two || a_half == 0, a_live1 = two && a_half == 1;
-        const bool s_live0 = !two || s_half == 0, s_live1 = two && s_half == 1;
+        const uint8_t* W0 = (const uint8_t*)p.W + ((int64_t)grp * N + n0) * K;
+        const uint8_t* SW0 = p.sw + (int64_t)grp * nbk * N + n0;
         const uint8_t* SA0 = p.sa + m0;
+        const int64_t a_bytes = (int64_t)rows_valid * K, w_bytes = (int64_t)cols_valid * K;
+        const bool a_live = live_half < 0 || a_half == live_half;
+        const bool s_live = live_half < 0 || s_half == live_half;
         auto rsrc_a = [&](int x) {
-            const bool p1 = x >= nbk;
-            const int64_t o = (int64_t)(p1 ? x - nbk : x) * 128;
-            const bool live = x < nstages && (p1 ? a_live1 : a_live0);
-            return rsrc_words(Abase + o, live ? (uint32_t)(a_bytes - o) : 0u);
+            const int64_t o = (int64_t)x * 128;
+            return rsrc_words(Abase + o, x < nbk && a_live ? (uint32_t)(a_bytes - o) : 0u);
         };
         auto rsrc_b = [&](int x) {
-            const bool p1 = x >= nbk;
-            const int64_t o = (int64_t)(p1 ? x - nbk : x) * 128;
-            return rsrc_words(W0 + (p1 ? wdelta : 0) + o, x < nstages ? (uint32_t)(w_bytes - o) : 0u);
+            const int64_t o = (int64_t)x * 128;
+            return rsrc_words(W0 + o, x < nbk ? (uint32_t)(w_bytes - o) : 0u);
         };
         auto rsrc_sa = [&](int x) {
-            const bool p1 = x >= nbk;
-            const bool live = x < nstages && (p1 ? s_live1 : s_live0);
-            return rsrc_words(SA0 + (int64_t)(p1 ? x - nbk : x) * M, live ? (uint32_t)rows_valid : 0u);
+            return rsrc_words(SA0 + (int64_t)x * M, x < nbk && s_live ? (uint32_t)rows_valid : 0u);
         };
-        auto rsrc_sb = [&](int x) {
-            const bool p1 = x >= nbk;
-            return rsrc_words(SW0 + (p1 ? swdelta : 0) + (int64_t)(p1 ? x - nbk : x) * N,
-                              x < nstages ? (uint32_t)cols_valid : 0u);
-        };
+        auto rsrc_sb = [&](int x) { return rsrc_words(SW0 + (int64_t)x * N, x < nbk ? (uint32_t)cols_valid : 0u); };
         f32x16 acc[4][4];
         zero_acc(acc);
-        fp8_kloop<false, false>(acc, tiles, tiles_addr, wave, lane, nstages, (uint32_t)K, (uint32_t)K,
+        fp8_kloop<false, false>(acc, tiles, tiles_addr, wave, lane, nbk, (uint32_t)K, (uint32_t)K,
                                 (uint32_t)(wm * 128 + lane), (uint32_t)(wn * 128 + lane), rsrc_a, rsrc_b, rsrc_sa,
                                 rsrc_sb);
-        const bool mine = wm ? v1 : v0;
+        const bool mine = split ? wm == live_half : (wm ? v1 : v0);
         if (mine) store_wave_tile_staged<OUT>(p, 0, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         barrier_no_fence();
     }

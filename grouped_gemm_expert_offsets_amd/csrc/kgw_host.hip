@@ -437,8 +437,9 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
     p.num_groups = num_groups;
     p.tiles_m = (int32_t)((m + 255) / 256);
     p.tiles_n = (int32_t)((n + 255) / 256);
-    if ((int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
-    p.num_items = p.tiles_m * p.tiles_n;
+    if (2 * (int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    p.num_items = 2 * p.num_tiles;
     p.accumulate = accumulate;
     p.num_xcds = d.num_xcds;
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
@@ -481,8 +482,9 @@ kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, c
     p.num_groups = num_groups;
     p.tiles_m = (int32_t)((m + 255) / 256);
     p.tiles_n = (int32_t)((n + 255) / 256);
-    if ((int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
-    p.num_items = p.tiles_m * p.tiles_n;
+    if (2 * (int64_t)p.tiles_m * p.tiles_n >= INT32_MAX) return KGW_ERROR_UNSUPPORTED;
+    p.num_tiles = p.tiles_m * p.tiles_n;
+    p.num_items = 2 * p.num_tiles;
     p.accumulate = accumulate;
     p.num_xcds = d.num_xcds;
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;

@@ -83,7 +83,9 @@ struct MGroupedParams {
     int32_t num_groups;
     int32_t tiles_m;
     int32_t tiles_n;
-    int32_t num_items;
+    int32_t num_tiles;      // tiles_m * tiles_n
+    int32_t num_items;      // 2 * num_tiles: item t < num_tiles is tile t, item num_tiles + t the
+                            // second half of tile t when its 128-row halves lie in two groups
     int32_t accumulate;
     int32_t num_xcds;
 };

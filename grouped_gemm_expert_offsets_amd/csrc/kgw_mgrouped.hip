@@ -15,11 +15,12 @@
 // Work decomposition: one item per 256x256 output tile (M-first columns of four
 // tiles, persistent grid, XCD-aware slots as in the k-grouped kernels).  The
 // two 128-row halves of a tile each lie in one group.  When they lie in two
-// different groups the item runs the K loop once per group, each pass loading
-// only its half's A rows (the other half's rows read as zeros through the
-// buffer range) and accumulating into the same registers, so one epilogue
-// writes both halves; only such boundary tiles do the extra MFMA work.  A half
-// of no group is not stored.
+// different groups the tile's item computes half 0 with its group and a second
+// item, in a second list after all tiles, half 1 with the other: each loads only
+// its half's A rows (the other half's rows read as zeros through the buffer
+// range) and stores only its half, so only such boundary tiles do extra MFMA
+// work, and every item of the first list costs one K loop.  A half of no group is
+// not stored.
 //
 // K loop (K a multiple of 64): the k-grouped bf16 kernel's pipeline.  A moves
 // in 64-token stages of full 128-byte rows through a 3-slot ring.  nn: W[g] is
@@ -103,8 +104,14 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
     const int kst = (int)(K / BK);          // K steps of one pass (even)
 
     for (int item = slot; item < p.num_items; item += G) {
+        // Items num_tiles.. are the second halves of the tiles whose 128-row halves lie in
+        // two groups: such a tile's first item computes half 0 with group g0, its second
+        // item half 1 with g1, each a K loop with the other half's A rows read as zeros.
+        // (As one item with two K loops it held up its workgroup a whole tile behind the
+        // others of its XCD, which then stopped sharing operand panels in the XCD's L2.)
+        const bool second = item >= p.num_tiles;
         int tm, tn;
-        tile_coords(item, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
+        tile_coords(second ? item - p.num_tiles : item, p.tiles_m, p.tiles_n, GROUP_M, tm, tn);
         const int64_t m0 = (int64_t)tm * BM;
         const int64_t n0 = (int64_t)tn * BN;
         // Groups of the two 128-row halves.
@@ -113,13 +120,14 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
         const bool v0 = g0 >= 0 && g0 < p.num_groups;
         const bool v1 = g1 >= 0 && g1 < p.num_groups;
         if (!v0 && !v1) continue;
-        const bool two = v0 && v1 && g0 != g1;        // two passes, rows masked per half
-        const int pg0 = v0 ? g0 : g1;
-        const int pg1 = two ? g1 : pg0;
-        const int ksteps = (two ? 2 : 1) * kst;
+        const bool split = v0 && v1 && g0 != g1;      // one item per half, A rows masked
+        if (second && !split) continue;
+        const int grp = second ? g1 : (v0 ? g0 : g1);
+        const int live_half = split ? (second ? 1 : 0) : -1;   // -1: both halves' A rows
+        const int ksteps = kst;
         const int rows_valid = (int)min<int64_t>(BM, M - m0);
         if (ksteps == 0) {                              // K == 0: the product is zero
-            if (!p.accumulate) {
+            if (!p.accumulate && !second) {
                 if (v0) zero_tile<OUT, 128, BN, NT>(p, 0, m0, n0, tid);
                 if (v1) zero_tile<OUT, 128, BN, NT>(p, 0, m0 + 128, n0, tid);
             }
@@ -141,41 +149,30 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
             const int krow = 8 * wave + 2 * t + (lane >> 5);
             b_voff[t] = (uint32_t)krow * (uint32_t)(N * 2) + (uint32_t)min(8 * b_q[t], cols_valid - 8) * 2u;
         }
-        // The weight of the first pass and the byte distance to the second pass's
-        // (an offset, not a choice between two pointers: a select of captured
-        // pointers keeps the lambdas' captures in scratch memory).
-        const char* W0 = (const char*)p.W + (int64_t)pg0 * K * N * 2;
-        const int64_t wdelta = (int64_t)(pg1 - pg0) * K * N * 2;
-        // The A loads of waves 0-1 cover tile rows 0-127 and those of waves 2-3
-        // rows 128-255 (row = 64*wave + ...), so with two passes a wave loads A
-        // only in its own half's pass and an empty range (zeros) in the other.
+        // The item's group's weight; the A loads of waves 0-1 cover tile rows 0-127 and
+        // those of waves 2-3 rows 128-255 (row = 64*wave + ...), so for one half of a split
+        // tile the other half's waves load A from an empty range (zeros).
+        const char* W0 = (const char*)p.W + (int64_t)grp * K * N * 2;
         const int my_half = wave >> 1;
+        const bool a_live = live_half < 0 || my_half == live_half;
 
         // A stage a (steps 2a, 2a+1) to slot a % NA, load `t` of the wave's eight.
         auto dma_a = [&](int a, int t) __attribute__((always_inline)) {
             const uint32_t dst = tiles_addr + (uint32_t)((a % NA) * A_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
-            const int pass = (two && 2 * a >= kst) ? 1 : 0;
-            const int la = a - pass * (kst / 2);
-            const bool live = 2 * a < ksteps && (!two || pass == my_half);
-            const i32x4 r = rsrc_words(Abase + (int64_t)la * (4 * BK), live ? 0xFFFFFFFFu : 0u);
+            const bool live = 2 * a < ksteps && a_live;
+            const i32x4 r = rsrc_words(Abase + (int64_t)a * (4 * BK), live ? 0xFFFFFFFFu : 0u);
             dma_16B(r, a_voff[t], dst);
         };
         // nn: B step sb (k-rows 32*sb.. of the pass's group) to slot sb % 4.
         auto dma_b = [&](int sb, int t) __attribute__((always_inline)) {
             const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (sb % NB) * B_STAGE) + (uint32_t)(4 * wave + t) * 1024u;
-            const bool pass1 = two && sb >= kst;
-            const int ls = pass1 ? sb - kst : sb;
-            const i32x4 r = rsrc_words(W0 + (pass1 ? wdelta : 0) + ((int64_t)ls * BK * N + n0) * 2,
-                                       sb < ksteps ? 0xFFFFFFFFu : 0u);
+            const i32x4 r = rsrc_words(W0 + ((int64_t)sb * BK * N + n0) * 2, sb < ksteps ? 0xFFFFFFFFu : 0u);
             dma_16B(r, b_voff[t], dst);
         };
         // nt: B stage b (steps 2b, 2b+1; n-rows n0.., 64 tokens) to slot b % 2.
         auto dma_bt = [&](int b, int t) __attribute__((always_inline)) {
             const uint32_t dst = tiles_addr + (uint32_t)(B_RING + (b % NB) * B_STAGE) + (uint32_t)(8 * wave + t) * 1024u;
-            const bool pass1 = two && 2 * b >= kst;
-            const int lb = pass1 ? b - kst / 2 : b;
-            const i32x4 r = rsrc_words(W0 + (pass1 ? wdelta : 0) + (n0 * K + (int64_t)lb * 2 * BK) * 2,
-                                       2 * b < ksteps ? 0xFFFFFFFFu : 0u);
+            const i32x4 r = rsrc_words(W0 + (n0 * K + (int64_t)b * 2 * BK) * 2, 2 * b < ksteps ? 0xFFFFFFFFu : 0u);
             dma_16B(r, bt_voff[t], dst);
         };
         // Loads of step s (also the prologue's virtual steps s < 0), in issue
@@ -335,8 +332,9 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_bf16_kernel(MGroupedParams p) 
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier_no_fence();
-        // each wave stores its own 128 x 128; a half of no group is left as is
-        const bool mine = wm ? v1 : v0;
+        // each wave stores its own 128 x 128; a half of no group is left as is, and each half
+        // of a split tile is stored by its own item
+        const bool mine = split ? wm == live_half : (wm ? v1 : v0);
         if (mine)
             store_wave_tile_staged<OUT>(p, 0, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         barrier_no_fence();
