@@ -358,20 +358,25 @@ def kgw_wgrad_fp8_native(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sf
 
 def kgw_wgrad_fp8_ex(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor,
                      offsets: torch.Tensor, *, scale_format: int = KGW_SCALES_U8, native: bool = False,
-                     a_major: str = "k", b_major: str = "n", out: Optional[torch.Tensor] = None, outs=None,
+                     a_major: str = "k", b_major: str = "n", ragged: bool = False, hidden: Optional[int] = None,
+                     n: Optional[int] = None, out: Optional[torch.Tensor] = None, outs=None,
                      out_dtype: torch.dtype = torch.bfloat16, accumulate: bool = False, validate: bool = False,
                      stream=None, split_k: bool = True):
     """fp8 product with a scale layout (KGW_SCALES_*: uint8 per 128 tokens, packed int32 words of
     four 128-token blocks, or packed words of four 32-token blocks) and a dense `out` or discrete
     `outs` (see kgw_wgrad_bf16_ex); native=True uses the scaled fp8 MFMA.  Operand layouts as for
     kgw_wgrad_bf16_ex: a_major "k" (A is (hidden, T), the default) or "m" (A stored (T, hidden));
-    b_major "n" (B is (T, n), the default) or "k" (B stored (n, T)).  Layouts other than the
-    default take the exact path with uint8 scales; the scales keep their (T/128, mn) shapes."""
+    b_major "n" (B is (T, n), the default) or "k" (B stored (n, T)); ragged=True (with a_major
+    "k", b_major "k"): per-expert K-contiguous blocks back to back, passed as flat buffers with
+    `hidden` and `n`.  Layouts other than the default take the exact path with uint8 scales;
+    the scales keep their (T/128, mn) shapes."""
     if a_major not in ("k", "m") or b_major not in ("n", "k"):
         raise ValueError("a_major is 'k' or 'm', b_major is 'n' or 'k'")
+    if ragged and (a_major != "k" or b_major != "k"):
+        raise ValueError("ragged input needs K-major A and B (a_major='k', b_major='k')")
     return _fp8_call("kgw_wgrad_fp8_ex", A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream,
                      split_k, scale_format=scale_format, native=native, outs=outs, a_m_major=a_major == "m",
-                     b_k_major=b_major == "k")
+                     b_k_major=b_major == "k", ragged_dims=(hidden, n) if ragged else None)
 
 
 def kgw_wgrad_fp4(A: torch.Tensor, sfa: torch.Tensor, B: torch.Tensor, sfb: torch.Tensor, offsets: torch.Tensor,
@@ -421,19 +426,28 @@ def scale_shape(tokens: int, mn: int, scale_format: int) -> Tuple[Tuple[int, int
 
 
 def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validate, stream, split_k,
-              scale_format=KGW_SCALES_U8, native=None, outs=None, a_m_major=False, b_k_major=False):
+              scale_format=KGW_SCALES_U8, native=None, outs=None, a_m_major=False, b_k_major=False,
+              ragged_dims=None):
     fp8_types = (torch.uint8, torch.float8_e4m3fn)
     if A.dtype not in fp8_types or B.dtype not in fp8_types:
         raise ValueError(f"{name} takes e4m3fn (or raw uint8) A and B")
     if sfa is None or sfb is None:
         raise ValueError(f"{name} needs both scale tensors sfa and sfb")
-    if A.dim() != 2 or B.dim() != 2:
-        raise ValueError("A and B must be 2-D")
-    hidden, T = (A.shape[1], A.shape[0]) if a_m_major else (A.shape[0], A.shape[1])
-    Tb, n = (B.shape[1], B.shape[0]) if b_k_major else (B.shape[0], B.shape[1])
-    if Tb != T:
-        raise ValueError(f"shape mismatch: A {tuple(A.shape)}{' (stored (T, hidden))' if a_m_major else ''}, "
-                         f"B {tuple(B.shape)}{' (stored (n, T))' if b_k_major else ''}")
+    if ragged_dims is not None:
+        hidden, n = ragged_dims
+        if hidden is None or n is None or hidden <= 0 or n <= 0 or A.numel() % hidden:
+            raise ValueError("ragged input needs hidden and n, and A.numel() a multiple of hidden")
+        T = A.numel() // hidden
+        if B.numel() != T * n:
+            raise ValueError(f"B must hold tokens_sum * n = {T * n} elements")
+    else:
+        if A.dim() != 2 or B.dim() != 2:
+            raise ValueError("A and B must be 2-D")
+        hidden, T = (A.shape[1], A.shape[0]) if a_m_major else (A.shape[0], A.shape[1])
+        Tb, n = (B.shape[1], B.shape[0]) if b_k_major else (B.shape[0], B.shape[1])
+        if Tb != T:
+            raise ValueError(f"shape mismatch: A {tuple(A.shape)}{' (stored (T, hidden))' if a_m_major else ''}, "
+                             f"B {tuple(B.shape)}{' (stored (n, T))' if b_k_major else ''}")
     (sa_shape, sdtype), (sb_shape, _) = scale_shape(T, hidden, scale_format), scale_shape(T, n, scale_format)
     if sfa.dtype != sdtype or sfb.dtype != sdtype:
         raise ValueError(f"this scale format takes {sdtype} scale tensors")
@@ -457,7 +471,8 @@ def _fp8_call(name, A, sfa, B, sfb, offsets, out, out_dtype, accumulate, validat
                 int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     else:
         st = fn(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), int(scale_format), int(bool(native)),
-                (KGW_A_M_MAJOR if a_m_major else 0) | (KGW_B_K_MAJOR if b_k_major else 0), _ptr(offsets), E,
+                (KGW_A_M_MAJOR if a_m_major else 0) | (KGW_B_K_MAJOR if b_k_major else 0) |
+                (KGW_RAGGED if ragged_dims is not None else 0), _ptr(offsets), E,
                 hidden, n, T, _ptr(out), _ptr(ptrs), code,
                 int(bool(accumulate)), _ptr(ws), ws_bytes, _stream_ptr(stream))
     _check(st, name)

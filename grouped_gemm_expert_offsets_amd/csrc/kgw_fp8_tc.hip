@@ -397,8 +397,8 @@ __device__ __forceinline__ i32x4 rsrc_bytes(const void* base, int64_t bytes, boo
 
 // k-grouped weight gradient in the operand layouts other than kgw_wgrad_fp8's default
 // (A_TR: A stored (tokens_sum, hidden); B_TR: B stored (tokens_sum, n), else (n,
-// tokens_sum)), one UE8M0 byte per 128 tokens for each operand (sfa (T/128, hidden),
-// sfb (T/128, n)).  Items, token ranges, split-K chunks, zero-fill and output as in
+// tokens_sum); with neither, p.ragged selects per-expert K-contiguous blocks), one UE8M0
+// byte per 128 tokens for each operand (sfa (T/128, hidden), sfb (T/128, n)).  Items, token ranges, split-K chunks, zero-fill and output as in
 // kgw_wgrad_fp8's kernel.
 template <int OUT, bool A_TR, bool B_TR>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p) {
@@ -427,15 +427,20 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p
         const int64_t n0 = (int64_t)tn * BN;
         const int64_t raw_begin = e ? (int64_t)p.offsets[e - 1] : 0;
         const int64_t raw_end = p.offsets[e];
-        int32_t begin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
-        int32_t end = max(begin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        const int32_t ebegin = (int32_t)(raw_begin < 0 ? 0 : (raw_begin > T ? T : raw_begin));
+        const int32_t eend = max(ebegin, (int32_t)(raw_end < 0 ? 0 : (raw_end > T ? T : raw_end)));
+        int32_t begin = ebegin, end = eend;
         if (p.split > 1) {
             const int32_t len = ((end - begin + p.split - 1) / p.split + kSplitUnit - 1) & ~(kSplitUnit - 1);
             const int32_t cb = (int32_t)min<int64_t>(end, (int64_t)begin + (int64_t)c * len);
             end = (int32_t)min<int64_t>(end, (int64_t)cb + len);
             begin = cb;
         }
-        begin &= ~127;
+        // whole 128-token blocks; ragged blocks are counted from their own start, so the loads
+        // stay inside the expert's block even for malformed offsets
+        const bool ragged = !A_TR && !B_TR && p.ragged;
+        if (ragged) begin = ebegin + ((begin - ebegin) & ~127);
+        else begin &= ~127;
         const int nblocks = (end - begin) / 128;
         if (nblocks == 0) {
             if (!p.accumulate) zero_tile<OUT, BM, BN, NT>(p, eo, m0, n0, tid);
@@ -447,11 +452,19 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p
         // (n) from row `begin`, the tile's 256 columns at m0 (n0); columns past hidden (n)
         // read the next row's bytes (outputs that are never stored), the range ending at the
         // end of the operand.
+        // Ragged (both TC): expert e's A block is (hidden, n_e) row-major from element
+        // ebegin*hidden, its B block (n, n_e) from ebegin*n; rows at stride n_e.
         // (bases and byte counts per item; a stage / step only adds a multiple of its size)
-        const uint8_t* Abase = (const uint8_t*)p.A + (A_TR ? (int64_t)begin * H + m0 : m0 * T + begin);
-        const uint8_t* Bbase = (const uint8_t*)p.B + (B_TR ? (int64_t)begin * N + n0 : n0 * T + begin);
-        const int64_t a_bytes = A_TR ? T * H - ((int64_t)begin * H + m0) : min<int64_t>(BM, H - m0) * T - begin;
-        const int64_t b_bytes = B_TR ? T * N - ((int64_t)begin * N + n0) : min<int64_t>(BN, N - n0) * T - begin;
+        const int64_t ne = (int64_t)eend - ebegin, koff = (int64_t)begin - ebegin;
+        const int64_t tc_stride = ragged ? ne : T;
+        const uint8_t* Abase = (const uint8_t*)p.A +
+                               (A_TR ? (int64_t)begin * H + m0 : ragged ? ebegin * H + m0 * ne + koff : m0 * T + begin);
+        const uint8_t* Bbase = (const uint8_t*)p.B +
+                               (B_TR ? (int64_t)begin * N + n0 : ragged ? ebegin * N + n0 * ne + koff : n0 * T + begin);
+        const int64_t a_bytes = A_TR ? T * H - ((int64_t)begin * H + m0)
+                                     : min<int64_t>(BM, H - m0) * tc_stride - (ragged ? koff : begin);
+        const int64_t b_bytes = B_TR ? T * N - ((int64_t)begin * N + n0)
+                                     : min<int64_t>(BN, N - n0) * tc_stride - (ragged ? koff : begin);
         const int64_t a_step = A_TR ? (int64_t)KS * H : 128;      // bytes per TR step / TC stage
         const int64_t b_step = B_TR ? (int64_t)KS * N : 128;
         const int a_units = A_TR ? nsteps : nblocks, b_units = B_TR ? nsteps : nblocks;
@@ -470,8 +483,8 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p
         auto rsrc_sb = [&](int x) { return rsrc_words(p.sfb + (gb0 + x) * N, x < nblocks ? (uint32_t)N : 0u); };
         f32x16 acc[4][4];
         zero_acc(acc);
-        fp8_kloop<A_TR, B_TR>(acc, tiles, tiles_addr, wave, lane, nblocks, (uint32_t)(A_TR ? H : T),
-                              (uint32_t)(B_TR ? N : T), (uint32_t)(m0 + wm * 128 + lane),
+        fp8_kloop<A_TR, B_TR>(acc, tiles, tiles_addr, wave, lane, nblocks, (uint32_t)(A_TR ? H : tc_stride),
+                              (uint32_t)(B_TR ? N : tc_stride), (uint32_t)(m0 + wm * 128 + lane),
                               (uint32_t)(n0 + wn * 128 + lane), rsrc_a, rsrc_b, rsrc_sa, rsrc_sb);
         store_wave_tile_staged<OUT>(p, eo, m0 + wm * 128, n0 + wn * 128, lane, acc, tiles + wave * 32768);
         barrier_no_fence();

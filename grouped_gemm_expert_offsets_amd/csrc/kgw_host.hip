@@ -180,11 +180,10 @@ kgw_status_t run(Kernel kernel, const void* A, const void* sfa, const void* B, c
     // token rows of an M-major A are addressed with 32-bit offsets, as B's (check_common)
     if ((layout & KGW_A_M_MAJOR) && 64 * hidden * 2 >= ((int64_t)1 << 31)) return KGW_ERROR_UNSUPPORTED;
     // fp8 / fp4: the default layout, or (exact fp8, one byte per 128 tokens) A M-major and / or
-    // B K-major; A M-major rows of tokens move in 16-byte pieces (hidden % 16) with 32-bit
-    // offsets over 64 token rows
+    // B K-major, or ragged blocks; A M-major rows of tokens move in 16-byte pieces
+    // (hidden % 16) with 32-bit offsets over 64 token rows
     if (fp8 && layout != 0) {
-        if ((layout & KGW_RAGGED) || kernel != Kernel::kFp8 || scale_format != KGW_SCALES_U8)
-            return KGW_ERROR_UNSUPPORTED;
+        if (kernel != Kernel::kFp8 || scale_format != KGW_SCALES_U8) return KGW_ERROR_UNSUPPORTED;
         if ((layout & KGW_A_M_MAJOR) && hidden % 16 != 0) return KGW_ERROR_MISALIGNED;
         if ((layout & KGW_A_M_MAJOR) && 64 * hidden >= ((int64_t)1 << 31)) return KGW_ERROR_UNSUPPORTED;
     }

@@ -256,17 +256,18 @@ kgw_status_t kgw_wgrad_fp8_native(const void* A, const uint8_t* sfa, const void*
  * blocks are exactly 32 tokens: each lane hands the instruction the byte of
  * its half of the 64-token step).  out / out_ptrs as for kgw_wgrad_bf16_ex.
  * layout: 0 (A (hidden, tokens_sum), B (tokens_sum, n), as for kgw_wgrad_fp8) or
- * KGW_A_M_MAJOR and / or KGW_B_K_MAJOR with the meaning they have for
- * kgw_wgrad_bf16_ex: A stored (tokens_sum, hidden), element (m, t) at
+ * the KGW_A_M_MAJOR / KGW_B_K_MAJOR / KGW_RAGGED combinations kgw_wgrad_bf16_ex
+ * takes, with the same meaning: A stored (tokens_sum, hidden), element (m, t) at
  * A[t * hidden + m]; B stored (n, tokens_sum), element (t, j) at
  * B[j * tokens_sum + t] (with the default A: both operands token-contiguous, the
- * pair a (M, K), b (N, K) of the DeepGEMM k-grouped page).  The scales keep their
- * (tokens_sum/128, hidden) and (tokens_sum/128, n) layouts.  The other layouts
- * are taken with native 0 and KGW_SCALES_U8 only, KGW_A_M_MAJOR needs hidden a
- * multiple of 16 (KGW_ERROR_MISALIGNED) and below 2^25; KGW_RAGGED, other
- * combinations or larger sizes are KGW_ERROR_UNSUPPORTED (bits outside the KGW_*
- * layout flags: KGW_ERROR_INVALID_VALUE).  Every layout gives the default
- * layout's result bit for bit.
+ * pair a (M, K), b (N, K) of the DeepGEMM k-grouped page); ragged per-expert
+ * K-contiguous blocks (KGW_RAGGED | KGW_B_K_MAJOR).  The scales keep their
+ * (tokens_sum/128, hidden) and (tokens_sum/128, n) layouts in every case.  These
+ * layouts are taken with native 0 and KGW_SCALES_U8 only (else
+ * KGW_ERROR_UNSUPPORTED); KGW_A_M_MAJOR needs hidden a multiple of 16
+ * (KGW_ERROR_MISALIGNED) and below 2^25 (KGW_ERROR_UNSUPPORTED); other
+ * combinations and bits are rejected as by kgw_wgrad_bf16_ex.  Every layout gives
+ * the default layout's result bit for bit.
  * Counts stay multiples of 128 for every format.  Everything else as for
  * kgw_wgrad_fp8; an unknown scale_format or native value is
  * KGW_ERROR_INVALID_VALUE, a misaligned KGW_SCALES_PACKED_32 pointer

@@ -207,7 +207,10 @@ def test_extended_entry_point_errors(lib):
         assert call_fp8_ex(lib, layout=lay, fmt=kgw.KGW_SCALES_PACKED_32) == kgw.KGW_ERROR_UNSUPPORTED
         assert call_fp8_ex(lib, layout=lay, H=0) == kgw.KGW_SUCCESS           # nothing to write
         assert call_fp8_ex(lib, layout=lay, N=520) == kgw.KGW_ERROR_MISALIGNED
-    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | BK) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | BK) == kgw.KGW_ERROR_DEVICE     # ragged blocks accepted
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | BK, native=1) == kgw.KGW_ERROR_UNSUPPORTED
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_fp8_ex(lib, layout=kgw.KGW_RAGGED | AM | BK) == kgw.KGW_ERROR_INVALID_VALUE
     assert call_fp8_ex(lib, layout=AM, H=264) == kgw.KGW_ERROR_MISALIGNED      # fp8 M-major rows: hidden % 16
     assert call_fp8_ex(lib, layout=BK, H=264) == kgw.KGW_ERROR_DEVICE
     assert call_fp8_ex(lib, layout=AM, H=1 << 25) == kgw.KGW_ERROR_UNSUPPORTED  # 32-bit row offsets

@@ -1,9 +1,10 @@
 """GPU parity of the fp8 products in the operand layouts other than kgw_wgrad_fp8's default:
 
   * the k-grouped weight gradient with A stored M-major (tokens_sum, hidden) and / or B stored
-    K-major (n, tokens_sum) -- the same logical operands as kgw_wgrad_fp8, stored by plain
-    transposed copies; the MFMAs see the same token sets in the same order as the default
-    layout, so the results must be identical bit for bit, besides matching the oracle;
+    K-major (n, tokens_sum), or as per-expert K-contiguous blocks (ragged) -- the same logical
+    operands as kgw_wgrad_fp8, stored by plain copies; the MFMAs see the same token sets in the
+    same order as the default layout, so the results must be identical bit for bit, besides
+    matching the oracle;
   * the m-grouped forward product with fp8 operands and one UE8M0 scale per 1x128 block
     along K (kgw_mgrouped_fp8), against the oracle's mgrouped_fp8.
 
@@ -25,8 +26,9 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
 
 DEV = "cuda"
-# (a_major, b_major): both token-contiguous; both token-major; A token-major, B token-contiguous
-LAYOUTS = [("k", "k"), ("m", "n"), ("m", "k")]
+# (a_major, b_major): both token-contiguous; both token-major; A token-major, B token-contiguous;
+# "r": per-expert K-contiguous blocks back to back (ragged)
+LAYOUTS = [("k", "k"), ("m", "n"), ("m", "k"), ("r", "r")]
 
 
 def nan_filled(shape, dtype=torch.float32):
@@ -53,10 +55,19 @@ def fp8_oracle(wl):
 
 def run_layout(wl, layout, out=None, outs=None, accumulate=False, split_k=True, out_dtype=torch.float32):
     a_major, b_major = layout
-    a = wl.A.t().contiguous() if a_major == "m" else wl.A
-    b = wl.B.t().contiguous() if b_major == "k" else wl.B
-    r = kgw.kgw_wgrad_fp8_ex(a, wl.sfa, b, wl.sfb, wl.offsets, a_major=a_major, b_major=b_major, out=out,
-                             outs=outs, out_dtype=out_dtype, accumulate=accumulate, split_k=split_k)
+    if a_major == "r":
+        # expert e's A block (hidden, n_e) and B block (n, n_e), row-major, back to back
+        off = [0] + wl.offsets.tolist()
+        a = torch.cat([wl.A[:, off[e]:off[e + 1]].contiguous().reshape(-1) for e in range(len(off) - 1)])
+        b = torch.cat([wl.B[off[e]:off[e + 1]].t().contiguous().reshape(-1) for e in range(len(off) - 1)])
+        r = kgw.kgw_wgrad_fp8_ex(a, wl.sfa, b, wl.sfb, wl.offsets, a_major="k", b_major="k", ragged=True,
+                                 hidden=wl.hidden, n=wl.n, out=out, outs=outs, out_dtype=out_dtype,
+                                 accumulate=accumulate, split_k=split_k)
+    else:
+        a = wl.A.t().contiguous() if a_major == "m" else wl.A
+        b = wl.B.t().contiguous() if b_major == "k" else wl.B
+        r = kgw.kgw_wgrad_fp8_ex(a, wl.sfa, b, wl.sfb, wl.offsets, a_major=a_major, b_major=b_major, out=out,
+                                 outs=outs, out_dtype=out_dtype, accumulate=accumulate, split_k=split_k)
     torch.cuda.synchronize()
     return r
 
