@@ -286,22 +286,25 @@ def run_mgrouped(layout: str, steps: int, warmup: int, min_warm_s: float = 0.0):
     return res
 
 
-def run_mgrouped_fp8(steps: int, warmup: int, min_warm_s: float = 0.0):
-    """kgw_mgrouped_fp8 on the fp8 workload's layer forward: X (T, 7168) @ W^T, W (32, 4096, 7168),
-    32 groups of roundup128(8192*U(0.7,1.3)) rows, e4m3 operands with 1x128 UE8M0 scales along K
-    (block-quantised Gaussian draws), bf16 output."""
+def run_mgrouped_fp8(layout: str, steps: int, warmup: int, min_warm_s: float = 0.0):
+    """kgw_mgrouped_fp8 on the fp8 workload's layer: 32 groups of roundup128(8192*U(0.7,1.3))
+    rows, e4m3 operands with 1x128 UE8M0 scales along K (block-quantised Gaussian draws), bf16
+    output; forward ("nt") X (T, 7168) @ W^T with W (32, 4096, 7168); dgrad ("nn") dY (T, 4096)
+    @ W with the weight stored (32, K=4096, N=7168)."""
     import torch
     import grouped_gemm_expert_offsets_amd as kgw
     import workloads
     counts = workloads.counts_uniform(32, 8192, 128, 1)
-    K, N = 7168, 4096
+    K, N = (7168, 4096) if layout == "nt" else (4096, 7168)
     wl = workloads.make_mgrouped_fp8(counts, K, N, seed=1, device="cuda")
+    W = wl.W if layout == "nt" else wl.W.transpose(1, 2).contiguous()
     out = torch.empty((wl.M, N), dtype=torch.bfloat16, device="cuda")
-    ms_step, launch_ms = time_call(lambda: kgw.kgw_mgrouped_fp8(wl.A, wl.sa, wl.W, wl.sw, offsets=wl.offsets,
-                                                                out=out), steps, warmup, min_warm_s)
+    ms_step, launch_ms = time_call(lambda: kgw.kgw_mgrouped_fp8(wl.A, wl.sa, W, wl.sw, offsets=wl.offsets,
+                                                                layout=layout, out=out), steps, warmup, min_warm_s)
     mean_launch = sum(launch_ms) / len(launch_ms)
     res = {
-        "workload": f"mgrouped_fp8_nt forward M={wl.M} K={K} N={N} E=32 e4m3 1x128 UE8M0, bf16 out",
+        "workload": (f"mgrouped_fp8_{layout} {'forward' if layout == 'nt' else 'dgrad'} M={wl.M} K={K} N={N} E=32 "
+                     "e4m3 1x128 UE8M0, bf16 out"),
         "ms_per_step": ms_step,
         "launch_ms_mean": mean_launch,
         "tflops": wl.flops / (mean_launch * 1e-3) / 1e12,
@@ -309,7 +312,7 @@ def run_mgrouped_fp8(steps: int, warmup: int, min_warm_s: float = 0.0):
     }
     res["frac_of_mfma_peak"] = res["tflops"] / PEAK_FP8_TFLOPS
     res["frac_of_bf16_mfma_peak"] = res["tflops"] / PEAK_BF16_TFLOPS
-    del wl, out
+    del wl, W, out
     torch.cuda.empty_cache()
     return res
 
@@ -565,7 +568,8 @@ def main():
         add(run_fp4(sec_steps, sec_warm, args.secondary_warm_seconds))
         for layout in ("nt", "nn"):
             add(run_mgrouped(layout, sec_steps, sec_warm, args.secondary_warm_seconds))
-        add(run_mgrouped_fp8(sec_steps, sec_warm, args.secondary_warm_seconds))
+        for layout in ("nt", "nn"):
+            add(run_mgrouped_fp8(layout, sec_steps, sec_warm, args.secondary_warm_seconds))
         for fp4 in (False, True):
             for axis in (1, 0):
                 add(run_quantize(axis, sec_steps, sec_warm, args.secondary_warm_seconds, fp4=fp4))

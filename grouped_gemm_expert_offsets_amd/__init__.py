@@ -98,7 +98,7 @@ def load_library():
     lib.kgw_mgrouped_bf16.restype = ctypes.c_int
     lib.kgw_mgrouped_bf16.argtypes = [p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_mgrouped_fp8.restype = ctypes.c_int
-    lib.kgw_mgrouped_fp8.argtypes = [p, p, p, p, p, p, i32, i64, i64, i64, p, i32, i32, p]
+    lib.kgw_mgrouped_fp8.argtypes = [p, p, p, p, i32, p, p, i32, i64, i64, i64, p, i32, i32, p]
     lib.kgw_quantize_fp8.restype = ctypes.c_int
     lib.kgw_quantize_fp8.argtypes = [p, i64, i64, i32, i32, p, p, p]
     lib.kgw_quantize_fp4.restype = ctypes.c_int
@@ -584,12 +584,13 @@ def kgw_mgrouped_bf16(A: torch.Tensor, W: torch.Tensor, *, offsets: Optional[tor
 
 def kgw_mgrouped_fp8(A: torch.Tensor, sa: torch.Tensor, W: torch.Tensor, sw: torch.Tensor, *,
                      offsets: Optional[torch.Tensor] = None, m_indices: Optional[torch.Tensor] = None,
-                     out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
-                     accumulate: bool = False, stream=None) -> torch.Tensor:
-    """m-grouped forward product with fp8 operands: out[r] = a(r) @ w(g(r))^T, where A is e4m3
-    (M, K) with UE8M0 sa (K/128, M) and W is e4m3 (E, N, K) with UE8M0 sw (E, K/128, N), one
-    scale per 1x128 block along K; groups from `offsets` or `m_indices` as for
-    kgw_mgrouped_bf16; rows of no group are left untouched."""
+                     layout: str = "nt", out: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, accumulate: bool = False, stream=None) -> torch.Tensor:
+    """m-grouped product with fp8 operands: A is e4m3 (M, K) with UE8M0 sa (K/128, M); W is e4m3
+    (E, N, K) for layout "nt" (forward, out[r] = a(r) @ w(g(r))^T) or (E, K, N) for "nn" (dgrad,
+    out[r] = a(r) @ w(g(r))), with UE8M0 sw (E, K/128, N) either way, one scale per 1x128 block
+    along K; groups from `offsets` or `m_indices` as for kgw_mgrouped_bf16; rows of no group
+    are left untouched."""
     fp8_types = (torch.uint8, torch.float8_e4m3fn)
     if A.dtype not in fp8_types or W.dtype not in fp8_types:
         raise ValueError("kgw_mgrouped_fp8 takes e4m3fn (or raw uint8) A and W")
@@ -600,10 +601,13 @@ def kgw_mgrouped_fp8(A: torch.Tensor, sa: torch.Tensor, W: torch.Tensor, sw: tor
     for t in (A, W, sa, sw):
         if not t.is_contiguous():
             raise ValueError("fp8 operands and scales must be contiguous")
+    if layout not in ("nt", "nn"):
+        raise ValueError("layout is 'nt' (forward) or 'nn' (dgrad)")
     M, K = A.shape
-    E, N = W.shape[0], W.shape[1]
-    if W.shape[2] != K:
-        raise ValueError(f"W {tuple(W.shape)} does not match A's K = {K}")
+    E = W.shape[0]
+    N = W.shape[1] if layout == "nt" else W.shape[2]
+    if (W.shape[2] if layout == "nt" else W.shape[1]) != K:
+        raise ValueError(f"W {tuple(W.shape)} does not match A's K = {K} for layout {layout}")
     if K % FP8_TOKEN_ALIGN != 0:
         raise ValueError(f"K ({K}) must be a multiple of {FP8_TOKEN_ALIGN}")
     if tuple(sa.shape) != (K // FP8_TOKEN_ALIGN, M) or tuple(sw.shape) != (E, K // FP8_TOKEN_ALIGN, N):
@@ -629,8 +633,10 @@ def kgw_mgrouped_fp8(A: torch.Tensor, sa: torch.Tensor, W: torch.Tensor, sw: tor
         out = torch.empty((M, N), dtype=out_dtype, device=device)
     elif tuple(out.shape) != (M, N) or not out.is_contiguous() or out.device != device:
         raise ValueError(f"out must be a contiguous {(M, N)} tensor on the operands' device")
-    st = load_library().kgw_mgrouped_fp8(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(offsets), _ptr(m_indices), E,
-                                         M, K, N, _ptr(out), code, int(bool(accumulate)), _stream_ptr(stream))
+    st = load_library().kgw_mgrouped_fp8(_ptr(A), _ptr(sa), _ptr(W), _ptr(sw),
+                                         KGW_LAYOUT_NT if layout == "nt" else KGW_LAYOUT_NN, _ptr(offsets),
+                                         _ptr(m_indices), E, M, K, N, _ptr(out), code, int(bool(accumulate)),
+                                         _stream_ptr(stream))
     _check(st, "kgw_mgrouped_fp8")
     return out
 

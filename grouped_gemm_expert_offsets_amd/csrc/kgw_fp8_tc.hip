@@ -491,12 +491,13 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp8_layout_kernel(GroupedParams p
     }
 }
 
-// m-grouped forward product with fp8 operands: A (M, K) with sa (K/128, M); W (E, N, K)
-// with sw (E, K/128, N); K a multiple of 128; groups from offsets or m_indices, each
-// starting on a multiple of 128 rows.  Items, and the treatment of a tile whose 128-row
-// halves lie in two groups (one item per half), follow kgw_mgrouped_bf16's kernel; a half
-// of no group is not stored.
-template <int OUT>
+// m-grouped product with fp8 operands: A (M, K) with sa (K/128, M); W with sw (E, K/128, N),
+// stored (E, N, K) for the forward (NTL, "nt": W staged TC) or (E, K, N) for dgrad ("nn":
+// W staged TR); K a multiple of 128; groups from offsets or m_indices, each starting on a
+// multiple of 128 rows.  Items, and the treatment of a tile whose 128-row halves lie in two
+// groups (one item per half), follow kgw_mgrouped_bf16's kernel; a half of no group is not
+// stored.
+template <int OUT, bool NTL>
 __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
@@ -542,7 +543,11 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
         const int rows_valid = (int)min<int64_t>(BM, M - m0);
         const int cols_valid = (int)min<int64_t>(BN, N - n0);
         const uint8_t* Abase = (const uint8_t*)p.A + m0 * K;
-        const uint8_t* W0 = (const uint8_t*)p.W + ((int64_t)grp * N + n0) * K;
+        // nt: the group's rows n0.. of (N, K); nn: its K rows of (K, N) from column n0, the
+        // range running to the end of W (columns past N read the next row's bytes, outputs
+        // that are never stored)
+        const uint8_t* W0 = (const uint8_t*)p.W + (NTL ? ((int64_t)grp * N + n0) * K : (int64_t)grp * K * N + n0);
+        const int64_t w_end = (int64_t)p.num_groups * K * N - ((int64_t)grp * K * N + n0);
         const uint8_t* SW0 = p.sw + (int64_t)grp * nbk * N + n0;
         const uint8_t* SA0 = p.sa + m0;
         const int64_t a_bytes = (int64_t)rows_valid * K, w_bytes = (int64_t)cols_valid * K;
@@ -553,8 +558,13 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
             return rsrc_words(Abase + o, x < nbk && a_live ? (uint32_t)(a_bytes - o) : 0u);
         };
         auto rsrc_b = [&](int x) {
-            const int64_t o = (int64_t)x * 128;
-            return rsrc_words(W0 + o, x < nbk ? (uint32_t)(w_bytes - o) : 0u);
+            if constexpr (NTL) {
+                const int64_t o = (int64_t)x * 128;
+                return rsrc_words(W0 + o, x < nbk ? (uint32_t)(w_bytes - o) : 0u);
+            } else {
+                const int64_t o = (int64_t)x * KS * N;
+                return rsrc_bytes(W0 + o, w_end - o, x < 2 * nbk);
+            }
         };
         auto rsrc_sa = [&](int x) {
             return rsrc_words(SA0 + (int64_t)x * M, x < nbk && s_live ? (uint32_t)rows_valid : 0u);
@@ -562,7 +572,7 @@ __global__ __launch_bounds__(NT, 1) void mgrouped_fp8_kernel(MGroupedParams p) {
         auto rsrc_sb = [&](int x) { return rsrc_words(SW0 + (int64_t)x * N, x < nbk ? (uint32_t)cols_valid : 0u); };
         f32x16 acc[4][4];
         zero_acc(acc);
-        fp8_kloop<false, false>(acc, tiles, tiles_addr, wave, lane, nbk, (uint32_t)K, (uint32_t)K,
+        fp8_kloop<false, !NTL>(acc, tiles, tiles_addr, wave, lane, nbk, (uint32_t)K, (uint32_t)(NTL ? K : N),
                                 (uint32_t)(wm * 128 + lane), (uint32_t)(wn * 128 + lane), rsrc_a, rsrc_b, rsrc_sa,
                                 rsrc_sb);
         const bool mine = split ? wm == live_half : (wm ? v1 : v0);
@@ -592,14 +602,19 @@ hipError_t launch_wgrad_fp8_layout(const GroupedParams& p, bool a_m_major, bool 
     return hipErrorInvalidValue;     // the default layout is kgw_wgrad_fp8's own kernel
 }
 
-hipError_t launch_mgrouped_fp8(const MGroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+template <bool NTL>
+hipError_t launch_mg8(const MGroupedParams& p, int out_kind, int grid, hipStream_t stream) {
     if (out_kind == kOutBf16)
-        hipLaunchKernelGGL(mgrouped_fp8_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((mgrouped_fp8_kernel<kOutBf16, NTL>), dim3(grid), dim3(NT), 0, stream, p);
     else if (out_kind == kOutF16)
-        hipLaunchKernelGGL(mgrouped_fp8_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((mgrouped_fp8_kernel<kOutF16, NTL>), dim3(grid), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(mgrouped_fp8_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((mgrouped_fp8_kernel<kOutF32, NTL>), dim3(grid), dim3(NT), 0, stream, p);
     return hipGetLastError();
+}
+
+hipError_t launch_mgrouped_fp8(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream) {
+    return nt ? launch_mg8<true>(p, out_kind, grid, stream) : launch_mg8<false>(p, out_kind, grid, stream);
 }
 
 }  // namespace kgw

@@ -446,17 +446,19 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 
-kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, const uint8_t* sw,
+kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, const uint8_t* sw, int32_t layout,
                               const int32_t* offsets, const int32_t* m_indices, int32_t num_groups, int64_t m,
                               int64_t k, int64_t n, void* out, int32_t out_dtype, int32_t accumulate, void* stream) {
     if (num_groups < 1 || m < 0 || k < 0 || n < 0) return KGW_ERROR_INVALID_VALUE;
+    if (layout != KGW_LAYOUT_NT && layout != KGW_LAYOUT_NN) return KGW_ERROR_INVALID_VALUE;
     if (out_dtype != KGW_OUT_FP32 && out_dtype != KGW_OUT_BF16 && out_dtype != KGW_OUT_FP16)
         return KGW_ERROR_INVALID_VALUE;
     if (accumulate != 0 && accumulate != 1) return KGW_ERROR_INVALID_VALUE;
     if ((offsets != nullptr) == (m_indices != nullptr)) return KGW_ERROR_INVALID_VALUE;
     if (num_groups > kgw::kMaxExperts) return KGW_ERROR_UNSUPPORTED;
     if (m > INT32_MAX || k >= ((int64_t)1 << 22) || n >= ((int64_t)1 << 24)) return KGW_ERROR_UNSUPPORTED;
-    if (k % 128 != 0 || n % 8 != 0) return KGW_ERROR_MISALIGNED;
+    // nn: W's rows of N values move in 16-byte pieces
+    if (k % 128 != 0 || n % (layout == KGW_LAYOUT_NN ? 16 : 8) != 0) return KGW_ERROR_MISALIGNED;
     if (m == 0 || n == 0) return KGW_SUCCESS;
     if (!out || (k > 0 && (!A || !W || !sa || !sw))) return KGW_ERROR_INVALID_VALUE;
     if (!aligned16(A) || !aligned16(W) || !aligned16(out) || (((uintptr_t)offsets | (uintptr_t)m_indices) & 3u))
@@ -487,7 +489,7 @@ kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, c
     p.accumulate = accumulate;
     p.num_xcds = d.num_xcds;
     const int grid = p.num_items < d.num_cus ? p.num_items : d.num_cus;
-    const hipError_t err = kgw::launch_mgrouped_fp8(p, out_dtype, grid, (hipStream_t)stream);
+    const hipError_t err = kgw::launch_mgrouped_fp8(p, layout == KGW_LAYOUT_NT, out_dtype, grid, (hipStream_t)stream);
     return err == hipSuccess ? KGW_SUCCESS : KGW_ERROR_DEVICE;
 }
 

@@ -141,7 +141,7 @@ hipError_t launch_mgrouped_bf16(const MGroupedParams& p, bool nt, int out_kind, 
 // a_m_major, B stored (n, tokens_sum) when b_k_major (at least one of them).
 hipError_t launch_wgrad_fp8_layout(const GroupedParams& p, bool a_m_major, bool b_k_major, int out_kind, int grid,
                                    hipStream_t stream);
-// m-grouped forward product with fp8 operands and 1x128 UE8M0 scales (nt layout).
-hipError_t launch_mgrouped_fp8(const MGroupedParams& p, int out_kind, int grid, hipStream_t stream);
+// m-grouped product with fp8 operands and 1x128 UE8M0 scales along K, forward (nt) or dgrad (nn).
+hipError_t launch_mgrouped_fp8(const MGroupedParams& p, bool nt, int out_kind, int grid, hipStream_t stream);
 
 }  // namespace kgw

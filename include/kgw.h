@@ -414,15 +414,15 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
                                void* out, int32_t out_dtype, int32_t accumulate, void* stream);
 
 /*
- * kgw_mgrouped_fp8 -- the m-grouped forward product with fp8 operands
+ * kgw_mgrouped_fp8 -- the m-grouped product with fp8 operands, forward or dgrad
  * (llm-infra-atlas "05 Grouped GEMM": section 2.1, m_grouped_fp8_gemm_nt_contiguous,
  * the contiguous layout; section 3, every fp8 input carries one power-of-two
- * (UE8M0) scale per 1x128 block along K, the scale tensor mn-major).  Row r of A
- * belongs to group g(r) and
+ * (UE8M0) scale per 1x128 block along K, the scale tensor mn-major; section 5.1,
+ * dgrad is m-grouped too).  Row r of A belongs to group g(r) and
  *
- *     out[r, j] = sum_k  a(r, k) * w(g(r), j, k),
- *     a(r, k)    = e4m3(A[r, k])      * 2^(sa[k/128, r] - 127),
- *     w(g, j, k) = e4m3(W[g, j, k])   * 2^(sw[g, k/128, j] - 127),
+ *     out[r, j] = sum_t  a(r, t) * w(g(r), j, t),        t = 0 .. k-1
+ *     a(r, t)    = e4m3(A[r, t])                  * 2^(sa[t/128, r] - 127),
+ *     w(g, j, t) = e4m3(W element (g, j, t))      * 2^(sw[g, t/128, j] - 127),
  *
  * computed as kgw_wgrad_fp8 does: each operand fragment converted exactly to bf16
  * with its scale folded in, products summed in fp32 on the bf16 MFMA, the output
@@ -431,23 +431,27 @@ kgw_status_t kgw_mgrouped_bf16(const void* A, const void* W, int32_t layout, con
  *   A          e4m3 bytes (m, k), row-major (k contiguous), device, 16-byte aligned.
  *   sa         uint8 (k/128, m): sa[b][r] is the biased exponent of the scale of
  *              A[r, 128b : 128b+128].
- *   W          e4m3 bytes (num_groups, n, k) (the "nt" layout: out = A @ W[g]^T),
- *              device, 16-byte aligned.
- *   sw         uint8 (num_groups, k/128, n): scale exponent of W[g, j, 128b : 128b+128].
+ *   W          e4m3 bytes, device, 16-byte aligned, laid out by `layout`:
+ *              KGW_LAYOUT_NT (forward, out = A @ W[g]^T): (num_groups, n, k), element
+ *              (g, j, t) at W[(g*n + j)*k + t]; KGW_LAYOUT_NN (dgrad, out = A @ W[g]):
+ *              (num_groups, k, n), element (g, j, t) at W[(g*k + t)*n + j].
+ *   sw         uint8 (num_groups, k/128, n): scale exponent of the 128 values
+ *              (g, j, 128b .. 128b+127) of W, in either layout.
  *   offsets / m_indices, out, out_dtype, accumulate, stream  as for kgw_mgrouped_bf16,
  *              with the same 128-row group contract (not checked on the host).
  *   A scale byte of 0xFF encodes NaN and, like a NaN operand, makes the affected
  *   outputs NaN.
  *
  * Sizes: 1 <= num_groups <= 65536, 0 <= m < 2^31, 0 <= k < 2^22 and a multiple of
- * 128, 0 <= n < 2^24 and a multiple of 8 (KGW_ERROR_MISALIGNED otherwise).
- * m == 0 or n == 0 does nothing; k == 0 writes zeros (overwrite) into the rows
- * of a group.  Errors as for kgw_wgrad_bf16.
+ * 128, 0 <= n < 2^24 and a multiple of 8 (NT) or 16 (NN) (KGW_ERROR_MISALIGNED
+ * otherwise); an unknown layout is KGW_ERROR_INVALID_VALUE.  m == 0 or n == 0 does
+ * nothing; k == 0 writes zeros (overwrite) into the rows of a group.  Errors as for
+ * kgw_wgrad_bf16.
  */
 kgw_status_t kgw_mgrouped_fp8(const void* A, const uint8_t* sa, const void* W, const uint8_t* sw,
-                              const int32_t* offsets, const int32_t* m_indices, int32_t num_groups,
-                              int64_t m, int64_t k, int64_t n, void* out, int32_t out_dtype,
-                              int32_t accumulate, void* stream);
+                              int32_t layout, const int32_t* offsets, const int32_t* m_indices,
+                              int32_t num_groups, int64_t m, int64_t k, int64_t n, void* out,
+                              int32_t out_dtype, int32_t accumulate, void* stream);
 
 /*
  * kgw_workspace_bytes -- device workspace the kgw_wgrad_* call uses for this shape

@@ -274,12 +274,16 @@ def test_mgrouped_argument_errors(lib):
 
 
 def call_mg8(lib, A=FAKE, sa=FAKE, W=FAKE, sw=FAKE, off=FAKE, idx=None, E=4, M=1024, K=256, N=512, out=FAKE, dt=1,
-             acc=0):
-    return lib.kgw_mgrouped_fp8(A, sa, W, sw, off, idx, E, M, K, N, out, dt, acc, None)
+             acc=0, layout=0):
+    return lib.kgw_mgrouped_fp8(A, sa, W, sw, layout, off, idx, E, M, K, N, out, dt, acc, None)
 
 
 def test_mgrouped_fp8_argument_errors(lib):
     assert call_mg8(lib, E=0) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, layout=2) == kgw.KGW_ERROR_INVALID_VALUE
+    assert call_mg8(lib, layout=kgw.KGW_LAYOUT_NN) == kgw.KGW_ERROR_DEVICE       # accepted, no GPU here
+    assert call_mg8(lib, layout=kgw.KGW_LAYOUT_NN, N=520) == kgw.KGW_ERROR_MISALIGNED   # nn: N % 16
+    assert call_mg8(lib, layout=kgw.KGW_LAYOUT_NT, N=520) == kgw.KGW_ERROR_DEVICE
     assert call_mg8(lib, off=None, idx=None) == kgw.KGW_ERROR_INVALID_VALUE    # no grouping
     assert call_mg8(lib, off=FAKE, idx=FAKE) == kgw.KGW_ERROR_INVALID_VALUE    # both
     assert call_mg8(lib, dt=5) == kgw.KGW_ERROR_INVALID_VALUE
@@ -320,6 +324,10 @@ def test_mgrouped_fp8_binding_rejects_bad_tensors():
         kgw.kgw_mgrouped_fp8(A, sa, W, sw, offsets=off[:1])
     with pytest.raises(ValueError):
         kgw.kgw_wgrad_fp8_ex(A, sa, W[0], sw[0], off, b_major="m")
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa, W, sw, offsets=off, layout="tt")
+    with pytest.raises(ValueError):
+        kgw.kgw_mgrouped_fp8(A, sa, W, sw, offsets=off, layout="nn")           # K mismatch for nn
 
 
 def test_mgrouped_binding_rejects_bad_tensors():

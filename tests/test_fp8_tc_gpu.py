@@ -169,9 +169,12 @@ COUNTS = [128, 384, 0, 384, 512]
 PAD = 128
 
 
-def run_mg(wl, grouping, out, accumulate=False):
+def run_mg(wl, grouping, out, accumulate=False, layout="nt"):
+    """The product with W passed in `layout`: "nn" stores the same logical weight as (E, K, N)
+    (a transposed copy; the scales are the same (E, K/128, N) bytes)."""
     kw = {"offsets": wl.offsets} if grouping == "offsets" else {"m_indices": wl.m_indices}
-    kgw.kgw_mgrouped_fp8(wl.A, wl.sa, wl.W, wl.sw, out=out, accumulate=accumulate, **kw)
+    W = wl.W if layout == "nt" else wl.W.transpose(1, 2).contiguous()
+    kgw.kgw_mgrouped_fp8(wl.A, wl.sa, W, wl.sw, layout=layout, out=out, accumulate=accumulate, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -181,20 +184,22 @@ def mg_oracle(wl, m_indices=None):
     return oracle.mgrouped_fp8(wl.A.cpu(), wl.sa.cpu(), wl.W.cpu(), wl.sw.cpu(), m_indices=idx.cpu())
 
 
+@pytest.mark.parametrize("layout", ["nt", "nn"])
 @pytest.mark.parametrize("accumulate", [False, True])
 @pytest.mark.parametrize("grouping", ["offsets", "m_indices"])
 @pytest.mark.parametrize("K", [128, 384, 640])
-def test_mgrouped_fp8_integer_bit_exact(K, grouping, accumulate):
-    wl = workloads.make_mgrouped_fp8(COUNTS, K, 264, seed=211, device=DEV, pad_rows=PAD, integer_range=4)
+def test_mgrouped_fp8_integer_bit_exact(K, grouping, accumulate, layout):
+    N = 264 if layout == "nt" else 272          # nn: N a multiple of 16
+    wl = workloads.make_mgrouped_fp8(COUNTS, K, N, seed=211, device=DEV, pad_rows=PAD, integer_range=4)
     wl.sa = random_scales(wl.sa.shape, 212)
     wl.sw = random_scales(wl.sw.shape, 213)
     M = wl.M
     if accumulate:
         g = torch.Generator(device=DEV).manual_seed(214)
-        c0 = torch.randint(-8, 9, (M, 264), generator=g, device=DEV, dtype=torch.int32).float()
+        c0 = torch.randint(-8, 9, (M, N), generator=g, device=DEV, dtype=torch.int32).float()
     else:
-        c0 = nan_filled((M, 264))
-    out = run_mg(wl, grouping, c0.clone(), accumulate)
+        c0 = nan_filled((M, N))
+    out = run_mg(wl, grouping, c0.clone(), accumulate, layout)
     ref = mg_oracle(wl)
     valid = ~np.isnan(ref[:, 0])
     assert valid.sum() == sum(COUNTS)
@@ -207,10 +212,16 @@ def test_mgrouped_fp8_integer_bit_exact(K, grouping, accumulate):
     assert not msg, f"rows of no group: {msg}"
 
 
+@pytest.mark.parametrize("layout", ["nt", "nn"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_mgrouped_fp8_random_against_oracle(out_dtype):
-    wl = workloads.make_mgrouped_fp8(COUNTS, 896, 392, seed=215, device=DEV, pad_rows=PAD)
-    out = run_mg(wl, "offsets", nan_filled((wl.M, 392), out_dtype))
+def test_mgrouped_fp8_random_against_oracle(out_dtype, layout):
+    wl = workloads.make_mgrouped_fp8(COUNTS, 896, 400, seed=215, device=DEV, pad_rows=PAD)
+    out = run_mg(wl, "offsets", nan_filled((wl.M, 400), out_dtype), layout=layout)
+    if layout == "nn":
+        # the same logical product: identical to the forward layout bit for bit
+        fwd = run_mg(wl, "offsets", nan_filled((wl.M, 400), out_dtype))
+        bits = torch.int32 if out_dtype == torch.float32 else torch.int16
+        assert torch.equal(out.view(bits), fwd.view(bits))
     ref = mg_oracle(wl)
     valid = ~np.isnan(ref[:, 0])
     got = to_f64(out)
@@ -256,12 +267,14 @@ def test_mgrouped_fp8_k_zero_and_unknown_group_ids():
     assert torch.all(out0[:384] == 0) and not torch.signbit(out0[:384]).any() and torch.all(out0[384:].isnan())
 
 
-def test_mgrouped_fp8_full_layer_every_element_sampled_rows():
-    # the fp8 workload's layer forward: X (T, 7168) @ W^T with W (32, 4096, 7168), 32 local
-    # experts of roundup128(8192 * U(0.7, 1.3)) rows; every element written (NaN prefill)
+@pytest.mark.parametrize("layout", ["nt", "nn"])
+def test_mgrouped_fp8_full_layer_every_element_sampled_rows(layout):
+    # the fp8 workload's layer: X (T, 7168) @ W^T with W (32, 4096, 7168) -- forward, and the
+    # same product with W stored (32, 7168, 4096) as dgrad reads it -- 32 local experts of
+    # roundup128(8192 * U(0.7, 1.3)) rows; every element written (NaN prefill)
     counts = workloads.counts_uniform(32, 8192, 128, 1)
     wl = workloads.make_mgrouped_fp8(counts, 7168, 4096, seed=1, device=DEV)
-    out = run_mg(wl, "offsets", nan_filled((wl.M, 4096), torch.bfloat16))
+    out = run_mg(wl, "offsets", nan_filled((wl.M, 4096), torch.bfloat16), layout=layout)
     assert not torch.isnan(out).any()
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([[0, 127, 128, wl.M - 1], rng.integers(0, wl.M, 12)]))
