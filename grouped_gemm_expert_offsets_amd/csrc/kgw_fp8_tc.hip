@@ -133,8 +133,8 @@ struct RawOp<true> {
 // rsrc_a / rsrc_b (TC stage x or TR step x) and rsrc_sa / rsrc_sb (block x) give the
 // buffer resources (an empty range for anything past the range, read as zeros).
 // sa_voff / sb_voff: the lane's scale byte offsets (+64 for the second 64 rows).  With
-// both operands TC the two strides must be equal (they are: tokens_sum, or K): the
-// loads of both then share their per-lane offsets.
+// both operands TC the two strides must be equal (they are: tokens_sum, an expert's
+// count for ragged blocks, or K): the loads of both then share their per-lane offsets.
 template <bool A_TR, bool B_TR, class RA, class RB, class RSA, class RSB>
 __device__ __forceinline__ void fp8_kloop(f32x16 (&acc)[4][4], lds_char* tiles, uint32_t tiles_addr, int wave,
                                           int lane, int nstages, uint32_t a_stride, uint32_t b_stride,
@@ -158,13 +158,14 @@ __device__ __forceinline__ void fp8_kloop(f32x16 (&acc)[4][4], lds_char* tiles, 
     // Loads issued during step s (modulo 4: R), in order: the TR steps s+3 (A, then B),
     // then for odd s the TC stages (s+3)/2 (A, then B) and the block's scale bytes (sa
     // rows 0-63 / 64-127 of this wave's half, then sb).
-    constexpr int TR_LOADS = (A_TR ? 4 : 0) + (B_TR ? 4 : 0);
-    constexpr int TC_LOADS = (A_TR ? 0 : 8) + (B_TR ? 0 : 8) + 4;
+    constexpr int TR_LOADS = (A_TR ? Operand<true>::kLoads : 0) + (B_TR ? Operand<true>::kLoads : 0);
+    constexpr int TC_LOADS = (A_TR ? 0 : Operand<false>::kLoads) + (B_TR ? 0 : Operand<false>::kLoads) + 4;
     auto loads_in = [](int R) { return TR_LOADS + ((R & 1) ? TC_LOADS : 0); };
     // Load d of step s belongs to one of six groups, in issue order: 0 A TR, 1 B TR (the
     // TR steps s+3), 2 A TC, 3 B TC (the TC stages (s+3)/2, odd s), 4 sa, 5 sb (two byte
     // loads each); group_first(q) is its first load number.
-    constexpr int n_a_tr = A_TR ? 4 : 0, n_b_tr = B_TR ? 4 : 0, n_a_tc = A_TR ? 0 : 8, n_b_tc = B_TR ? 0 : 8;
+    constexpr int n_a_tr = A_TR ? Operand<true>::kLoads : 0, n_b_tr = B_TR ? Operand<true>::kLoads : 0;
+    constexpr int n_a_tc = A_TR ? 0 : Operand<false>::kLoads, n_b_tc = B_TR ? 0 : Operand<false>::kLoads;
     auto group_of = [](int d) {
         if (d < n_a_tr) return 0;
         d -= n_a_tr;
