@@ -20,7 +20,7 @@ import torch
 import grouped_gemm_expert_offsets_amd as kgw
 import oracle
 import workloads
-from helpers import assert_bf16_close, assert_fp32_close, to_f64
+from helpers import assert_bf16_close, assert_fp16_close, assert_fp32_close, to_f64
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -95,7 +95,7 @@ def test_wgrad_layout_integer_bit_exact(layout, accumulate):
     assert not msg, msg
 
 
-@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_wgrad_layout_equals_default_layout_and_oracle(layout, out_dtype):
     counts = [384, 0, 1152, 256, 640]
@@ -107,8 +107,22 @@ def test_wgrad_layout_equals_default_layout_and_oracle(layout, out_dtype):
     ref = fp8_oracle(wl)
     if out_dtype == torch.float32:
         assert_fp32_close(to_f64(out), ref, f"fp8 {layout} fp32")
-    else:
+    elif out_dtype == torch.bfloat16:
         assert_bf16_close(to_f64(out), ref, f"fp8 {layout} bf16")
+    else:
+        assert_fp16_close(to_f64(out), ref, f"fp8 {layout} fp16")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wgrad_layout_malformed_offsets_stay_in_bounds(layout):
+    # decreasing and past-the-end offsets: wrong values allowed for those experts, but the call
+    # completes without leaving the operands and the well-formed first expert is exact
+    counts = [256, 256, 256]
+    wl = integer_wgrad_case(counts, 272, 256, False, seed=205)
+    good = oracle.wgrad_fp8(wl.A.cpu(), wl.sfa.cpu(), wl.B.cpu(), wl.sfb.cpu(), wl.offsets.cpu())
+    wl.offsets = torch.tensor([256, 4096, 128], dtype=torch.int32, device=DEV)
+    out = run_layout(wl, layout, out=nan_filled((3, 272, 256)))
+    assert np.array_equal(to_f64(out[0]), good[0])
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -213,7 +227,7 @@ def test_mgrouped_fp8_integer_bit_exact(K, grouping, accumulate, layout):
 
 
 @pytest.mark.parametrize("layout", ["nt", "nn"])
-@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_mgrouped_fp8_random_against_oracle(out_dtype, layout):
     wl = workloads.make_mgrouped_fp8(COUNTS, 896, 400, seed=215, device=DEV, pad_rows=PAD)
     out = run_mg(wl, "offsets", nan_filled((wl.M, 400), out_dtype), layout=layout)
@@ -228,8 +242,10 @@ def test_mgrouped_fp8_random_against_oracle(out_dtype, layout):
     assert np.all(np.isnan(got[~valid]))
     if out_dtype == torch.float32:
         assert_fp32_close(got[valid][None], ref[valid][None], "mgrouped fp8 fp32")
-    else:
+    elif out_dtype == torch.bfloat16:
         assert_bf16_close(got[valid][None], ref[valid][None], "mgrouped fp8 bf16")
+    else:
+        assert_fp16_close(got[valid][None], ref[valid][None], "mgrouped fp8 fp16")
 
 
 def test_mgrouped_fp8_two_group_tile_matches_single_group_runs():
