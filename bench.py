@@ -397,8 +397,9 @@ def _oracle_sample(name: str, target_seconds: float):
 def run_mfma_ceiling(iters: int = 20000):
     """What this board's MFMAs sustain on the workloads' own operand values (kgw_mfma_ceiling):
     bf16 MFMA on N(0,1)*0.02 bf16 values (the balanced workload's distribution), bf16 MFMA on
-    e4m3 codes converted to bf16 (the exact fp8 path's operands) and the scaled fp8 MFMA on the
-    same codes (the native path), each from the seeded generators of those workloads.  MFMA power
+    e4m3 codes converted to bf16 (the exact fp8 path's operands), the scaled fp8 MFMA on the
+    same codes (the native path) and the scaled MFMA's FP4 mode on uniformly random e2m1 codes
+    (the FP4 line's operands), each from the seeded generators of those workloads.  MFMA power
     depends on the data and the chip lowers its clock past its power limit, so these rates,
     with the clock they ran at, bound what any kernel can reach on such operands."""
     import torch
@@ -408,15 +409,18 @@ def run_mfma_ceiling(iters: int = 20000):
     bf = workloads.randn_bf16((1024, 8192), 0.02, g, "cuda")
     x = workloads.randn_bf16((1024, 8192), 1.0, g, "cuda")
     codes, _ = workloads.quantize_token_blocks(x, token_axis=1)
+    fp4 = torch.randint(0, 256, (1024, 8192), generator=g, device="cuda", dtype=torch.uint8)
     out = {}
     for name, src, kind, peak in (("bf16 MFMA, N(0,1)*0.02 bf16 operands", bf, 0, PEAK_BF16_TFLOPS),
                                   ("bf16 MFMA, e4m3 codes as bf16 (exact fp8 path)", codes, 1, PEAK_BF16_TFLOPS),
-                                  ("scaled fp8 MFMA, e4m3 codes (native fp8 path)", codes, 2, PEAK_FP8_TFLOPS)):
+                                  ("scaled fp8 MFMA, e4m3 codes (native fp8 path)", codes, 2, PEAK_FP8_TFLOPS),
+                                  ("scaled FP4 MFMA, uniformly random e2m1 codes (FP4 path)", fp4, 3,
+                                   PEAK_FP4_TFLOPS)):
         for _ in range(3):
             kgw.kgw_mfma_ceiling(src, kind, iters=iters // 4)
         tflops, ghz = kgw.kgw_mfma_ceiling(src, kind, iters=iters)
         out[name] = {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3), "frac_of_peak": round(tflops / peak, 4)}
-    del bf, x, codes
+    del bf, x, codes, fp4
     torch.cuda.empty_cache()
     return out
 

@@ -684,7 +684,7 @@ def kgw_check_offsets(offsets: torch.Tensor, tokens_sum: int, alignment: int,
 def kgw_mfma_ceiling(src: torch.Tensor, kind: int, iters: int = 20000, workgroups: int = 1024,
                      stream=None) -> Tuple[float, float]:
     """Time MFMA-only loops on the bytes of `src` (kind 0 bf16, 1 e4m3 as bf16, 2 e4m3 on the scaled
-    fp8 MFMA): returns (TFLOP/s from HIP events around the launch, mean clock in GHz the loop ran
+    fp8 MFMA, 3 e2m1 pairs on the scaled MFMA's FP4 mode): returns (TFLOP/s from HIP events around the launch, mean clock in GHz the loop ran
     at).  A measurement helper: it synchronises."""
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous device tensor")
@@ -700,7 +700,7 @@ def kgw_mfma_ceiling(src: torch.Tensor, kind: int, iters: int = 20000, workgroup
     ms = start.elapsed_time(end)
     c = cycles.view(-1, 2).double().cpu()
     ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1
-    flop_per_mfma = 131072.0 if kind == 2 else 32768.0
+    flop_per_mfma = 131072.0 if kind in (2, 3) else 32768.0
     flops = 16.0 * iters * workgroups * 4 * flop_per_mfma
     return flops / (ms * 1e-3) / 1e12, ghz
 

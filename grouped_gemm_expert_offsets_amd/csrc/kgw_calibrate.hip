@@ -6,7 +6,8 @@
 // One workgroup of four waves per compute unit at a time (the launch bound leaves one
 // wave per SIMD, as in the product kernels).  Each lane loads its operand fragments once
 // from the caller's buffer (bf16 values, or e4m3 bytes converted exactly to bf16, or e4m3
-// bytes for the scaled fp8 MFMA), then the wave runs `iters` rounds of 16 independent
+// bytes for the scaled fp8 MFMA, or e2m1 pairs for the scaled MFMA in its FP4 mode),
+// then the wave runs `iters` rounds of 16 independent
 // MFMAs on them with nothing else in the loop.  Thread 0 of every workgroup records the
 // shader-clock cycles and the 100 MHz real-time ticks the loop took.
 #include <hip/hip_runtime.h>
@@ -32,7 +33,26 @@ __global__ __launch_bounds__(kCalThreads, 1) void mfma_ceiling_kernel(const uint
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
     uint64_t t0 = 0, r0 = 0;
-    if constexpr (KIND == 2) {
+    if constexpr (KIND == 3) {
+        // e2m1 x e2m1 (format code 4 for both operands): four dwords per operand and lane,
+        // the upper half of the instruction's eight-dword arguments unused
+        i32x8 a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                a[i][k] = k < 4 ? (int)src[base + 4 * i + k] : 0;
+                b[i][k] = k < 4 ? (int)src[base + 16 + 4 * i + k] : 0;
+            }
+        t0 = clock64();
+        r0 = wall_clock64();
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[m & 1], b[(m >> 1) & 1], acc[m], 4, 4, 0,
+                                                                         127, 0, 127);
+        }
+    } else if constexpr (KIND == 2) {
         i32x8 a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -96,8 +116,10 @@ hipError_t launch_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind,
         hipLaunchKernelGGL(mfma_ceiling_kernel<0>, dim3(workgroups), dim3(kCalThreads), 0, stream, s, words, iters, cycles);
     else if (kind == 1)
         hipLaunchKernelGGL(mfma_ceiling_kernel<1>, dim3(workgroups), dim3(kCalThreads), 0, stream, s, words, iters, cycles);
-    else
+    else if (kind == 2)
         hipLaunchKernelGGL(mfma_ceiling_kernel<2>, dim3(workgroups), dim3(kCalThreads), 0, stream, s, words, iters, cycles);
+    else
+        hipLaunchKernelGGL(mfma_ceiling_kernel<3>, dim3(workgroups), dim3(kCalThreads), 0, stream, s, words, iters, cycles);
     return hipGetLastError();
 }
 

@@ -551,7 +551,7 @@ kgw_status_t kgw_check_offsets(const int32_t* offsets, int32_t num_experts, int6
 
 kgw_status_t kgw_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters, int32_t workgroups,
                               uint64_t* cycles, void* stream) {
-    if (!src || !cycles || src_bytes < 4096 || kind < 0 || kind > 2 || iters < 1 || iters > 10000000 ||
+    if (!src || !cycles || src_bytes < 4096 || kind < 0 || kind > 3 || iters < 1 || iters > 10000000 ||
         workgroups < 1 || workgroups > 65536)
         return KGW_ERROR_INVALID_VALUE;
     if (src_bytes >= ((int64_t)1 << 34)) return KGW_ERROR_UNSUPPORTED;

@@ -515,11 +515,13 @@ kgw_status_t kgw_check_offsets(const int32_t* offsets, int32_t num_experts, int6
  *   kind 0: v_mfma_f32_32x32x16_bf16 on the words of `src` read as bf16 pairs;
  *   kind 1: the same MFMA on e4m3 bytes of `src` converted exactly to bf16 (the operand
  *           values the exact fp8 entry point feeds its MFMAs);
- *   kind 2: v_mfma_scale_f32_32x32x64_f8f6f4 on e4m3 bytes of `src`, unit scales.
+ *   kind 2: v_mfma_scale_f32_32x32x64_f8f6f4 on e4m3 bytes of `src`, unit scales;
+ *   kind 3: the same instruction with both operands e2m1 (two FP4 codes per byte of
+ *           `src`), unit scales (the FP4 entry point's MFMA).
  * Per workgroup w it writes cycles[2w] = shader-clock cycles and cycles[2w+1] = 100 MHz
  * real-time ticks of the loop (8-byte aligned device array of 2 * workgroups values), so
  * cycles / ticks * 1e8 is the clock the loop ran at.  The FLOP count is 16 * iters MFMAs
- * per wave (32768 FLOP each for kinds 0-1, 131072 for kind 2).  Asynchronous on `stream`.
+ * per wave (32768 FLOP each for kinds 0-1, 131072 for kinds 2-3).  Asynchronous on `stream`.
  */
 kgw_status_t kgw_mfma_ceiling(const void* src, int64_t src_bytes, int32_t kind, int32_t iters,
                               int32_t workgroups, uint64_t* cycles, void* stream);

@@ -394,7 +394,8 @@ def test_mfma_ceiling_argument_errors(lib):
     assert f(None, 1 << 20, 0, 100, 256, FAKE, None) == bad
     assert f(FAKE, 1 << 20, 0, 100, 256, None, None) == bad
     assert f(FAKE, 1024, 0, 100, 256, FAKE, None) == bad            # fewer than 4096 bytes
-    assert f(FAKE, 1 << 20, 3, 100, 256, FAKE, None) == bad         # unknown kind
+    assert f(FAKE, 1 << 20, 4, 100, 256, FAKE, None) == bad         # unknown kind
+    assert f(FAKE, 1 << 20, -1, 100, 256, FAKE, None) == bad
     assert f(FAKE, 1 << 20, 0, 0, 256, FAKE, None) == bad
     assert f(FAKE, 1 << 20, 0, 100, 0, FAKE, None) == bad
     assert f(FAKE + 2, 1 << 20, 0, 100, 256, FAKE, None) == kgw.KGW_ERROR_MISALIGNED

@@ -636,6 +636,7 @@ def test_mfma_ceiling_helper_runs():
     g = torch.Generator(device=DEV).manual_seed(9)
     x = workloads.randn_bf16((256, 4096), 1.0, g, DEV)
     codes, _ = workloads.quantize_token_blocks(x, token_axis=1)
-    for src, kind in ((x, 0), (codes, 1), (codes, 2)):
+    fp4 = torch.randint(0, 256, (256, 4096), generator=g, device=DEV, dtype=torch.uint8)
+    for src, kind in ((x, 0), (codes, 1), (codes, 2), (fp4, 3)):
         tflops, ghz = kgw.kgw_mfma_ceiling(src, kind, iters=200, workgroups=256)
         assert 1.0 < tflops < 12000.0 and 0.3 < ghz < 3.5, (kind, tflops, ghz)
