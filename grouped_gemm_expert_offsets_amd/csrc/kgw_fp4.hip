@@ -24,7 +24,10 @@
 // 2-slot scale ring; a stage covers four steps.  Stage y's 24 loads per wave
 // (8 A, 8 B, 4 + 4 scale words) are issued in steps 4y-5, 4y-4 and 4y-3, eight
 // each, spread between the MFMAs, so they have two to four steps to land (two
-// steps of twelve measured 2% slower, four of six 2% slower again).  Slots only
+// steps of twelve measured 2% slower, four of six 2% slower again).  When the
+// scale rows allow 16-byte loads (hidden and n multiples of 4, 16-byte aligned
+// scale arrays) the scale words take one load per operand instead of four
+// (18 loads: A and B, A and B, then the two scale loads).  Slots only
 // change at stage boundaries, so the only barrier is at the start of each
 // stage's last step: it publishes the next stage (after all its loads have
 // landed) and certifies that the stage before has been read.  The fragments
@@ -64,7 +67,9 @@ __device__ __forceinline__ f32x16 mfma_scale_e2m1_32x32x64(i32x4 a, i32x4 b, f32
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
 
-template <int OUT>
+// SC16: scale words by 16-byte loads (the host checks hidden % 4 == 0, n % 4 == 0 and
+// 16-byte aligned scale arrays), else by dword loads.
+template <int OUT, bool SC16>
 __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_TOTAL];
     lds_char* tiles = (lds_char*)smem;
@@ -137,6 +142,9 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
         const int64_t gb0 = begin / 128;               // first 128-token scale word of the range
         const uint32_t sa_voff = (uint32_t)(m0 + wm * 128 + lane) * 4u;
         const uint32_t sb_voff = (uint32_t)(n0 + wn * 128 + lane) * 4u;
+        // 16-byte form: lane L fetches rows 4(L&31) .. +3 of word L>>5 (the stage's two words)
+        const uint32_t sa16_voff = (uint32_t)((int64_t)(lane >> 5) * H + m0 + wm * 128 + 4 * (lane & 31)) * 4u;
+        const uint32_t sb16_voff = (uint32_t)((int64_t)(lane >> 5) * N + n0 + wn * 128 + 4 * (lane & 31)) * 4u;
 
         // Half `hf` (0, 1) of stage y's loads: A and B loads 4hf..4hf+3, then the
         // scale words w = hf of both halves of this wave's rows and columns.
@@ -164,10 +172,26 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
                        dst);
             }
         };
+        // Both scale words of stage y for this wave's rows (q 0) or columns (q 1) in one 16-byte
+        // load per lane; they land where the dword loads of dma_half put them.
+        auto dma_scales16 = [&](int y, int q) __attribute__((always_inline)) {
+            const bool bs = q == 1;
+            const int64_t mn = bs ? N : H;
+            const uint8_t* base = (bs ? p.sfb : p.sfa) + (gb0 + 2 * y) * mn * 4;
+            const uint32_t dst = tiles_addr + sc_wave + (uint32_t)((y & 1) * SC_STAGE) + (bs ? 1024u : 0u);
+            dma_16B(rsrc_words(base, y < nstages ? (uint32_t)(mn * 8) : 0u), bs ? sb16_voff : sa16_voff, dst);
+        };
         // Loads of step s (and of the prologue's virtual steps): steps with
         // s & 3 == 3, 0 and 1 issue the first, second and third eight of the 24 loads
         // of stage (s+5)/4, (s+4)/4 and (s+3)/4 (dma_half order: A, B, scale words).
+        // With 16-byte scale loads: A and B of half 0, A and B of half 1, then the two
+        // scale loads (18 in all).
         auto dma_third = [&](int y, int k, int d) __attribute__((always_inline)) {
+            if constexpr (SC16) {
+                if (k < 2) dma_half(y, k, d);
+                else if (d < 2) dma_scales16(y, d);
+                return;
+            }
             const int g = 8 * k + d;
             dma_half(y, g >= 12 ? 1 : 0, g >= 12 ? g - 12 : g);
         };
@@ -275,16 +299,25 @@ __global__ __launch_bounds__(NT, 1) void wgrad_fp4_kernel(GroupedParams p) {
     }
 }
 
+template <bool SC16>
+hipError_t launch_fp4(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
+    if (out_kind == kOutBf16)
+        hipLaunchKernelGGL((wgrad_fp4_kernel<kOutBf16, SC16>), dim3(grid), dim3(NT), 0, stream, p);
+    else if (out_kind == kOutF16)
+        hipLaunchKernelGGL((wgrad_fp4_kernel<kOutF16, SC16>), dim3(grid), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((wgrad_fp4_kernel<kOutF32, SC16>), dim3(grid), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_wgrad_fp4(const GroupedParams& p, int out_kind, int grid, hipStream_t stream) {
-    if (out_kind == kOutBf16)
-        hipLaunchKernelGGL(wgrad_fp4_kernel<kOutBf16>, dim3(grid), dim3(NT), 0, stream, p);
-    else if (out_kind == kOutF16)
-        hipLaunchKernelGGL(wgrad_fp4_kernel<kOutF16>, dim3(grid), dim3(NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL(wgrad_fp4_kernel<kOutF32>, dim3(grid), dim3(NT), 0, stream, p);
-    return hipGetLastError();
+    // scale words move 16 bytes per lane (four rows) when every such load is aligned: one
+    // load per operand and stage instead of four dword loads
+    const bool sc16 = ((p.hidden | p.n) & 3) == 0 && (((uintptr_t)p.sfa | (uintptr_t)p.sfb) & 15u) == 0;
+    if (sc16) return launch_fp4<true>(p, out_kind, grid, stream);
+    return launch_fp4<false>(p, out_kind, grid, stream);
 }
 
 }  // namespace kgw

@@ -29,19 +29,34 @@ def fp4_oracle(wl):
     return oracle.wgrad_fp4(wl["A"], wl["sfa"], wl["B"], wl["sfb"], wl["offsets"])
 
 
+def misaligned_copy(t):
+    # the same words at an address 4 bytes past a 16-byte boundary
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+# the scale words move by 16-byte loads when hidden and n are multiples of 4 and both scale
+# arrays are 16-byte aligned, else by dword loads: both paths, bit for bit
+@pytest.mark.parametrize("scale_path", ["16B", "dword_hidden", "dword_pointer"])
 @pytest.mark.parametrize("accumulate", [False, True])
-def test_integer_bit_exact_with_block_scales(accumulate):
+def test_integer_bit_exact_with_block_scales(accumulate, scale_path):
     # integers of e2m1 with random per-32-token scales 2^-1..2^2: exact in fp32
     counts = [256, 0, 512, 768, 256]
-    wl = workloads.make_fp4_operands(counts, 264, 392, seed=121, integer_range=6)
+    H = 270 if scale_path == "dword_hidden" else 264
+    wl = workloads.make_fp4_operands(counts, H, 392, seed=121, integer_range=6)
     g = torch.Generator().manual_seed(122)
     wl["sfa"] = torch.randint(126, 130, wl["sfa"].shape, generator=g, dtype=torch.int32).to(torch.uint8)
     wl["sfb"] = torch.randint(126, 130, wl["sfb"].shape, generator=g, dtype=torch.int32).to(torch.uint8)
     A, sa, B, sb, off = to_dev(wl)
+    if scale_path == "dword_pointer":
+        sa, sb = misaligned_copy(sa), misaligned_copy(sb)
+        assert sa.data_ptr() % 16 == 4
     if accumulate:
-        c0 = torch.randint(-8, 9, (5, 264, 392), generator=g, dtype=torch.int32).float().to(DEV)
+        c0 = torch.randint(-8, 9, (5, H, 392), generator=g, dtype=torch.int32).float().to(DEV)
     else:
-        c0 = torch.full((5, 264, 392), float("nan"), device=DEV)
+        c0 = torch.full((5, H, 392), float("nan"), device=DEV)
     out = c0.clone()
     kgw.kgw_wgrad_fp4(A, sa, B, sb, off, out=out, accumulate=accumulate)
     torch.cuda.synchronize()
