@@ -554,120 +554,141 @@ __global__ __launch_bounds__(NT) void quantize_fp4_cols(const uint16_t* __restri
 
 // tokens along the rows: x (rows, cols) -> q (cols, rows/2), the token axis made
 // contiguous (the FP4 weight gradient's B layout), scales with mn = cols.  A
-// workgroup of 512 threads takes 256 tokens x 128 columns: wave w (0..7) tokens
-// 32w .. 32w+31 -- one 32-token block -- and lane l columns 8*(l & 15) .. +7 and
-// tokens 8*(l >> 4) .. +7 of the wave's 32 (each load 4 rows x 256 bytes; eight
-// consecutive tokens make one 4-byte code word per column).  The code words
-// collect in LDS so each column's 128 bytes leave as whole-line stores
-// (scattered 4-byte stores ran at a third of the speed); scales as bytes
-// ((rows/32, cols)) or as the 128-token groups' words, assembled through LDS.  A
-// trailing 128-token half tile is skipped by waves 4-7.
+// workgroup of 512 threads takes runs of FP4_ROWS_SPAN units of 256 tokens x 128
+// columns that share their columns (1024 consecutive tokens): in a unit, wave w
+// (0..7) takes tokens 32w .. 32w+31 -- one 32-token block -- and lane l columns
+// 8*(l & 15) .. +7 and tokens 8*(l >> 4) .. +7 of the wave's 32 (each load 4 rows
+// x 256 bytes; eight consecutive tokens make one 4-byte code word per column).
+// The code words of the whole run collect in LDS, so each column's 512 bytes
+// leave as four consecutive whole lines: the output is transposed, and with one
+// 128-byte line per column and unit the scattered stores ran at about 2 TB/s and
+// took 40% of the kernel's time.  Scales as bytes ((rows/32, cols), stored per
+// unit) or as the 128-token groups' words (assembled in LDS, stored per run).
+// Units past the last 256-token chunk are skipped; a trailing 128-token half unit
+// is skipped by waves 4-7.
 constexpr int NT_FP4_ROWS = 512;
+constexpr int FP4_ROWS_SPAN = 4;
 template <int FMT>
 __global__ __launch_bounds__(NT_FP4_ROWS) void quantize_fp4_rows(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int64_t cols, uint8_t* __restrict__ q,
                                                                 uint8_t* __restrict__ s) {
     constexpr bool MX = FMT == kScalesPacked32;
-    __shared__ uint32_t codes_lds[2][128][33];  // [column][token group of 8] (+1: bank spread)
-    __shared__ uint8_t red_e[2][8][128];        // [32-token block of the tile][column]
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    constexpr int S = FP4_ROWS_SPAN;
+    __shared__ uint32_t codes_lds[128][32 * S + 1];   // [column][token group of 8] (+1: bank spread)
+    __shared__ uint8_t red_e[8 * S][128];             // [32-token block of the run][column]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int cg = lane & 15, tg = lane >> 4;
     const int64_t cchunks = (cols + 127) / 128;
     const int64_t tchunks = (rows + 255) / 256;
-    const int64_t units = tchunks * cchunks;
-    // unit u's input block for this lane (zeros for lanes outside the tensor)
-    auto load_unit = [&](int64_t u, i32x4 (&v)[8]) __attribute__((always_inline)) {
-        const int64_t b = u / cchunks;
-        const int64_t n0 = (u - b * cchunks) * 128 + 8 * cg;
-        const int64_t tw = 256 * b + 32 * wave;
+    const int64_t runs = ((tchunks + S - 1) / S) * cchunks;
+    // unit i of run r: its input block for this lane (zeros for lanes outside the tensor)
+    auto load_unit = [&](int64_t r, int i, i32x4 (&v)[8]) __attribute__((always_inline)) {
+        const int64_t g = r / cchunks;
+        const int64_t n0 = (r - g * cchunks) * 128 + 8 * cg;
+        const int64_t tw = 256 * (g * S + i) + 32 * wave;
         const bool active = tw < rows && n0 < cols;
         const int64_t t0 = tw + 8 * tg;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (active) v[i] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + i) * cols + n0));
-            else v[i] = i32x4{0, 0, 0, 0};
+        for (int k = 0; k < 8; ++k) {
+            if (active) v[k] = __builtin_nontemporal_load((const i32x4*)(x + (t0 + k) * cols + n0));
+            else v[k] = i32x4{0, 0, 0, 0};
         }
     };
     i32x4 v[8], vn[8];
-    if (blockIdx.x < units) load_unit(blockIdx.x, v);
-    int par = 0;
-    for (int64_t u = blockIdx.x; u < units; u += gridDim.x, par ^= 1) {
-        const int64_t b = u / cchunks;
-        const int64_t c0 = (u - b * cchunks) * 128;
+    if (blockIdx.x < runs) load_unit(blockIdx.x, 0, v);
+    for (int64_t r = blockIdx.x; r < runs; r += gridDim.x) {
+        const int64_t g = r / cchunks;
+        const int64_t c0 = (r - g * cchunks) * 128;
         const int64_t n0 = c0 + 8 * cg;
-        const int64_t tw = 256 * b + 32 * wave;         // the wave's first token
-        const bool wave_live = tw < rows;                // rows is a multiple of 128: whole waves
-        const bool active = wave_live && n0 < cols;      // cols is a multiple of 8
-        // largest magnitude pattern of columns 2h (low half) and 2h+1 (high half)
-        // over the lane's 8 tokens, then over the 4 lanes of the 32-token block
-        uint32_t mag[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < S; ++i) {
+            const int64_t b = g * S + i;                     // the unit's 256-token chunk
+            const int64_t tw = 256 * b + 32 * wave;          // the wave's first token
+            const bool active = tw < rows && n0 < cols;      // rows: a multiple of 128; cols: of 8
+            // largest magnitude pattern of columns 2h (low half) and 2h+1 (high half)
+            // over the lane's 8 tokens, then over the 4 lanes of the 32-token block
+            uint32_t mag[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)v[i][h] & kBf16MagMask);
+            for (int k = 0; k < 8; ++k)
 #pragma unroll
-        for (int m = 16; m < 64; m <<= 1)
+                for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)v[k][h] & kBf16MagMask);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)__shfl_xor((int)mag[h], m, 64));
-        uint32_t e[8];
+            for (int m = 16; m < 64; m <<= 1)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fp4_block_exponent((j & 1) ? mag[j >> 1] >> 16 : mag[j >> 1] & 0xFFFFu);
-        // column j's eight tokens: value i of the word is token t0 + i; tokens 2p and
-        // 2p+1 of the column are joined into one bf16 pair (v_perm_b32) and converted
-        // together into byte p
+                for (int h = 0; h < 4; ++h) mag[h] = max_u16x2(mag[h], (uint32_t)__shfl_xor((int)mag[h], m, 64));
+            uint32_t e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float sc_j = e8m0_scale(e[j] == 255u ? 127u : e[j]);
-            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            uint32_t codes = e2m1_pair<0>(0u, __builtin_amdgcn_perm((uint32_t)v[1][j >> 1], (uint32_t)v[0][j >> 1], sel), sc_j);
-            codes = e2m1_pair<1>(codes, __builtin_amdgcn_perm((uint32_t)v[3][j >> 1], (uint32_t)v[2][j >> 1], sel), sc_j);
-            codes = e2m1_pair<2>(codes, __builtin_amdgcn_perm((uint32_t)v[5][j >> 1], (uint32_t)v[4][j >> 1], sel), sc_j);
-            codes = e2m1_pair<3>(codes, __builtin_amdgcn_perm((uint32_t)v[7][j >> 1], (uint32_t)v[6][j >> 1], sel), sc_j);
-            if (e[j] == 255u) codes = 0;
-            codes_lds[par][8 * cg + j][4 * wave + tg] = codes;
-        }
-        if constexpr (!MX) {
-            if (tg == 0 && active) {
-                const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
-                                  (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
-                *(i32x2*)(s + (8 * b + wave) * cols + n0) = sw;
+            for (int j = 0; j < 8; ++j) e[j] = fp4_block_exponent((j & 1) ? mag[j >> 1] >> 16 : mag[j >> 1] & 0xFFFFu);
+            // column j's eight tokens: value k of the word is token t0 + k; tokens 2p and
+            // 2p+1 of the column are joined into one bf16 pair (v_perm_b32) and converted
+            // together into byte p
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float sc_j = e8m0_scale(e[j] == 255u ? 127u : e[j]);
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t codes = e2m1_pair<0>(0u, __builtin_amdgcn_perm((uint32_t)v[1][j >> 1], (uint32_t)v[0][j >> 1], sel), sc_j);
+                codes = e2m1_pair<1>(codes, __builtin_amdgcn_perm((uint32_t)v[3][j >> 1], (uint32_t)v[2][j >> 1], sel), sc_j);
+                codes = e2m1_pair<2>(codes, __builtin_amdgcn_perm((uint32_t)v[5][j >> 1], (uint32_t)v[4][j >> 1], sel), sc_j);
+                codes = e2m1_pair<3>(codes, __builtin_amdgcn_perm((uint32_t)v[7][j >> 1], (uint32_t)v[6][j >> 1], sel), sc_j);
+                if (e[j] == 255u) codes = 0;
+                codes_lds[8 * cg + j][32 * i + 4 * wave + tg] = codes;
             }
-        } else {
-            if (tg == 0) {
+            if constexpr (!MX) {
+                if (tg == 0 && active) {
+                    const i32x2 sw = {(int)(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24)),
+                                      (int)(e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24))};
+                    *(i32x2*)(s + (8 * b + wave) * cols + n0) = sw;
+                }
+            } else {
+                if (tg == 0) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) red_e[par][wave][8 * cg + j] = (uint8_t)e[j];
+                    for (int j = 0; j < 8; ++j) red_e[8 * i + wave][8 * cg + j] = (uint8_t)e[j];
+                }
             }
+            // the next unit's loads go out before this unit's conversions finish
+            if (i + 1 < S) load_unit(r, i + 1, vn);
+            else if (r + gridDim.x < runs) load_unit(r + gridDim.x, 0, vn);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = vn[k];
         }
-        // the next unit's loads go out before this unit's code stores
-        if (u + gridDim.x < units) load_unit(u + gridDim.x, vn);
         __syncthreads();
-        // codes: thread -> column tid >> 2, bytes 32*(tid & 3) .. +31 of the tile's 128
-        {
-            const int tid = threadIdx.x;
-            const int col = tid >> 2, part = tid & 3;
-            const int64_t tpart = 256 * b + 64 * part;    // the part's first token
-            if (c0 + col < cols && tpart < rows) {
-                const uint32_t* src = &codes_lds[par][col][8 * part];
-                uint8_t* dst = q + (c0 + col) * (rows / 2) + tpart / 2;
-                __builtin_nontemporal_store(i32x4{(int)src[0], (int)src[1], (int)src[2], (int)src[3]}, (i32x4*)dst);
-                __builtin_nontemporal_store(i32x4{(int)src[4], (int)src[5], (int)src[6], (int)src[7]}, (i32x4*)(dst + 16));
+        // codes: in pass p, thread -> column 64p + (tid >> 3); store m writes bytes
+        // 16*(tid & 7) .. +15 of the column's line m (unit m: 256 tokens, 128 bytes), so every
+        // store instruction writes eight whole lines and each column's run leaves in order
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int col = 64 * pass + (tid >> 3), l8 = tid & 7;
+            if (c0 + col < cols) {
+                uint8_t* dst_col = q + (c0 + col) * (rows / 2) + 128 * g * S + 16 * l8;
+#pragma unroll
+                for (int m = 0; m < S; ++m) {
+                    const int64_t tchunk = 256 * (g * S + m) + 32 * l8;   // the chunk's first token
+                    if (tchunk < rows) {
+                        const uint32_t* src = &codes_lds[col][32 * m + 4 * l8];
+                        __builtin_nontemporal_store(i32x4{(int)src[0], (int)src[1], (int)src[2], (int)src[3]},
+                                                    (i32x4*)(dst_col + 128 * m));
+                    }
+                }
             }
         }
         if constexpr (MX) {
-            // the tile's two 128-token groups: word (group, column) from blocks 4*group .. +3
-            const int tid = threadIdx.x;
-            const int grp = tid >> 7, col = tid & 127;
-            const int64_t gg = 2 * b + grp;
-            if (grp < 2 && c0 + col < cols && 128 * gg < rows) {
-                const uint32_t w = (uint32_t)red_e[par][4 * grp][col] | ((uint32_t)red_e[par][4 * grp + 1][col] << 8) |
-                                   ((uint32_t)red_e[par][4 * grp + 2][col] << 16) |
-                                   ((uint32_t)red_e[par][4 * grp + 3][col] << 24);
-                ((uint32_t*)s)[gg * cols + c0 + col] = w;
+            // the run's 2S 128-token groups: word (group, column) from blocks 4*group .. +3
+            const int col = tid & 127;
+#pragma unroll
+            for (int k = 0; k < (2 * S + 3) / 4; ++k) {
+                const int grp = (tid >> 7) + 4 * k;
+                const int64_t gg = 2 * g * S + grp;
+                if (grp < 2 * S && c0 + col < cols && 128 * gg < rows) {
+                    const uint32_t w = (uint32_t)red_e[4 * grp][col] | ((uint32_t)red_e[4 * grp + 1][col] << 8) |
+                                       ((uint32_t)red_e[4 * grp + 2][col] << 16) |
+                                       ((uint32_t)red_e[4 * grp + 3][col] << 24);
+                    ((uint32_t*)s)[gg * cols + c0 + col] = w;
+                }
             }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = vn[i];
+        __syncthreads();                                  // the LDS is refilled by the next run
     }
 }
 
@@ -697,7 +718,7 @@ hipError_t launch_quantize_fp4(const void* x, int64_t rows, int64_t cols, int32_
             hipLaunchKernelGGL(quantize_fp4_cols<kScalesU8>, dim3((unsigned)blocks), dim3(NT), 0, stream,
                                (const uint16_t*)x, rows, cols, (uint8_t*)q, (uint8_t*)s);
     } else {
-        int64_t blocks = ((rows + 255) / 256) * ((cols + 127) / 128);
+        int64_t blocks = ((rows + 256 * FP4_ROWS_SPAN - 1) / (256 * FP4_ROWS_SPAN)) * ((cols + 127) / 128);
         const int64_t cap = (int64_t)num_cus * 8;
         if (blocks > cap) blocks = cap;
         if (blocks < 1) blocks = 1;
