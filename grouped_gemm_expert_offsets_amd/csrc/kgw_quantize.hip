@@ -559,11 +559,12 @@ __global__ __launch_bounds__(NT) void quantize_fp4_cols(const uint16_t* __restri
 // (0..7) takes tokens 32w .. 32w+31 -- one 32-token block -- and lane l columns
 // 8*(l & 15) .. +7 and tokens 8*(l >> 4) .. +7 of the wave's 32 (each load 4 rows
 // x 256 bytes; eight consecutive tokens make one 4-byte code word per column).
-// The code words of the whole run collect in LDS, so each column's 512 bytes
-// leave as four consecutive whole lines: the output is transposed, and with one
-// 128-byte line per column and unit the scattered stores ran at about 2 TB/s and
-// took 40% of the kernel's time.  Scales as bytes ((rows/32, cols), stored per
-// unit) or as the 128-token groups' words (assembled in LDS, stored per run).
+// The code words of the whole run collect in LDS, and each column's 512 bytes
+// leave as four consecutive lines, eight lanes per column, so every store
+// instruction writes whole lines (the output is transposed: stores that each
+// wrote half of every line they touched ran at about 2 TB/s and took 40% of the
+// kernel's time).  Scales as bytes ((rows/32, cols), stored per unit) or as the
+// 128-token groups' words (assembled in LDS, stored per run).
 // Units past the last 256-token chunk are skipped; a trailing 128-token half unit
 // is skipped by waves 4-7.
 constexpr int NT_FP4_ROWS = 512;
