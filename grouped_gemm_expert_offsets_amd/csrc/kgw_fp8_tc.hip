@@ -8,7 +8,7 @@
 //   - the m-grouped forward product out[m] = A[m] @ W[g(m)]^T of the same MoE layer
 //     (llm-infra-atlas "05 Grouped GEMM", section 2.1, m_grouped_fp8_gemm_nt_contiguous;
 //     section 3: each fp8 input comes with one scale per 1x128 block along K, the
-//     scales mn-major).
+//     scales mn-major), and its dgrad out[m] = A[m] @ W[g(m)] with W stored (E, K, N).
 //
 // As in kgw_wgrad_fp8's kernel, every MFMA operand fragment is converted exactly to
 // bf16 with its block scale folded in (v_cvt_scalef32_pk_bf16_fp8) and the bf16 MFMA
