@@ -425,6 +425,20 @@ def run_mfma_ceiling(iters: int = 20000):
     return out
 
 
+# The secondary measurements that `--line` runs alone: (steps, warmup, min_warm_s) -> result.
+LINES = {
+    "fp4": lambda k, w, t: run_fp4(k, w, t),
+    "mgrouped_nt": lambda k, w, t: run_mgrouped("nt", k, w, t),
+    "mgrouped_nn": lambda k, w, t: run_mgrouped("nn", k, w, t),
+    "mgrouped_fp8_nt": lambda k, w, t: run_mgrouped_fp8("nt", k, w, t),
+    "mgrouped_fp8_nn": lambda k, w, t: run_mgrouped_fp8("nn", k, w, t),
+    "quantize_fp8_A": lambda k, w, t: run_quantize(1, k, w, t),
+    "quantize_fp8_B": lambda k, w, t: run_quantize(0, k, w, t),
+    "quantize_fp4_A": lambda k, w, t: run_quantize(1, k, w, t, fp4=True),
+    "quantize_fp4_B": lambda k, w, t: run_quantize(0, k, w, t, fp4=True),
+}
+
+
 def cpu_baseline(target_seconds: float):
     """The CPU oracle on a bounded sample of every configuration (about `target_seconds` in
     all), plus a one-thread sample of the balanced workload; the headline's is the top level."""
@@ -472,6 +486,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--line", choices=sorted(LINES),
+                    help="run only this secondary measurement and print its result (for profiling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -491,6 +507,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.line:
+        print(json.dumps(LINES[args.line](args.steps, args.warmup, args.warmup_seconds)), flush=True)
         return
 
     head = run_workload(args.workload, args.steps, args.warmup, native=args.native_fp8,

@@ -90,3 +90,14 @@ def test_headline_workload_bytes_and_flops():
     T = 264320
     assert bench.algorithmic_bytes(w) == 7168 * T + T * 4096 + (T // 128) * (7168 + 4096) + 32 * 7168 * 4096 * 2
     assert 2 * w.hidden * w.n * w.tokens_sum == 2 * 7168 * 4096 * 264320
+
+
+def test_single_line_option_names_every_secondary_kind():
+    # `--line` runs one secondary measurement alone (what the committed profiles of those
+    # kernels were taken with); unknown names are refused before anything runs
+    assert set(bench.LINES) == {"fp4", "mgrouped_nt", "mgrouped_nn", "mgrouped_fp8_nt", "mgrouped_fp8_nn",
+                                "quantize_fp8_A", "quantize_fp8_B", "quantize_fp4_A", "quantize_fp4_B"}
+    assert all(callable(f) for f in bench.LINES.values())
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--line", "no_such_line"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "invalid choice" in r.stderr
